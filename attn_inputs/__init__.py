@@ -1,0 +1,281 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module is shared by the CPU oracle side and the GPU side, and by nothing
+else.  It holds no attention arithmetic: only random draws, the rounding of those
+draws to bfloat16, the workload table, the paged-cache layout (which page holds
+which token) and the counting of work units used to express throughput.
+
+Every tensor slice is drawn from its own counter-keyed stream
+``numpy.random.SeedSequence([seed, tensor, b, h])`` so that any single head of a
+full-size workload can be regenerated on its own (the oracle checks sampled
+heads of the large workloads without drawing the whole tensor).
+
+Value recipe (all workloads): i.i.d. float32 N(0, 1) draws, optionally multiplied
+by a constant in float32, rounded to bfloat16 with round-to-nearest-even.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+# Stream identifiers inside one workload seed.
+T_Q, T_K, T_V, T_LEN, T_PERM = 0, 1, 2, 3, 4
+
+BF16_NAN = np.uint16(0x7FC0)
+
+
+# ----------------------------------------------------------------------------
+# bfloat16 rounding of float32 draws
+# ----------------------------------------------------------------------------
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even).
+
+    Returns the 16-bit patterns as uint16.  Inputs are finite draws; NaN and
+    infinity are not produced by the generators and are not handled here.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float64."""
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _stream(seed: int, tensor: int, b: int = 0, h: int = 0) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([seed, tensor, b, h]))
+
+
+def normal_bf16(seed: int, tensor: int, b: int, h: int, shape, mult: float = 1.0) -> np.ndarray:
+    """One head's slice: float32 N(0,1) draws (times ``mult`` in float32), rounded to bf16 bits."""
+    x = _stream(seed, tensor, b, h).standard_normal(shape, dtype=np.float32)
+    if mult != 1.0:
+        x *= np.float32(mult)
+    return to_bf16_bits(x)
+
+
+# ----------------------------------------------------------------------------
+# Workload table
+# ----------------------------------------------------------------------------
+@dataclass(frozen=True)
+class PrefillCfg:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    seed: int
+    q_mult: float = 1.0
+
+    @property
+    def scale(self) -> float:
+        """Softmax scale 1/sqrt(d), as the float32 value both sides receive."""
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+
+@dataclass(frozen=True)
+class DecodeCfg:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    seed: int
+    paged: bool
+    page_size: int = 16
+    fixed_len: int = 0            # every sequence this long (contiguous workload)
+    len_range: tuple = (0, 0)     # inclusive uniform range of lengths (paged workload)
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+
+CONFIGS = {
+    # Tiny prefill: correctness-sized, several tiles and heads.
+    "tiny_prefill": PrefillCfg("tiny_prefill", B=1, Hq=4, Hkv=4, Nq=512, Nk=512, d=64,
+                               causal=True, seed=1),
+    # Llama-2-7B-shaped prefill (32 heads x d=128), causal and non-causal on the same tensors.
+    "llama2_7b_prefill": PrefillCfg("llama2_7b_prefill", B=4, Hq=32, Hkv=32, Nq=2048, Nk=2048,
+                                    d=128, causal=True, seed=2),
+    "llama2_7b_prefill_noncausal": PrefillCfg("llama2_7b_prefill_noncausal", B=4, Hq=32, Hkv=32,
+                                              Nq=2048, Nk=2048, d=128, causal=False, seed=2),
+    # Long-context prefill, Q scaled by 3 before rounding so softmax rows are peaky.
+    "long_prefill_32k": PrefillCfg("long_prefill_32k", B=1, Hq=32, Hkv=32, Nq=32768, Nk=32768,
+                                   d=128, causal=True, seed=3, q_mult=3.0),
+    # GQA decode on a contiguous cache, every sequence 8192 tokens long.
+    "gqa_decode_contig": DecodeCfg("gqa_decode_contig", B=64, Hq=32, Hkv=8, d=128, seed=4,
+                                   paged=False, fixed_len=8192),
+    # Paged GQA decode, 16-token pages, lengths uniform in [1024, 131072].
+    "paged_gqa_decode": DecodeCfg("paged_gqa_decode", B=8, Hq=32, Hkv=8, d=128, seed=5,
+                                  paged=True, page_size=16, len_range=(1024, 131072)),
+}
+
+
+# ----------------------------------------------------------------------------
+# Prefill inputs
+# ----------------------------------------------------------------------------
+def prefill_head(cfg: PrefillCfg, tensor: int, b: int, h: int) -> np.ndarray:
+    """bf16 bits of one head: Q [Nq, d] for tensor T_Q, K/V [Nk, d] for T_K/T_V."""
+    if tensor == T_Q:
+        return normal_bf16(cfg.seed, T_Q, b, h, (cfg.Nq, cfg.d), cfg.q_mult)
+    return normal_bf16(cfg.seed, tensor, b, h, (cfg.Nk, cfg.d))
+
+
+def prefill_inputs(cfg: PrefillCfg):
+    """Whole tensors as bf16 bits: q [B,Hq,Nq,d], k and v [B,Hkv,Nk,d]."""
+    q = np.empty((cfg.B, cfg.Hq, cfg.Nq, cfg.d), np.uint16)
+    k = np.empty((cfg.B, cfg.Hkv, cfg.Nk, cfg.d), np.uint16)
+    v = np.empty_like(k)
+    for b in range(cfg.B):
+        for h in range(cfg.Hq):
+            q[b, h] = prefill_head(cfg, T_Q, b, h)
+        for h in range(cfg.Hkv):
+            k[b, h] = prefill_head(cfg, T_K, b, h)
+            v[b, h] = prefill_head(cfg, T_V, b, h)
+    return q, k, v
+
+
+def custom_prefill(seed: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int,
+                   q_mult: float = 1.0):
+    """Inputs for an arbitrary prefill shape (edge cases), same recipe."""
+    cfg = PrefillCfg("custom", B, Hq, Hkv, Nq, Nk, d, True, seed, q_mult)
+    return prefill_inputs(cfg)
+
+
+# ----------------------------------------------------------------------------
+# Decode inputs
+# ----------------------------------------------------------------------------
+def decode_lengths(cfg: DecodeCfg) -> np.ndarray:
+    """KV length of every sequence, int32 [B]."""
+    if not cfg.paged:
+        return np.full(cfg.B, cfg.fixed_len, np.int32)
+    lo, hi = cfg.len_range
+    return _stream(cfg.seed, T_LEN).integers(lo, hi, size=cfg.B, endpoint=True).astype(np.int32)
+
+
+def decode_q(cfg: DecodeCfg) -> np.ndarray:
+    """q [B, Hq, d] bf16 bits."""
+    q = np.empty((cfg.B, cfg.Hq, cfg.d), np.uint16)
+    for b in range(cfg.B):
+        for h in range(cfg.Hq):
+            q[b, h] = normal_bf16(cfg.seed, T_Q, b, h, (cfg.d,))
+    return q
+
+
+def decode_kv_logical(cfg: DecodeCfg, tensor: int, b: int, kvh: int, length: int) -> np.ndarray:
+    """The first ``length`` cached K (or V) rows of sequence b, KV head kvh: [length, d] bits."""
+    return normal_bf16(cfg.seed, tensor, b, kvh, (length, cfg.d))
+
+
+@dataclass
+class PagedLayout:
+    """Which physical page holds which 16-token block of which sequence."""
+    page_size: int
+    num_pages: int
+    max_blocks: int
+    block_table: np.ndarray = field(repr=False)   # int32 [B, max_blocks], -1 = unused
+
+
+def paged_layout(lengths: np.ndarray, page_size: int, seed: int, max_blocks: int | None = None,
+                 extra_pages: int = 0) -> PagedLayout:
+    """Pool of sum(ceil(len/page)) pages (+ ``extra_pages`` never referenced); sequence b takes a
+    consecutive slice of a seeded random permutation of the pool."""
+    nblk = [(int(n) + page_size - 1) // page_size for n in lengths]
+    total = sum(nblk)
+    num_pages = total + extra_pages
+    mb = max(max(nblk) if nblk else 1, 1) if max_blocks is None else max_blocks
+    perm = _stream(seed, T_PERM).permutation(num_pages).astype(np.int32)
+    table = np.full((len(lengths), mb), -1, np.int32)
+    off = 0
+    for b, n in enumerate(nblk):
+        table[b, :n] = perm[off:off + n]
+        off += n
+    return PagedLayout(page_size, num_pages, mb, table)
+
+
+def build_contig_cache(cfg: DecodeCfg, tensor: int, lengths: np.ndarray, max_len: int,
+                       pad_bits=BF16_NAN) -> np.ndarray:
+    """[B, Hkv, max_len, d] bits; slots at or past lengths[b] hold ``pad_bits``."""
+    c = np.full((cfg.B, cfg.Hkv, max_len, cfg.d), pad_bits, np.uint16)
+    for b in range(cfg.B):
+        n = int(lengths[b])
+        for h in range(cfg.Hkv):
+            c[b, h, :n] = decode_kv_logical(cfg, tensor, b, h, n)
+    return c
+
+
+def build_paged_cache(cfg: DecodeCfg, tensor: int, lengths: np.ndarray, layout: PagedLayout,
+                      pad_bits=BF16_NAN) -> np.ndarray:
+    """[num_pages, Hkv, page_size, d] bits; unused slots and pages hold ``pad_bits``."""
+    ps = layout.page_size
+    pool = np.full((layout.num_pages, cfg.Hkv, ps, cfg.d), pad_bits, np.uint16)
+    for b in range(cfg.B):
+        n = int(lengths[b])
+        nblk = (n + ps - 1) // ps
+        pages = layout.block_table[b, :nblk]
+        for h in range(cfg.Hkv):
+            rows = decode_kv_logical(cfg, tensor, b, h, n)
+            padded = np.full((nblk * ps, cfg.d), pad_bits, np.uint16)
+            padded[:n] = rows
+            pool[pages, h] = padded.reshape(nblk, ps, cfg.d)
+    return pool
+
+
+# ----------------------------------------------------------------------------
+# Work counting (for throughput figures; no attention arithmetic)
+# ----------------------------------------------------------------------------
+def visible_pairs(Nq: int, Nk: int, causal: bool) -> int:
+    """Number of (query, key) pairs a row-wise softmax sees.  Causal masking is
+    aligned bottom-right: key j is visible to query i iff j <= i + (Nk - Nq)."""
+    if not causal:
+        return Nq * Nk
+    if Nq > Nk:
+        raise ValueError("causal attention needs Nq <= Nk")
+    off = Nk - Nq
+    # row i sees i + off + 1 keys (never more than Nk since i <= Nq - 1)
+    return Nq * (off + 1) + Nq * (Nq - 1) // 2
+
+
+def prefill_flops(cfg: PrefillCfg) -> int:
+    """Algorithmic FLOPs: 2*d for Q.K^T plus 2*d for P.V per visible pair."""
+    return 4 * cfg.d * cfg.B * cfg.Hq * visible_pairs(cfg.Nq, cfg.Nk, cfg.causal)
+
+
+def prefill_bytes(cfg: PrefillCfg) -> int:
+    """Algorithmic HBM bytes: Q, K, V read once, O written once, LSE written once."""
+    q = cfg.B * cfg.Hq * cfg.Nq * cfg.d * 2
+    kv = 2 * cfg.B * cfg.Hkv * cfg.Nk * cfg.d * 2
+    return q + kv + q + cfg.B * cfg.Hq * cfg.Nq * 4
+
+
+def decode_bytes(cfg: DecodeCfg, lengths: np.ndarray) -> int:
+    """Algorithmic HBM bytes of one decode step: K and V of the live tokens, Q, O,
+    LSE, the lengths and (paged) the live block-table entries."""
+    tot = int(np.sum(lengths, dtype=np.int64))
+    kv = 2 * tot * cfg.Hkv * cfg.d * 2
+    qo = 2 * cfg.B * cfg.Hq * cfg.d * 2
+    lse = cfg.B * cfg.Hq * 4
+    lens = cfg.B * 4
+    table = 0
+    if cfg.paged:
+        table = 4 * sum((int(n) + cfg.page_size - 1) // cfg.page_size for n in lengths)
+    return kv + qo + lse + lens + table
+
+
+def decode_flops(cfg: DecodeCfg, lengths: np.ndarray) -> int:
+    return 4 * cfg.d * cfg.Hq * int(np.sum(lengths, dtype=np.int64))

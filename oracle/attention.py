@@ -1,0 +1,239 @@
+"""CPU oracle for exact attention, numpy float64.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import or call anything in this package.  The GPU product
+path never routes through it, and it shares no code with the GPU path.
+
+What it computes is the plain definition of attention,
+    O = softmax(scale * Q K^T [+ causal mask]) V,
+from the page "FlashAttention 완전 정리" (cell-devlog), section "Attention이 뭔가"
+(what attention is): the formula softmax(Q K^T / sqrt(d_k)) V, with Q K^T the
+all-pairs similarity matrix, softmax turning each row into probabilities, and the
+product with V the weighted sum.  It is run the way the same page's section
+"문제 — Attention은 메모리 병목이다" (attention is memory-bound) lays out standard
+attention: materialise S = Q K^T, take the row softmax of S, multiply by V.  The
+fused method reaches the same result (same page, section on FlashAttention 1:
+"accuracy unchanged, not an approximation"), so this definition is the parity
+target.
+
+Readings where the pages are silent (each one also listed in the design notes):
+  * scale is an explicit argument (the pages write 1/sqrt(d_k); the flash_attn_func
+    call on the page "메모리 장벽을 넘어" (tiptinker), section on the forward pass,
+    defaults softmax_scale to None);
+  * causal masking is aligned bottom-right: key j is visible to query i iff
+    j <= i + (Nk - Nq); causal with Nq > Nk is rejected;
+  * grouped-query heads: query head h reads KV head h // (Hq / Hkv);
+  * LSE = m + ln(l), natural log, over the visible keys only;
+  * layout [B, H, N, d] for Q, K, V, O;
+  * a decode step is one query row per sequence attending to the first
+    seqlens[b] cached keys; seqlens[b] == 0 gives O = 0 and LSE = -inf.
+
+Parity status: every function here is pinned by tests/test_oracle.py against
+brute force, closed forms and invariants (no function is parity unpinned).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# Prefill: three passes over a materialised score matrix
+# ---------------------------------------------------------------------------
+def _causal_visible(rows: np.ndarray, Nq: int, Nk: int) -> np.ndarray:
+    """Boolean [len(rows), Nk]: key j visible to query row i iff j <= i + (Nk - Nq)."""
+    j = np.arange(Nk)[None, :]
+    return j <= (rows[:, None] + (Nk - Nq))
+
+
+def attention_scores(q_rows: np.ndarray, k: np.ndarray, scale: float, causal: bool,
+                     rows: np.ndarray, Nq: int) -> np.ndarray:
+    """Pass 1: S = scale * Q K^T for the given query rows, masked entries -inf."""
+    s = scale * (q_rows @ k.T)
+    if causal:
+        s = np.where(_causal_visible(rows, Nq, k.shape[0]), s, -np.inf)
+    return s
+
+
+def softmax_rows(s: np.ndarray):
+    """Pass 2: row softmax of S.  Returns (P, m, l) with m the row max,
+    l = sum exp(S - m) and P = exp(S - m) / l (the m, f, l of the page
+    "Flash Attention: GPU 메모리_IO를 최적화하는..." (holysheep), section
+    "수학적 원리: Online Softmax 알고리즘" (math: online softmax))."""
+    m = s.max(axis=1, keepdims=True)
+    f = np.exp(s - m)
+    l = f.sum(axis=1, keepdims=True)
+    return f / l, m[:, 0], l[:, 0]
+
+
+def attention_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                   causal: bool, rows: np.ndarray, Nq: int):
+    """Attention for selected query rows of one head.
+
+    q_rows [R, d] are queries with indices ``rows`` (0-based, out of Nq);
+    k, v [Nk, d].  Returns (O [R, d], LSE [R]) in float64.
+    """
+    s = attention_scores(q_rows, k, scale, causal, rows, Nq)
+    p, m, l = softmax_rows(s)
+    o = p @ v                                           # pass 3
+    lse = m + np.log(l)
+    return o, lse
+
+
+def attention_prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                      causal: bool, row_block: int = 1024):
+    """Full prefill.  q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d] (float64 holding the exact
+    input values).  Returns O [B,Hq,Nq,d] and LSE [B,Hq,Nq], float64.
+
+    Rows are processed in blocks of ``row_block`` only to bound the size of the
+    materialised S; each block is the full three-pass computation for its rows.
+    """
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if Bk != B or dk != d or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if causal and Nq > Nk:
+        raise ValueError("causal attention needs Nq <= Nk")
+    G = Hq // Hkv
+    o = np.empty((B, Hq, Nq, d))
+    lse = np.empty((B, Hq, Nq))
+    for b in range(B):
+        for h in range(Hq):
+            kvh = h // G
+            for i0 in range(0, Nq, row_block):
+                rows = np.arange(i0, min(Nq, i0 + row_block))
+                o[b, h, rows], lse[b, h, rows] = attention_rows(
+                    q[b, h, rows], k[b, kvh], v[b, kvh], scale, causal, rows, Nq)
+    return o, lse
+
+
+def attention_probabilities(q: np.ndarray, k: np.ndarray, scale: float, causal: bool):
+    """P for one head, q [Nq,d], k [Nk,d]: the softmax rows pass 2 produces."""
+    rows = np.arange(q.shape[0])
+    p, _, _ = softmax_rows(attention_scores(q, k, scale, causal, rows, q.shape[0]))
+    return p
+
+
+# ---------------------------------------------------------------------------
+# Decode: one query per sequence against the first seqlens[b] cached keys
+# ---------------------------------------------------------------------------
+def gather_paged(pool: np.ndarray, block_table: np.ndarray, b: int, kvh: int, length: int,
+                 page_size: int) -> np.ndarray:
+    """Rows 0..length-1 of sequence b, KV head kvh, from a paged pool
+    [num_pages, Hkv, page_size, d]: token t lives in page block_table[b, t // page_size],
+    slot t % page_size (the paged KV cache of the page "메모리 장벽을 넘어" (tiptinker),
+    section "2. FlashInfer" (PagedAttention integration))."""
+    t = np.arange(length)
+    pages = block_table[b, t // page_size]
+    return pool[pages, kvh, t % page_size]
+
+
+def attention_decode(q: np.ndarray, kcache: np.ndarray, vcache: np.ndarray,
+                     seqlens: np.ndarray, scale: float, block_table: np.ndarray | None = None,
+                     page_size: int = 16):
+    """q [B,Hq,d].  Contiguous cache (block_table None): k/vcache [B,Hkv,Nmax,d];
+    paged: [num_pages,Hkv,page_size,d] with block_table [B, max_blocks].
+    Returns O [B,Hq,d], LSE [B,Hq] (float64)."""
+    B, Hq, d = q.shape
+    Hkv = kcache.shape[1]
+    G = Hq // Hkv
+    o = np.zeros((B, Hq, d))
+    lse = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        n = int(seqlens[b])
+        if n == 0:
+            continue
+        for kvh in range(Hkv):
+            if block_table is None:
+                K = kcache[b, kvh, :n]
+                V = vcache[b, kvh, :n]
+            else:
+                K = gather_paged(kcache, block_table, b, kvh, n, page_size)
+                V = gather_paged(vcache, block_table, b, kvh, n, page_size)
+            hs = slice(kvh * G, (kvh + 1) * G)
+            ob, lb = attention_rows(q[b, hs], K, V, scale, False, np.arange(G), G)
+            o[b, hs], lse[b, hs] = ob, lb
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Combining partial results over disjoint key sets
+# ---------------------------------------------------------------------------
+def merge_partials(o_parts: np.ndarray, lse_parts: np.ndarray):
+    """Combine attention results computed over disjoint key subsets of one row.
+
+    o_parts [S, d] are the per-subset normalised outputs, lse_parts [S] their
+    log-sum-exps (-inf for an empty subset).  From l = sum exp(x - m) (page
+    "Flash Attention: GPU 메모리_IO를 최적화하는...", section on online softmax),
+    the subset with statistics (m_s, l_s) contributes exp(lse_s) = exp(m_s) l_s to the
+    full row's normaliser, so the full row is the exp(lse_s)-weighted mean of the
+    o_s and its LSE is ln sum exp(lse_s).
+    """
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    M = np.max(lse_parts)
+    if M == -np.inf:
+        return np.zeros(o_parts.shape[1:]), -np.inf
+    w = np.exp(lse_parts - M)
+    W = w.sum()
+    return (w[:, None] * o_parts).sum(axis=0) / W, M + math.log(W)
+
+
+# ---------------------------------------------------------------------------
+# Twins used only to check the oracle itself
+# ---------------------------------------------------------------------------
+def brute_force_attention(q, k, v, scale: float, causal: bool):
+    """Pure-Python scalar attention for tiny inputs (lists or arrays of one head:
+    q [Nq][d], k [Nk][d], v [Nk][d]).  math.exp and math.fsum, no numpy.
+    Returns (O as nested lists, LSE as a list)."""
+    Nq, Nk = len(q), len(k)
+    d = len(q[0])
+    out, lses = [], []
+    for i in range(Nq):
+        scores = []
+        for j in range(Nk):
+            if causal and j > i + (Nk - Nq):
+                continue
+            scores.append((j, float(scale) * math.fsum(float(q[i][t]) * float(k[j][t])
+                                                       for t in range(d))))
+        mx = max(s for _, s in scores)
+        wts = [(j, math.exp(s - mx)) for j, s in scores]
+        tot = math.fsum(w for _, w in wts)
+        out.append([math.fsum(w * float(v[j][c]) for j, w in wts) / tot for c in range(d)])
+        lses.append(mx + math.log(tot))
+    return out, lses
+
+
+def online_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool,
+                     block: int):
+    """One head, key blocks of size ``block`` visited in order with the online-softmax
+    recurrence (page "FlashAttention 완전 정리", section "Tiling": track the running max
+    per block and update earlier partial results as each block arrives):
+
+        m' = max(m, rowmax S_j)
+        l' = exp(m - m') l + rowsum exp(S_j - m')
+        A' = exp(m - m') A + exp(S_j - m') V_j
+    and O = A / l at the end.  Used only to check the two-pass oracle."""
+    Nq, d = q.shape
+    Nk = k.shape[0]
+    rows = np.arange(Nq)
+    m = np.full(Nq, -np.inf)
+    l = np.zeros(Nq)
+    acc = np.zeros((Nq, d))
+    for j0 in range(0, Nk, block):
+        j1 = min(Nk, j0 + block)
+        s = scale * (q @ k[j0:j1].T)
+        if causal:
+            vis = np.arange(j0, j1)[None, :] <= (rows[:, None] + (Nk - Nq))
+            s = np.where(vis, s, -np.inf)
+        m_new = np.maximum(m, s.max(axis=1))
+        # rows with no visible key so far keep m = -inf; guard the -inf - -inf case
+        safe = np.where(np.isfinite(m_new), m_new, 0.0)
+        alpha = np.where(np.isfinite(m), np.exp(m - safe), 0.0)
+        p = np.exp(s - safe[:, None])
+        l = alpha * l + p.sum(axis=1)
+        acc = alpha[:, None] * acc + p @ v[j0:j1]
+        m = m_new
+    return acc / l[:, None], m + np.log(l)

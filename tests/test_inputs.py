@@ -1,0 +1,86 @@
+"""Checks of the seeded input generators and work counting (CPU only)."""
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs as ai
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100_000).astype(np.float32) * 3,
+                        rng.uniform(-1e30, 1e30, 1000).astype(np.float32),
+                        np.array([0.0, -0.0, 1.0, 1.00390625, 1.01171875, 65504.0], np.float32)])
+    # exact ties: low 16 bits == 0x8000, with both parities of the kept lsb
+    ties = (np.arange(64, dtype=np.uint32) << 17 | 0x3F808000).view(np.float32)
+    x = np.concatenate([x, ties, -ties])
+    ours = ai.to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+    back = ai.bf16_bits_to_f64(ours)
+    np.testing.assert_array_equal(back, torch.from_numpy(x).to(torch.bfloat16).double().numpy())
+
+
+def test_streams_are_deterministic_and_independent():
+    a = ai.normal_bf16(5, ai.T_K, 1, 2, (8, 4))
+    b = ai.normal_bf16(5, ai.T_K, 1, 2, (8, 4))
+    c = ai.normal_bf16(5, ai.T_V, 1, 2, (8, 4))
+    np.testing.assert_array_equal(a, b)
+    assert (a != c).any()
+
+
+def test_prefill_q_multiplier_applied_before_rounding():
+    cfg = ai.PrefillCfg("t", 1, 1, 1, 4, 4, 8, True, seed=9, q_mult=3.0)
+    q = ai.prefill_head(cfg, ai.T_Q, 0, 0)
+    x = np.random.default_rng(np.random.SeedSequence([9, ai.T_Q, 0, 0])).standard_normal(
+        (4, 8), dtype=np.float32) * np.float32(3.0)
+    np.testing.assert_array_equal(q, ai.to_bf16_bits(x))
+
+
+def test_paged_layout_is_a_partition_of_the_pool():
+    lens = np.array([17, 1, 32, 0, 100], np.int32)
+    lay = ai.paged_layout(lens, 16, seed=3, extra_pages=3)
+    used = []
+    for b, n in enumerate(lens):
+        nb = (n + 15) // 16
+        row = lay.block_table[b]
+        assert (row[:nb] >= 0).all() and (row[nb:] == -1).all()
+        used += row[:nb].tolist()
+    assert len(used) == len(set(used)) == sum((n + 15) // 16 for n in lens)
+    assert max(used) < lay.num_pages
+
+
+def test_paged_cache_holds_logical_rows():
+    cfg = ai.DecodeCfg("t", B=2, Hq=4, Hkv=2, d=8, seed=11, paged=True, len_range=(3, 40))
+    lens = ai.decode_lengths(cfg)
+    lay = ai.paged_layout(lens, 16, cfg.seed)
+    pool = ai.build_paged_cache(cfg, ai.T_K, lens, lay)
+    for b in range(2):
+        for h in range(2):
+            rows = ai.decode_kv_logical(cfg, ai.T_K, b, h, int(lens[b]))
+            for t in range(int(lens[b])):
+                np.testing.assert_array_equal(pool[lay.block_table[b, t // 16], h, t % 16], rows[t])
+
+
+def test_pair_counts_match_the_pages():
+    # N^2 counts printed on the page "Flash Attention: GPU 메모리_IO를 최적화하는...",
+    # section "왜 Flash Attention이 필요한가?": 512 tokens -> about 262,000 weights,
+    # 4096 tokens -> about 16,000,000.
+    assert ai.visible_pairs(512, 512, False) == 262_144
+    assert abs(ai.visible_pairs(4096, 4096, False) - 16_000_000) / 16e6 < 0.05
+    # causal: 1 + 2 + ... + N
+    assert ai.visible_pairs(512, 512, True) == 512 * 513 // 2
+    assert ai.visible_pairs(3, 10, True) == 8 + 9 + 10
+    with pytest.raises(ValueError):
+        ai.visible_pairs(4, 3, True)
+
+
+def test_config_work_figures():
+    c1 = ai.CONFIGS["tiny_prefill"]
+    assert ai.prefill_flops(c1) == 4 * 64 * 4 * 131_328
+    c2 = ai.CONFIGS["llama2_7b_prefill"]
+    assert ai.prefill_flops(c2) == 137_506_062_336
+    assert ai.prefill_flops(ai.CONFIGS["llama2_7b_prefill_noncausal"]) == 274_877_906_944
+    assert ai.prefill_flops(ai.CONFIGS["long_prefill_32k"]) == 8_796_361_457_664
+    c4 = ai.CONFIGS["gqa_decode_contig"]
+    assert ai.decode_bytes(c4, ai.decode_lengths(c4)) == 2_148_540_672

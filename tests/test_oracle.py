@@ -1,0 +1,341 @@
+"""Pins for the CPU oracle: brute force, closed forms, invariants (CPU only).
+
+Each test checks the oracle against something other than itself, chosen so that a
+plausible slip (a dropped term, a wrong sign or index, a transposed operand, a
+mis-aligned causal mask, a wrong head mapping) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import (attention_decode, attention_prefill, attention_probabilities, attention_rows,
+                    brute_force_attention, merge_partials, online_attention, softmax_rows)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rnd(seed, *shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# ----------------------------------------------------------------------------- brute force
+@pytest.mark.parametrize("Nq,Nk,d,causal", [
+    (1, 1, 1, False), (3, 5, 2, False), (5, 5, 3, True), (4, 7, 4, True), (8, 8, 4, True),
+    (2, 8, 3, False), (6, 6, 1, True)])
+def test_matches_brute_force(Nq, Nk, d, causal):
+    q, k, v = rnd(1, Nq, d), rnd(2, Nk, d), rnd(3, Nk, d)
+    scale = 0.7
+    o, lse = attention_prefill(q[None, None], k[None, None], v[None, None], scale, causal)
+    bo, bl = brute_force_attention(q.tolist(), k.tolist(), v.tolist(), scale, causal)
+    np.testing.assert_allclose(o[0, 0], np.array(bo), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0, 0], np.array(bl), rtol=0, atol=1e-12)
+
+
+def test_brute_force_batched_gqa():
+    B, Hq, Hkv, Nq, Nk, d = 2, 4, 2, 3, 6, 2
+    q, k, v = rnd(4, B, Hq, Nq, d), rnd(5, B, Hkv, Nk, d), rnd(6, B, Hkv, Nk, d)
+    o, lse = attention_prefill(q, k, v, 0.5, True)
+    for b in range(B):
+        for h in range(Hq):
+            kvh = h // (Hq // Hkv)
+            bo, bl = brute_force_attention(q[b, h].tolist(), k[b, kvh].tolist(),
+                                           v[b, kvh].tolist(), 0.5, True)
+            np.testing.assert_allclose(o[b, h], bo, atol=1e-12, rtol=0)
+            np.testing.assert_allclose(lse[b, h], bl, atol=1e-12, rtol=0)
+
+
+def test_row_blocking_does_not_change_result():
+    q, k, v = rnd(7, 1, 2, 37, 4), rnd(8, 1, 2, 37, 4), rnd(9, 1, 2, 37, 4)
+    a = attention_prefill(q, k, v, 0.3, True, row_block=1024)
+    b = attention_prefill(q, k, v, 0.3, True, row_block=5)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+# ----------------------------------------------------------------------------- worked example
+def test_worked_example_golden():
+    g = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    q = np.array(g["q"])[None, None]
+    k = np.array(g["k"])[None, None]
+    v = np.array(g["v"])[None, None]
+    o, lse = attention_prefill(q, k, v, g["scale"], False)
+    assert abs(o[0, 0, 0, 0] - g["expected_o"][0][0]) <= g["tolerance"] * 4
+    assert abs(lse[0, 0, 0] - g["expected_lse"][0]) <= g["tolerance"] * 2
+
+
+# ----------------------------------------------------------------------------- closed forms
+def test_single_key_returns_that_value():
+    q, k, v = rnd(10, 1, 1, 1, 8), rnd(11, 1, 1, 1, 8), rnd(12, 1, 1, 1, 8)
+    o, lse = attention_prefill(q, k, v, 0.25, False)
+    np.testing.assert_array_equal(o[0, 0, 0], v[0, 0, 0])
+    assert lse[0, 0, 0] == pytest.approx(0.25 * float(q[0, 0, 0] @ k[0, 0, 0]), abs=1e-15)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_scale_is_mean_of_visible_values(causal):
+    Nq, Nk, d = 6, 9, 3
+    q, k, v = rnd(13, Nq, d), rnd(14, Nk, d), rnd(15, Nk, d)
+    o, lse = attention_prefill(q[None, None], k[None, None], v[None, None], 0.0, causal)
+    for i in range(Nq):
+        n = (i + Nk - Nq + 1) if causal else Nk
+        np.testing.assert_allclose(o[0, 0, i], v[:n].mean(axis=0), atol=1e-14)
+        assert lse[0, 0, i] == pytest.approx(math.log(n), abs=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_equal_key_rows_give_uniform_weights(causal):
+    Nq, Nk, d = 5, 8, 4
+    q, v = rnd(16, Nq, d), rnd(17, Nk, d)
+    krow = rnd(18, d)
+    k = np.tile(krow, (Nk, 1))
+    scale = 0.9
+    o, lse = attention_prefill(q[None, None], k[None, None], v[None, None], scale, causal)
+    for i in range(Nq):
+        n = (i + Nk - Nq + 1) if causal else Nk
+        np.testing.assert_allclose(o[0, 0, i], v[:n].mean(axis=0), atol=1e-13)
+        assert lse[0, 0, i] == pytest.approx(scale * q[i] @ krow + math.log(n), abs=1e-13)
+
+
+# ----------------------------------------------------------------------------- causal mask
+def test_causal_first_row_is_first_value():
+    N, d = 16, 8
+    q, k, v = rnd(19, N, d), rnd(20, N, d), rnd(21, N, d)
+    o, lse = attention_prefill(q[None, None], k[None, None], v[None, None], 0.4, True)
+    np.testing.assert_array_equal(o[0, 0, 0], v[0])
+    assert lse[0, 0, 0] == pytest.approx(0.4 * q[0] @ k[0], abs=1e-15)
+
+
+def test_causal_row_i_is_noncausal_over_prefix():
+    N, d = 12, 5
+    q, k, v = rnd(22, N, d), rnd(23, N, d), rnd(24, N, d)
+    o, lse = attention_prefill(q[None, None], k[None, None], v[None, None], 0.6, True)
+    for i in range(N):
+        bo, bl = brute_force_attention([q[i].tolist()], k[:i + 1].tolist(), v[:i + 1].tolist(),
+                                       0.6, False)
+        np.testing.assert_allclose(o[0, 0, i], bo[0], atol=1e-12)
+        assert lse[0, 0, i] == pytest.approx(bl[0], abs=1e-12)
+
+
+def test_causal_bottom_right_alignment():
+    # Nq < Nk: the last query row sees every key, the first sees Nk - Nq + 1 keys.
+    Nq, Nk, d = 3, 10, 4
+    q, k, v = rnd(25, Nq, d), rnd(26, Nk, d), rnd(27, Nk, d)
+    o, _ = attention_prefill(q[None, None], k[None, None], v[None, None], 0.5, True)
+    full, _ = attention_prefill(q[None, None], k[None, None], v[None, None], 0.5, False)
+    np.testing.assert_allclose(o[0, 0, -1], full[0, 0, -1], atol=1e-14)
+    first, _ = attention_rows(q[:1], k[:Nk - Nq + 1], v[:Nk - Nq + 1], 0.5, False,
+                              np.arange(1), 1)
+    np.testing.assert_allclose(o[0, 0, 0], first[0], atol=1e-14)
+
+
+def test_causal_rejects_more_queries_than_keys():
+    with pytest.raises(ValueError):
+        attention_prefill(rnd(1, 1, 1, 4, 2), rnd(2, 1, 1, 3, 2), rnd(3, 1, 1, 3, 2), 1.0, True)
+
+
+# ----------------------------------------------------------------------------- softmax invariants
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_rows_sum_to_one(causal):
+    q, k = rnd(28, 9, 4), rnd(29, 9, 4)
+    p = attention_probabilities(q, k, 1.3, causal)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-14)
+    assert (p >= 0).all()
+    if causal:
+        assert (np.triu(p, 1) == 0).all()
+
+
+def test_constant_values_give_constant_output():
+    q, k = rnd(30, 1, 1, 7, 4), rnd(31, 1, 1, 7, 4)
+    vrow = rnd(32, 4)
+    v = np.tile(vrow, (1, 1, 7, 1))
+    for causal in (False, True):
+        o, _ = attention_prefill(q, k, v, 0.8, causal)
+        np.testing.assert_allclose(o[0, 0], np.tile(vrow, (7, 1)), atol=1e-14)
+
+
+def test_score_shift_invariance():
+    s = rnd(33, 4, 6)
+    c = rnd(34, 4)[:, None] * 50.0
+    p0, m0, l0 = softmax_rows(s)
+    p1, m1, l1 = softmax_rows(s + c)
+    np.testing.assert_allclose(p1, p0, atol=1e-14)
+    np.testing.assert_allclose(m1 + np.log(l1), m0 + np.log(l0) + c[:, 0], atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_shift_invariance(causal):
+    # Adding u to every key row adds scale * q.u to a whole score row.
+    q, k, v = rnd(35, 6, 4), rnd(36, 6, 4), rnd(37, 6, 4)
+    u = rnd(38, 4)
+    scale = 0.7
+    o0, l0 = attention_prefill(q[None, None], k[None, None], v[None, None], scale, causal)
+    o1, l1 = attention_prefill(q[None, None], (k + u)[None, None], v[None, None], scale, causal)
+    np.testing.assert_allclose(o1, o0, atol=1e-13)
+    np.testing.assert_allclose(l1[0, 0], l0[0, 0] + scale * q @ u, atol=1e-13)
+
+
+def test_lse_bounds_and_convex_hull():
+    Nq, Nk, d = 8, 11, 3
+    q, k, v = rnd(39, Nq, d), rnd(40, Nk, d), rnd(41, Nk, d)
+    scale = 1.1
+    for causal in (False, True):
+        o, lse = attention_prefill(q[None, None], k[None, None], v[None, None], scale, causal)
+        for i in range(Nq):
+            n = (i + Nk - Nq + 1) if causal else Nk
+            s = scale * (k[:n] @ q[i])
+            assert s.max() - 1e-12 <= lse[0, 0, i] <= s.max() + math.log(n) + 1e-12
+            assert (o[0, 0, i] >= v[:n].min(axis=0) - 1e-12).all()
+            assert (o[0, 0, i] <= v[:n].max(axis=0) + 1e-12).all()
+
+
+def test_noncausal_key_permutation_equivariance():
+    q, k, v = rnd(42, 5, 4), rnd(43, 9, 4), rnd(44, 9, 4)
+    perm = np.random.default_rng(45).permutation(9)
+    o0, l0 = attention_prefill(q[None, None], k[None, None], v[None, None], 0.5, False)
+    o1, l1 = attention_prefill(q[None, None], k[perm][None, None], v[perm][None, None], 0.5, False)
+    np.testing.assert_allclose(o1, o0, atol=1e-14)
+    np.testing.assert_allclose(l1, l0, atol=1e-14)
+
+
+def test_swapping_k_and_v_roles_is_detected():
+    # A transposed operand (using V where K belongs) must change the result.
+    q, k, v = rnd(46, 4, 4), rnd(47, 6, 4), rnd(48, 6, 4)
+    o, _ = attention_prefill(q[None, None], k[None, None], v[None, None], 0.5, False)
+    bad, _ = attention_prefill(q[None, None], v[None, None], k[None, None], 0.5, False)
+    assert np.abs(o - bad).max() > 1e-3
+
+
+# ----------------------------------------------------------------------------- online recurrence
+@pytest.mark.parametrize("causal", [False, True])
+def test_online_one_block_equals_two_pass(causal):
+    q, k, v = rnd(49, 10, 4), rnd(50, 10, 4), rnd(51, 10, 4)
+    o2, l2 = attention_prefill(q[None, None], k[None, None], v[None, None], 0.9, causal)
+    o1, l1 = online_attention(q, k, v, 0.9, causal, block=10)
+    np.testing.assert_allclose(o1, o2[0, 0], atol=1e-15, rtol=0)
+    np.testing.assert_allclose(l1, l2[0, 0], atol=1e-15, rtol=0)
+
+
+@pytest.mark.parametrize("block", [1, 3, 4, 7, 16])
+@pytest.mark.parametrize("causal", [False, True])
+def test_online_many_blocks_equals_two_pass(block, causal):
+    Nq, Nk = 9, 13
+    q, k, v = rnd(52, Nq, 5) * 3, rnd(53, Nk, 5), rnd(54, Nk, 5)
+    o2, l2 = attention_prefill(q[None, None], k[None, None], v[None, None], 0.8, causal)
+    o1, l1 = online_attention(q, k, v, 0.8, causal, block=block)
+    np.testing.assert_allclose(o1, o2[0, 0], atol=1e-12)
+    np.testing.assert_allclose(l1, l2[0, 0], atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- GQA
+def test_gqa_equals_repeated_heads():
+    B, Hq, Hkv, N, d = 2, 6, 2, 7, 4
+    q, k, v = rnd(55, B, Hq, N, d), rnd(56, B, Hkv, N, d), rnd(57, B, Hkv, N, d)
+    o, lse = attention_prefill(q, k, v, 0.5, True)
+    G = Hq // Hkv
+    o2, lse2 = attention_prefill(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), 0.5, True)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, lse2)
+    # a wrong mapping (h % Hkv) gives a different answer on these inputs
+    o3, _ = attention_prefill(q, np.tile(k, (1, G, 1, 1)), np.tile(v, (1, G, 1, 1)), 0.5, True)
+    assert np.abs(o3 - o).max() > 1e-3
+
+
+# ----------------------------------------------------------------------------- decode
+def _decode_case(seed=60, B=3, Hq=4, Hkv=2, d=4, lens=(5, 1, 9), ps=4):
+    rng = np.random.default_rng(seed)
+    Nmax = max(lens)
+    q = rng.standard_normal((B, Hq, d))
+    kc = np.full((B, Hkv, Nmax + 2, d), np.nan)
+    vc = np.full((B, Hkv, Nmax + 2, d), np.nan)
+    for b, n in enumerate(lens):
+        kc[b, :, :n] = rng.standard_normal((Hkv, n, d))
+        vc[b, :, :n] = rng.standard_normal((Hkv, n, d))
+    return q, kc, vc, np.array(lens, np.int32)
+
+
+def _to_paged(kc, lens, ps, perm_seed):
+    B, Hkv, _, d = kc.shape
+    nblk = [(n + ps - 1) // ps for n in lens]
+    P = sum(nblk) + 2
+    perm = np.random.default_rng(perm_seed).permutation(P)
+    table = np.full((B, max(nblk)), -1, np.int32)
+    pool = np.full((P, Hkv, ps, d), np.nan)
+    off = 0
+    for b, n in enumerate(lens):
+        table[b, :nblk[b]] = perm[off:off + nblk[b]]
+        off += nblk[b]
+        for t in range(n):
+            pool[table[b, t // ps], :, t % ps] = kc[b, :, t]
+    return pool, table
+
+
+def test_decode_matches_brute_force_and_ignores_padding():
+    q, kc, vc, lens = _decode_case()
+    o, lse = attention_decode(q, kc, vc, lens, 0.5)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    for b, n in enumerate(lens):
+        for h in range(4):
+            kvh = h // 2
+            bo, bl = brute_force_attention([q[b, h].tolist()], kc[b, kvh, :n].tolist(),
+                                           vc[b, kvh, :n].tolist(), 0.5, False)
+            np.testing.assert_allclose(o[b, h], bo[0], atol=1e-12)
+            assert lse[b, h] == pytest.approx(bl[0], abs=1e-12)
+
+
+def test_decode_is_last_row_of_causal_prefill():
+    rng = np.random.default_rng(61)
+    n, d = 11, 4
+    Q, K, V = rng.standard_normal((n, d)), rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    op, lp = attention_prefill(Q[None, None], K[None, None], V[None, None], 0.7, True)
+    od, ld = attention_decode(Q[-1][None, None], K[None, None], V[None, None],
+                              np.array([n], np.int32), 0.7)
+    np.testing.assert_allclose(od[0, 0], op[0, 0, -1], atol=1e-14)
+    assert ld[0, 0] == pytest.approx(lp[0, 0, -1], abs=1e-14)
+    # bottom-right: one causal query against n keys is the decode row too
+    o1, l1 = attention_prefill(Q[-1][None, None, None], K[None, None], V[None, None], 0.7, True)
+    np.testing.assert_allclose(o1[0, 0, 0], od[0, 0], atol=1e-14)
+
+
+def test_paged_equals_contiguous_and_page_order_is_irrelevant():
+    q, kc, vc, lens = _decode_case(seed=62, lens=(7, 4, 13))
+    o0, l0 = attention_decode(q, kc, vc, lens, 0.6)
+    for seed in (1, 2):
+        kp, table = _to_paged(kc, lens, 4, seed)
+        vp, table2 = _to_paged(vc, lens, 4, seed)
+        assert (table == table2).all()
+        o1, l1 = attention_decode(q, kp, vp, lens, 0.6, block_table=table, page_size=4)
+        np.testing.assert_array_equal(o1, o0)
+        np.testing.assert_array_equal(l1, l0)
+
+
+def test_decode_zero_length():
+    q, kc, vc, _ = _decode_case()
+    o, lse = attention_decode(q, kc, vc, np.array([0, 1, 0], np.int32), 0.5)
+    assert (o[0] == 0).all() and (lse[0] == -np.inf).all()
+    assert (o[2] == 0).all() and np.isfinite(lse[1]).all()
+
+
+# ----------------------------------------------------------------------------- split + merge
+def test_merge_of_halves_equals_full_row():
+    rng = np.random.default_rng(63)
+    q, k, v = rng.standard_normal((1, 6)), rng.standard_normal((20, 6)), rng.standard_normal((20, 6))
+    full_o, full_l = attention_rows(q, k, v, 0.4, False, np.arange(1), 1)
+    for cuts in ([7], [1, 19], [3, 9, 15]):
+        edges = [0] + cuts + [20]
+        parts = [attention_rows(q, k[a:b], v[a:b], 0.4, False, np.arange(1), 1)
+                 for a, b in zip(edges[:-1], edges[1:])]
+        o, l = merge_partials(np.stack([p[0][0] for p in parts]), np.array([p[1][0] for p in parts]))
+        np.testing.assert_allclose(o, full_o[0], atol=1e-14)
+        assert l == pytest.approx(full_l[0], abs=1e-13)
+
+
+def test_merge_with_empty_split_is_identity():
+    o = np.array([[1.0, 2.0], [9.0, 9.0]])
+    r, l = merge_partials(o, np.array([0.3, -np.inf]))
+    np.testing.assert_array_equal(r, o[0])
+    assert l == 0.3
+    r, l = merge_partials(o, np.array([-np.inf, -np.inf]))
+    assert (r == 0).all() and l == -np.inf
