@@ -1,0 +1,304 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+One step = one pass of the whole hot path on one batch of synthetic input:
+  * prefill, Llama-2-7B-shaped causal attention (B=4, H=32, N=2048, d=128), and
+  * decode, paged GQA (B=8, Hq=32, Hkv=8, d=128, 16-token pages, lengths U[1024, 131072]).
+Inputs are seeded, synthetic and resident in HBM before timing starts.  W untimed warmup
+steps, then K timed steps bracketed by device synchronisation; each kernel launch is
+also bracketed by HIP events on the stream it runs on.
+
+Prints ONE JSON line.  `value` is the prefill throughput in TFLOP/s (algorithmic FLOPs
+4*d per visible query-key pair); the decode half of the metric (KV GB/s) is reported in
+the `decode` object.  Each carries a `roofline` (dense bf16 MFMA peak for prefill, HBM
+peak for decode).  `cpu_baseline` times the CPU oracle on a bounded sample of the same
+prefill workload on this host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import attn_inputs as ai  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "prefill attention TFLOPS and decode KV GB/s at 1 MI355X, % of roofline"
+PREFILL_CFG = "llama2_7b_prefill"
+DECODE_CFG = "paged_gqa_decode"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip the other workloads (non-causal, 32K prefill, contiguous decode)")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="approximate CPU time budget of the oracle sample")
+    return p.parse_args()
+
+
+def to_dev(bits):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    return t.cuda()
+
+
+def kernel_sources_digest() -> str:
+    h = hashlib.sha256()
+    cdir = os.path.join(ROOT, "io_aware_exact_attention_amd", "csrc")
+    for name in sorted(os.listdir(cdir)):
+        with open(os.path.join(cdir, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch recorded from rocprofv3 counter runs in profiles/, if they
+    were taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    digest = kernel_sources_digest()
+    for line in open(path):
+        m = re.match(r"\|\s*" + re.escape(kernel) + r"\s*\|\s*([0-9a-f]+)\s*\|\s*(\d+)\s*\|", line)
+        if m and m.group(1) == digest:
+            return int(m.group(2))
+    return None
+
+
+# ------------------------------------------------------------------------------ workloads
+def prefill_setup(name):
+    import torch
+    cfg = ai.CONFIGS[name]
+    q, k, v = ai.prefill_inputs(cfg)
+    dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+    o = torch.empty_like(dq)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    return cfg, (dq, dk, dv, o, lse)
+
+
+def decode_setup(name):
+    import torch
+    cfg = ai.CONFIGS[name]
+    lens = ai.decode_lengths(cfg)
+    q = ai.decode_q(cfg)
+    if cfg.paged:
+        lay = ai.paged_layout(lens, cfg.page_size, cfg.seed)
+        kc = ai.build_paged_cache(cfg, ai.T_K, lens, lay, pad_bits=np.uint16(0))
+        vc = ai.build_paged_cache(cfg, ai.T_V, lens, lay, pad_bits=np.uint16(0))
+        table = torch.from_numpy(lay.block_table).cuda()
+        maxlen = int(lens.max())
+    else:
+        maxlen = cfg.fixed_len
+        kc = ai.build_contig_cache(cfg, ai.T_K, lens, maxlen, pad_bits=np.uint16(0))
+        vc = ai.build_contig_cache(cfg, ai.T_V, lens, maxlen, pad_bits=np.uint16(0))
+        table = None
+    dq, dkc, dvc = to_dev(q), to_dev(kc), to_dev(vc)
+    del kc, vc
+    o = torch.empty_like(dq)
+    lse = torch.empty((cfg.B, cfg.Hq), dtype=torch.float32, device="cuda")
+    seq = torch.from_numpy(lens).cuda()
+    return cfg, lens, maxlen, (dq, dkc, dvc, table, seq, o, lse)
+
+
+def time_kernel(fn, steps, warmup):
+    """Average microseconds per call, from HIP events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)]
+    return float(np.mean(per)), float(np.median(per)), float(np.min(per))
+
+
+# ------------------------------------------------------------------------------ CPU baseline
+def cpu_baseline(budget_s: float):
+    """Time the fp64 oracle on whole heads of the prefill workload until ~budget_s."""
+    from oracle import attention_rows
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    cfg = ai.CONFIGS[PREFILL_CFG]
+    rows = np.arange(cfg.Nq)
+    flops = 0
+    heads = 0
+    t_total = 0.0
+    for h in range(cfg.Hq):
+        q = ai.bf16_bits_to_f64(ai.prefill_head(cfg, ai.T_Q, 0, h))
+        k = ai.bf16_bits_to_f64(ai.prefill_head(cfg, ai.T_K, 0, h))
+        v = ai.bf16_bits_to_f64(ai.prefill_head(cfg, ai.T_V, 0, h))
+        t0 = time.perf_counter()
+        for i0 in range(0, cfg.Nq, 1024):
+            attention_rows(q[i0:i0 + 1024], k, v, cfg.scale, cfg.causal, rows[i0:i0 + 1024],
+                           cfg.Nq)
+        t_total += time.perf_counter() - t0
+        heads += 1
+        flops += 4 * cfg.d * ai.visible_pairs(cfg.Nq, cfg.Nk, cfg.causal)
+        if t_total >= budget_s:
+            break
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{heads} whole heads (b=0, h=0..{heads - 1}) of {PREFILL_CFG}, "
+                      f"{t_total:.1f} s, numpy fp64 three-pass"}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ------------------------------------------------------------------------------ main
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the attention kernels "
+              "here have no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import io_aware_exact_attention_amd as mi
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    pcfg, (q, k, v, o, lse) = prefill_setup(PREFILL_CFG)
+    dcfg, lens, maxlen, (dq, dkc, dvc, table, seq, do, dlse) = decode_setup(DECODE_CFG)
+    ws = mi.decode_workspace(dcfg.B, dcfg.Hq, dcfg.Hkv, dcfg.d, maxlen, 0)
+
+    def prefill_call():
+        mi.attn_fwd_prefill(q, k, v, o, lse, pcfg.causal, pcfg.scale, stream)
+
+    def decode_call():
+        mi.attn_fwd_decode(dq, dkc, dvc, table, seq, do, dlse, maxlen, dcfg.scale, 0, ws,
+                           stream=stream)
+
+    # warmup, then K timed steps (prefill + decode), each launch bracketed by events
+    for _ in range(args.warmup):
+        prefill_call()
+        decode_call()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
+    t_wall0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        prefill_call()
+        ev[2 * i + 1].record(stream)
+        decode_call()
+        ev[2 * i + 2].record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    p_us = [ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(args.steps)]
+    d_us = [ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) * 1e3 for i in range(args.steps)]
+    p_avg, d_avg = float(np.mean(p_us)), float(np.mean(d_us))
+
+    p_flops = ai.prefill_flops(pcfg)
+    p_tflops = p_flops / (p_avg * 1e-6) / 1e12
+    d_bytes = ai.decode_bytes(dcfg, lens)
+    d_gbs = d_bytes / (d_avg * 1e-6) / 1e9
+    props = torch.cuda.get_device_properties(0)
+
+    out = {
+        "metric": METRIC,
+        "value": round(p_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded i.i.d. N(0,1) draws rounded to bf16",
+        "config": {
+            "workload": "prefill llama2_7b_prefill (causal, B=4, H=32, N=2048, d=128) + decode "
+                        "paged_gqa_decode (B=8, Hq=32, Hkv=8, d=128, page 16, "
+                        f"sum(len)={int(lens.sum())}, max len={maxlen})",
+            "prefill": {"B": pcfg.B, "Hq": pcfg.Hq, "Hkv": pcfg.Hkv, "Nq": pcfg.Nq,
+                        "Nk": pcfg.Nk, "d": pcfg.d, "causal": pcfg.causal},
+            "decode": {"B": dcfg.B, "Hq": dcfg.Hq, "Hkv": dcfg.Hkv, "d": dcfg.d,
+                       "page_size": dcfg.page_size, "lengths": lens.tolist(),
+                       "num_splits": mi.attn_decode_num_splits(dcfg.B, dcfg.Hq, dcfg.Hkv,
+                                                               dcfg.d, maxlen, 0)},
+        },
+        "roofline": {"bound": "mfma", "achieved": round(p_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic("prefill_kernel<128,causal>"),
+                     "kernel": "prefill_kernel<128, causal>",
+                     "us_per_launch": round(p_avg, 2), "flops_per_launch": p_flops},
+        "decode": {
+            "value": round(d_gbs, 1), "unit": "GB/s", "us_per_step": round(d_avg, 2),
+            "roofline": {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(d_gbs / PEAK_HBM_GBS, 4),
+                         "traffic": recorded_traffic("decode_split_kernel<128,paged>"),
+                         "kernel": "decode_split_kernel<128, paged> + decode_merge_kernel<128>",
+                         "bytes_per_launch": d_bytes},
+        },
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "kernel_sources": kernel_sources_digest()},
+    }
+
+    if not args.no_extra:
+        extra = {}
+        del q, k, v, o, lse
+        for name in ("llama2_7b_prefill_noncausal", "long_prefill_32k"):
+            cfg, (eq, ek, ev_, eo, el) = prefill_setup(name)
+            avg, med, mn = time_kernel(
+                lambda: mi.attn_fwd_prefill(eq, ek, ev_, eo, el, cfg.causal, cfg.scale, stream),
+                max(3, args.steps // 4) if name == "long_prefill_32k" else args.steps,
+                args.warmup)
+            tf = ai.prefill_flops(cfg) / (avg * 1e-6) / 1e12
+            extra[name] = {"us": round(avg, 2), "us_min": round(mn, 2), "TFLOP/s": round(tf, 2),
+                           "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+            del eq, ek, ev_, eo, el
+            torch.cuda.empty_cache()
+        del dq, dkc, dvc, table, seq, do, dlse, ws
+        torch.cuda.empty_cache()
+        cfg, clens, cmax, (cq, ckc, cvc, ctab, cseq, co, cl) = decode_setup("gqa_decode_contig")
+        cws = mi.decode_workspace(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cmax, 0)
+        avg, med, mn = time_kernel(
+            lambda: mi.attn_fwd_decode(cq, ckc, cvc, None, cseq, co, cl, cmax, cfg.scale, 0, cws,
+                                       stream=stream), args.steps, args.warmup)
+        gbs = ai.decode_bytes(cfg, clens) / (avg * 1e-6) / 1e9
+        extra["gqa_decode_contig"] = {"us": round(avg, 2), "us_min": round(mn, 2),
+                                      "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        out["other_workloads"] = extra
+
+    if not args.no_cpu:
+        cb = cpu_baseline(args.cpu_seconds)
+        cb["cpu_model"] = cpu_model()
+        out["cpu_baseline"] = cb
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,131 @@
+/*
+ * miattn — fused exact attention forward for AMD Instinct MI355X (gfx950, CDNA4).
+ *
+ * Computes O = softmax(scale * Q K^T [+ causal mask]) V without ever writing the
+ * N x N score matrix to memory: key/value tiles are streamed through on-chip memory
+ * and the softmax is accumulated online (running row max m, running sum l, rescaled
+ * partial output).
+ *
+ * Sources for what is computed:
+ *  - the definition softmax(Q K^T / sqrt(d_k)) V: page "FlashAttention 완전 정리"
+ *    (cell-devlog), section "Attention이 뭔가" (what attention is);
+ *  - tiling with the score matrix kept on chip, and the online softmax that makes the
+ *    blockwise result exact: same page, section "FlashAttention의 핵심 아이디어 —
+ *    Tiling" (core idea: tiling); m, f, l definitions: page "Flash Attention: GPU
+ *    메모리_IO를 최적화하는 어텐션 메커니즘 완전 가이드" (holysheep), section
+ *    "수학적 원리: Online Softmax 알고리즘";
+ *  - separate prefill and decode kernels, decode as a single query against a growing
+ *    KV cache, and paged KV caches: page "메모리 장벽을 넘어: LLM 연산자 가속 라이브러리
+ *    심층 분석" (tiptinker), section "2. FlashInfer";
+ *  - the call shape (q, k, v, softmax_scale, causal) and the caller-side checks (device
+ *    tensors, bf16, contiguous memory): same page, section "최적화된 어텐션 순전파
+ *    (Forward Pass)".
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE memory owned by the caller.  The library never
+ *    allocates, frees or synchronises; every call is asynchronous on `stream`
+ *    (0 = the null stream) and its outputs are valid once the stream reaches it.
+ *  - Tensors are dense, contiguous, row-major, in the layouts stated per argument; no
+ *    strides are taken.  bf16 tensors are passed as `const void*` (16-bit patterns).
+ *    Outputs must not alias inputs.
+ *  - Every call returns an attn_status_t.  Arguments are validated before any HIP call;
+ *    a failed validation launches nothing.  Nothing throws across this interface.
+ *  - Grouped-query attention: query head h reads KV head h / (Hq / Hkv).
+ *  - Causal masking is aligned bottom-right: key j is visible to query i iff
+ *    j <= i + (Nk - Nq).  Causal with Nq > Nk is rejected.
+ *  - LSE is the natural-log log-sum-exp of the scaled visible scores of a row,
+ *    m + ln(l), in fp32.
+ *  - Supported head dimensions: d in {64, 128}.  Inputs must be finite.
+ */
+#ifndef MIATTN_H
+#define MIATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, non-finite scale */
+  ATTN_ERR_UNSUPPORTED = 2,      /* d not in {64,128}, page_size != 16, too large a grid */
+  ATTN_ERR_WORKSPACE = 3,        /* decode workspace missing or too small */
+  ATTN_ERR_HIP = 4               /* the HIP runtime reported a launch error */
+} attn_status_t;
+
+/*
+ * Prefill: many queries per sequence.
+ *
+ *   q    [B, Hq,  Nq, d] bf16, 16-byte aligned
+ *   k, v [B, Hkv, Nk, d] bf16, 16-byte aligned
+ *   o    [B, Hq,  Nq, d] bf16 (written), 16-byte aligned
+ *   lse  [B, Hq,  Nq]    fp32 (written) or NULL to skip it, 4-byte aligned
+ *   causal != 0 applies the bottom-right causal mask.
+ *   scale multiplies Q K^T before the softmax (usually 1/sqrt(d)); any finite value.
+ *
+ * Errors: INVALID_ARGUMENT for a null q/k/v/o, misalignment, any size < 1,
+ * Hq % Hkv != 0, causal with Nq > Nk, non-finite scale; UNSUPPORTED for d not in
+ * {64,128} or a grid beyond 2^31-1 workgroups; HIP if the launch fails.
+ */
+int attn_fwd_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                     hipStream_t stream);
+
+/*
+ * Decode: one query per sequence against the sequence's KV cache, split along the
+ * KV length into chunks whose partial results are merged by log-sum-exp.
+ *
+ *   q        [B, Hq, d] bf16
+ *   o        [B, Hq, d] bf16 (written)
+ *   lse      [B, Hq] fp32 (written) or NULL
+ *   seqlens  [B] int32, DEVICE memory, each in [0, max_seqlen] (not read on the host);
+ *            seqlens[b] == 0 gives o = 0 and lse = -inf for that sequence.
+ *   Contiguous cache (block_table == NULL):
+ *     kcache, vcache [B, Hkv, max_seqlen, d] bf16; token t of sequence b is row t.
+ *     page_size, max_blocks_per_seq and num_pages are ignored.
+ *   Paged cache (block_table != NULL):
+ *     kcache, vcache [num_pages, Hkv, page_size, d] bf16 with page_size == 16;
+ *     block_table [B, max_blocks_per_seq] int32, DEVICE memory; token t of sequence b
+ *     is slot t % page_size of page block_table[b, t / page_size].  Entries for
+ *     tokens < seqlens[b] must lie in [0, num_pages); other entries are never read.
+ *     Needs max_blocks_per_seq >= ceil(max_seqlen / page_size).
+ *   Cache rows at or past seqlens[b] are never read (they may hold anything).
+ *   num_splits: number of KV chunks per sequence; 0 picks one automatically.  The
+ *     count actually used is attn_decode_num_splits(...) of the same arguments.
+ *   workspace: device scratch of at least attn_decode_workspace_bytes(...) bytes,
+ *     16-byte aligned; may be NULL when that size is 0.  Its contents on entry do
+ *     not matter; calls that share one workspace must be ordered on one stream.
+ *
+ * Errors: INVALID_ARGUMENT for a null required pointer, misalignment, any size < 1,
+ * Hq % Hkv != 0, max_blocks_per_seq too small, num_splits < 0, non-finite scale;
+ * UNSUPPORTED for d not in {64,128} or page_size != 16; WORKSPACE when the workspace
+ * is missing or too small; HIP if a launch fails.
+ */
+int attn_fwd_decode(const void* q, const void* kcache, const void* vcache,
+                    const int32_t* block_table, const int32_t* seqlens, void* o, float* lse,
+                    int B, int Hq, int Hkv, int d, int max_seqlen, int page_size,
+                    int max_blocks_per_seq, int num_pages, float scale, int num_splits,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Number of KV chunks attn_fwd_decode uses for these arguments (num_splits 0 = auto).
+ * Returns 0 for invalid arguments.  Pure host arithmetic; no HIP call. */
+int attn_decode_num_splits(int B, int Hq, int Hkv, int d, int max_seqlen, int num_splits);
+
+/* Workspace bytes attn_fwd_decode needs for these arguments: fp32 partial outputs and
+ * log-sum-exps, B*Hq*splits*(d+1)*4 rounded up to 256, or 0 when one chunk suffices.
+ * Returns 0 for invalid arguments.  Pure host arithmetic; no HIP call. */
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seqlen,
+                                   int num_splits);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIATTN_H */

@@ -1,0 +1,215 @@
+"""Python binding of libmiattn (fused exact attention forward for MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels of
+libmiattn.so.  PyTorch supplies device memory and the current stream.  There is no
+fallback: if the library is not built, importing the entry points raises.
+
+Entry points (same names and argument order as include/miattn.h):
+    attn_fwd_prefill(q, k, v, o, lse, causal, scale, stream=None)
+    attn_fwd_decode(q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen, scale,
+                    num_splits=0, workspace=None, page_size=16, num_pages=None, stream=None)
+    attn_decode_workspace_bytes(B, Hq, Hkv, d, max_seqlen, num_splits)
+    attn_decode_num_splits(B, Hq, Hkv, d, max_seqlen, num_splits)
+    attn_status_string(status)
+Conveniences that allocate the outputs with torch and call the above:
+    prefill(q, k, v, causal=True, scale=None) -> (o, lse)
+    decode(q, kcache, vcache, seqlens, max_seqlen, block_table=None, scale=None,
+           num_splits=0) -> (o, lse)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libmiattn.so")
+
+ATTN_OK = 0
+_lib = None
+
+
+class AttnError(RuntimeError):
+    """A libmiattn call returned a non-zero status."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {attn_status_string(status)} (status {status})")
+
+
+def load_library():
+    """Load libmiattn.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -c "
+                           "'import __graft_entry__ as g; g.build()'` from the repository root")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_fwd_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+                                     vp]
+    lib.attn_fwd_prefill.restype = i32
+    lib.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                    i32, f32, i32, vp, ctypes.c_size_t, vp]
+    lib.attn_fwd_decode.restype = i32
+    lib.attn_decode_workspace_bytes.argtypes = [i32] * 6
+    lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_decode_num_splits.argtypes = [i32] * 6
+    lib.attn_decode_num_splits.restype = i32
+    lib.attn_status_string.argtypes = [i32]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def attn_status_string(status: int) -> str:
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return ctypes.c_void_p(handle)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+
+
+def _check(t, name, dtype, ndim, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# -------------------------------------------------------------------------------- prefill
+def attn_fwd_prefill(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
+    """q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d], o [B,Hq,Nq,d] bf16; lse [B,Hq,Nq] fp32 or None."""
+    lib = load_library()
+    _check(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    _check(k, "k", torch.bfloat16, 4, dev)
+    _check(v, "v", torch.bfloat16, 4, dev)
+    _check(o, "o", torch.bfloat16, 4, dev)
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if Bk != B or dk != d or tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q, k, v, o")
+    if lse is not None:
+        _check(lse, "lse", torch.float32, 3, dev)
+        if tuple(lse.shape) != (B, Hq, Nq):
+            raise ValueError("lse must be [B, Hq, Nq]")
+    st = lib.attn_fwd_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk,
+                              d, 1 if causal else 0, float(scale), _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_prefill")
+
+
+def prefill(q, k, v, causal: bool = True, scale: float | None = None):
+    """Allocate O and LSE and run attn_fwd_prefill.  scale None means 1/sqrt(d)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    attn_fwd_prefill(q, k, v, o, lse, causal, scale)
+    return o, lse
+
+
+# -------------------------------------------------------------------------------- decode
+def attn_decode_workspace_bytes(B, Hq, Hkv, d, max_seqlen, num_splits=0) -> int:
+    return int(load_library().attn_decode_workspace_bytes(B, Hq, Hkv, d, max_seqlen, num_splits))
+
+
+def attn_decode_num_splits(B, Hq, Hkv, d, max_seqlen, num_splits=0) -> int:
+    return int(load_library().attn_decode_num_splits(B, Hq, Hkv, d, max_seqlen, num_splits))
+
+
+def attn_fwd_decode(q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen: int,
+                    scale: float, num_splits: int = 0, workspace=None, page_size: int = 16,
+                    num_pages: int | None = None, stream=None) -> None:
+    """q/o [B,Hq,d] bf16; lse [B,Hq] fp32 or None; seqlens int32 [B] (device).
+    block_table None: caches [B,Hkv,max_seqlen,d]; else caches [num_pages,Hkv,16,d] and
+    block_table int32 [B, max_blocks]."""
+    lib = load_library()
+    _check(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _check(kcache, "kcache", torch.bfloat16, 4, dev)
+    _check(vcache, "vcache", torch.bfloat16, 4, dev)
+    _check(o, "o", torch.bfloat16, 3, dev)
+    _check(seqlens, "seqlens", torch.int32, 1, dev)
+    B, Hq, d = q.shape
+    if tuple(vcache.shape) != tuple(kcache.shape) or tuple(o.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q/o or kcache/vcache")
+    if seqlens.shape[0] != B:
+        raise ValueError("seqlens must be [B]")
+    Hkv = kcache.shape[1]
+    if kcache.shape[3] != d:
+        raise ValueError("cache head dimension differs from q")
+    max_blocks = 0
+    if block_table is None:
+        if kcache.shape[0] != B or kcache.shape[2] != max_seqlen:
+            raise ValueError("contiguous caches must be [B, Hkv, max_seqlen, d]")
+        num_pages = 0
+    else:
+        _check(block_table, "block_table", torch.int32, 2, dev)
+        if block_table.shape[0] != B:
+            raise ValueError("block_table must be [B, max_blocks]")
+        max_blocks = block_table.shape[1]
+        if kcache.shape[2] != page_size:
+            raise ValueError("paged caches must be [num_pages, Hkv, page_size, d]")
+        if num_pages is None:
+            num_pages = kcache.shape[0]
+    if lse is not None:
+        _check(lse, "lse", torch.float32, 2, dev)
+        if tuple(lse.shape) != (B, Hq):
+            raise ValueError("lse must be [B, Hq]")
+    ws_bytes = 0
+    if workspace is not None:
+        if workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on q's device")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.attn_fwd_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(block_table),
+                             _ptr(seqlens), _ptr(o), _ptr(lse), B, Hq, Hkv, d, int(max_seqlen),
+                             int(page_size), int(max_blocks), int(num_pages), float(scale),
+                             int(num_splits), _ptr(workspace), ws_bytes, _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_decode")
+
+
+def decode_workspace(B, Hq, Hkv, d, max_seqlen, num_splits=0, device="cuda"):
+    """A workspace tensor of the size attn_fwd_decode needs (None when it needs none)."""
+    n = attn_decode_workspace_bytes(B, Hq, Hkv, d, max_seqlen, num_splits)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def decode(q, kcache, vcache, seqlens, max_seqlen: int, block_table=None,
+           scale: float | None = None, num_splits: int = 0, workspace=None):
+    """Allocate O, LSE (and the workspace when not given) and run attn_fwd_decode."""
+    B, Hq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, kcache.shape[1], d, max_seqlen, num_splits, q.device)
+    attn_fwd_decode(q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen, scale,
+                    num_splits, workspace)
+    return o, lse
+
+
+__all__ = ["attn_fwd_prefill", "attn_fwd_decode", "attn_decode_workspace_bytes",
+           "attn_decode_num_splits", "attn_status_string", "prefill", "decode",
+           "decode_workspace", "load_library", "AttnError", "LIB_PATH"]

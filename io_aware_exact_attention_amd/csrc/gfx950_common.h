@@ -1,0 +1,79 @@
+// gfx950 (CDNA4) device helpers shared by the attention kernels: MFMA wrappers, the
+// transposing LDS read, bf16 packing, workgroup placement across XCDs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace miattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// The running max used for exponentiation is only moved up when a row's true max
+// exceeds it by more than this many powers of two; exp2 arguments therefore stay
+// <= kRescaleLog2 and P <= 2^kRescaleLog2, far from fp32/bf16 overflow.  In exact
+// arithmetic the result does not depend on which reference max is used.
+constexpr float kRescaleLog2 = 8.0f;
+
+// D = A(32x16) * B(16x32) + C, bf16 inputs, fp32 accumulate.
+// Lane l holds A[l%32][8*(l/32) .. +7], B[8*(l/32) .. +7][l%32] and
+// C[8*(r/4) + 4*(l/32) + r%4][l%32] in accumulator r.
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// D = A(16x32) * B(32x16) + C.  Lane l holds A[l%16][8*(l/16) .. +7],
+// B[8*(l/16) .. +7][l%16] and C[4*(l/16) + r][l%16] in accumulator r.
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i
+// supplies the address of 4 consecutive bf16 holding row i/4, columns 4*(i%4)..+3 of a
+// 4x16 block; lane i receives column i of that block (rows 0..3).
+__device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+}
+
+__device__ __forceinline__ bf16x8 concat(bf16x4 lo, bf16x4 hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// acc + lo(x) + hi(x) for a packed bf16 pair x (v_dot2_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float add_bf16x2(uint32_t x, float acc) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), ones, acc, false);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_xor(float x, int m) { return __shfl_xor(x, m, 64); }
+
+// Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).  Give XCD x a
+// contiguous range of logical work ids so that neighbouring ids (same head, adjacent
+// query tiles) share one L2.  Bijective on [0, total).
+__device__ __forceinline__ int xcd_remap(int p, int total) {
+  const int per = total >> 3, rem = total & 7;
+  const int x = p & 7, k = p >> 3;
+  const int base = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+  return base + k;
+}
+
+}  // namespace miattn

@@ -1,0 +1,49 @@
+// Kernel parameter blocks and launchers (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace miattn {
+
+struct PrefillParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int B, Hq, Hkv, Nq, Nk;
+  float c;        // |scale| * log2(e)
+  int negate_q;   // scale < 0: Q's sign is flipped on load (exact) so c >= 0
+  int num_qtiles; // filled by launch_prefill
+  int total_wg;   // filled by launch_prefill
+};
+
+struct DecodeParams {
+  const uint16_t* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  const int32_t* block_table;  // null: contiguous cache
+  const int32_t* seqlens;
+  uint16_t* o;
+  float* lse;
+  float* ws_o;    // [B, Hq, num_splits, d] fp32 partial outputs (num_splits > 1)
+  float* ws_lse;  // [B, Hq, num_splits] fp32 partial log-sum-exps
+  int B, Hq, Hkv, G, ngroups;
+  int max_seqlen;  // row count of the contiguous cache
+  int max_blocks;  // block-table row length (paged)
+  int num_splits, chunk;
+  float c;
+  int negate_q;
+};
+
+// Query heads sharing one KV head that a decode workgroup serves at once.
+constexpr int kDecodeHeadsPerGroup = 16;
+// Keys one decode wave consumes per step; chunks are multiples of it.
+constexpr int kDecodeBlock = 32;
+constexpr int kDecodeWaves = 4;
+
+hipError_t launch_prefill(PrefillParams p, int d, int causal, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t stream);
+
+}  // namespace miattn

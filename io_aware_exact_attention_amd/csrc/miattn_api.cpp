@@ -1,0 +1,170 @@
+// C-ABI entry points of libmiattn: argument validation (before any HIP call), launch
+// planning (kernel instance, grid, decode chunking, workspace layout) and launch on the
+// caller's stream.  The library never allocates, frees or synchronises.
+//
+// The caller-side checks mirror the ones shown before the forward call on the page
+// "메모리 장벽을 넘어: LLM 연산자 가속 라이브러리 심층 분석" (tiptinker), section
+// "최적화된 어텐션 순전파 (Forward Pass)": device tensors, bf16, contiguous memory.  Here
+// they are reported as status codes instead of silent casts and copies.
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/miattn.h"
+#include "launch.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Decode chunking: chunk = ceil(max_seqlen / splits) rounded up to a whole number of
+// 32-key blocks; the split count actually used is ceil(max_seqlen / chunk).
+struct Plan {
+  int splits;
+  int chunk;
+};
+
+constexpr int kAutoTargetWorkgroups = 2048;  // ~8 per compute unit on 256 CUs
+constexpr int kMinChunk = 256;               // keys per chunk in the automatic plan
+constexpr int kMaxSplits = 1024;
+
+bool decode_sizes_ok(int B, int Hq, int Hkv, int d, int max_seqlen) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || max_seqlen < 1) return false;
+  if (Hq % Hkv) return false;
+  (void)d;
+  return true;
+}
+
+Plan plan_decode(int B, int Hq, int Hkv, int max_seqlen, int num_splits) {
+  const int G = Hq / Hkv;
+  const int ngroups = (G + miattn::kDecodeHeadsPerGroup - 1) / miattn::kDecodeHeadsPerGroup;
+  int want = num_splits;
+  if (want <= 0) {
+    const long base = (long)B * Hkv * ngroups;
+    long s = (kAutoTargetWorkgroups + base - 1) / base;
+    const long cap = (max_seqlen + kMinChunk - 1) / kMinChunk;
+    if (s > cap) s = cap;
+    want = (int)(s < 1 ? 1 : s);
+  }
+  if (want > kMaxSplits) want = kMaxSplits;
+  const int blk = miattn::kDecodeBlock;
+  long chunk = ((long)max_seqlen + want - 1) / want;
+  chunk = (chunk + blk - 1) / blk * blk;
+  const int splits = (int)(((long)max_seqlen + chunk - 1) / chunk);
+  return Plan{splits, (int)chunk};
+}
+
+size_t workspace_for(int B, int Hq, int d, const Plan& pl) {
+  if (pl.splits <= 1) return 0;
+  const size_t n = (size_t)B * Hq * pl.splits;
+  const size_t bytes = n * (size_t)d * 4 + n * 4;
+  return (bytes + 255) / 256 * 256;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int attn_fwd_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                     hipStream_t stream) {
+  if (!q || !k || !v || !o) return ATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (lse && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return ATTN_ERR_INVALID_ARGUMENT;
+  if (Hq % Hkv) return ATTN_ERR_INVALID_ARGUMENT;
+  if (causal && Nq > Nk) return ATTN_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  const long qtiles = (Nq + 127) / 128;
+  if (qtiles * (long)Hq * B > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
+  if ((long)B * Hq > 0x7fffffffL || (long)B * Hkv > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
+
+  miattn::PrefillParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk;
+  p.c = std::fabs(scale) * 1.4426950408889634f;
+  p.negate_q = scale < 0.f;
+  (void)hipGetLastError();  // clear a stale error so the check below is ours
+  return miattn::launch_prefill(p, d, causal ? 1 : 0, stream) == hipSuccess ? ATTN_OK
+                                                                             : ATTN_ERR_HIP;
+}
+
+int attn_decode_num_splits(int B, int Hq, int Hkv, int d, int max_seqlen, int num_splits) {
+  if (!decode_sizes_ok(B, Hq, Hkv, d, max_seqlen) || num_splits < 0) return 0;
+  return plan_decode(B, Hq, Hkv, max_seqlen, num_splits).splits;
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seqlen,
+                                   int num_splits) {
+  if (!decode_sizes_ok(B, Hq, Hkv, d, max_seqlen) || num_splits < 0) return 0;
+  return workspace_for(B, Hq, d, plan_decode(B, Hq, Hkv, max_seqlen, num_splits));
+}
+
+int attn_fwd_decode(const void* q, const void* kcache, const void* vcache,
+                    const int32_t* block_table, const int32_t* seqlens, void* o, float* lse,
+                    int B, int Hq, int Hkv, int d, int max_seqlen, int page_size,
+                    int max_blocks_per_seq, int num_pages, float scale, int num_splits,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !kcache || !vcache || !seqlens || !o) return ATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(kcache, 16) || !aligned(vcache, 16) || !aligned(o, 16) ||
+      !aligned(seqlens, 4))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (lse && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (!decode_sizes_ok(B, Hq, Hkv, d, max_seqlen) || d < 1) return ATTN_ERR_INVALID_ARGUMENT;
+  if (num_splits < 0 || !std::isfinite(scale)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (block_table) {
+    if (!aligned(block_table, 4) || num_pages < 1) return ATTN_ERR_INVALID_ARGUMENT;
+    if (page_size != 16) return ATTN_ERR_UNSUPPORTED;
+    if (max_blocks_per_seq < (max_seqlen + page_size - 1) / page_size)
+      return ATTN_ERR_INVALID_ARGUMENT;
+  }
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  const int G = Hq / Hkv;
+  const int ngroups = (G + miattn::kDecodeHeadsPerGroup - 1) / miattn::kDecodeHeadsPerGroup;
+  if (B > 65535 || (long)Hkv * ngroups > 65535) return ATTN_ERR_UNSUPPORTED;
+
+  const Plan pl = plan_decode(B, Hq, Hkv, max_seqlen, num_splits);
+  const size_t need = workspace_for(B, Hq, d, pl);
+  if (need) {
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return ATTN_ERR_WORKSPACE;
+  }
+
+  miattn::DecodeParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.kc = static_cast<const uint16_t*>(kcache);
+  p.vc = static_cast<const uint16_t*>(vcache);
+  p.block_table = block_table;
+  p.seqlens = seqlens;
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.ws_o = need ? static_cast<float*>(workspace) : nullptr;
+  p.ws_lse = need ? p.ws_o + (size_t)B * Hq * pl.splits * d : nullptr;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = G; p.ngroups = ngroups;
+  p.max_seqlen = max_seqlen;
+  p.max_blocks = block_table ? max_blocks_per_seq : 0;
+  p.num_splits = pl.splits;
+  p.chunk = pl.chunk;
+  p.c = std::fabs(scale) * 1.4426950408889634f;
+  p.negate_q = scale < 0.f;
+  (void)hipGetLastError();
+  return miattn::launch_decode(p, d, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // extern "C"

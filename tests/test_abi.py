@@ -1,0 +1,118 @@
+"""The C-ABI library: it loads, exports what include/miattn.h declares, and its host-side
+validation and planning behave as documented (CPU only; no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import io_aware_exact_attention_amd as mi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "miattn.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, 1, 2, 3, 4
+P = ctypes.c_void_p(4096)        # a non-null, 16-byte aligned dummy pointer (never dereferenced)
+MIS = ctypes.c_void_p(4096 + 2)  # misaligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mi.LIB_PATH):
+        pytest.fail("libmiattn.so is not built; run __graft_entry__.build() first")
+    return mi.load_library()
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(["attn_fwd_prefill", "attn_fwd_decode",
+                                           "attn_decode_workspace_bytes",
+                                           "attn_decode_num_splits", "attn_status_string"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert mi.attn_status_string(OK) == "ok"
+    for s in (INVALID, UNSUPPORTED, WORKSPACE, HIPERR):
+        assert mi.attn_status_string(s) not in ("ok", "unknown status")
+    assert mi.attn_status_string(99) == "unknown status"
+
+
+def prefill(lib, q=P, k=P, v=P, o=P, lse=None, B=1, Hq=2, Hkv=1, Nq=4, Nk=4, d=64, causal=1,
+            scale=0.125):
+    return lib.attn_fwd_prefill(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal,
+                                ctypes.c_float(scale), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID),
+    (dict(o=None), INVALID), (dict(q=MIS), INVALID), (dict(o=MIS), INVALID),
+    (dict(lse=ctypes.c_void_p(4098)), INVALID),
+    (dict(B=0), INVALID), (dict(Hq=0), INVALID), (dict(Hkv=0), INVALID), (dict(Nq=0), INVALID),
+    (dict(Nk=0), INVALID), (dict(Hq=3, Hkv=2), INVALID), (dict(Nq=5, Nk=4, causal=1), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(d=32), UNSUPPORTED), (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
+    (dict(B=65536, Hq=65536, Hkv=1, Nq=128, Nk=128), UNSUPPORTED),
+])
+def test_prefill_validation(lib, kw, status):
+    assert prefill(lib, **kw) == status
+
+
+def decode(lib, q=P, kc=P, vc=P, table=None, seqlens=P, o=P, lse=None, B=2, Hq=8, Hkv=2, d=128,
+           max_seqlen=100, page_size=16, max_blocks=7, num_pages=10, scale=0.1, splits=1,
+           ws=None, ws_bytes=0):
+    return lib.attn_fwd_decode(q, kc, vc, table, seqlens, o, lse, B, Hq, Hkv, d, max_seqlen,
+                               page_size, max_blocks, num_pages, ctypes.c_float(scale), splits,
+                               ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(kc=None), INVALID), (dict(vc=None), INVALID),
+    (dict(seqlens=None), INVALID), (dict(o=None), INVALID), (dict(kc=MIS), INVALID),
+    (dict(seqlens=ctypes.c_void_p(4098)), INVALID), (dict(B=0), INVALID),
+    (dict(Hq=6, Hkv=4), INVALID), (dict(max_seqlen=0), INVALID), (dict(splits=-1), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(d=80), UNSUPPORTED),
+    (dict(table=P, page_size=32), UNSUPPORTED), (dict(table=P, max_blocks=6), INVALID),
+    (dict(table=P, num_pages=0), INVALID), (dict(B=70000), UNSUPPORTED),
+    # more than one chunk needs a workspace of the advertised size
+    (dict(max_seqlen=4096, splits=4), WORKSPACE),
+    (dict(max_seqlen=4096, splits=4, ws=P, ws_bytes=100), WORKSPACE),
+])
+def test_decode_validation(lib, kw, status):
+    assert decode(lib, **kw) == status
+
+
+def test_decode_split_plan(lib):
+    # explicit split counts: chunk = ceil(L / s) rounded up to 32 keys
+    assert mi.attn_decode_num_splits(2, 8, 2, 128, 4096, 4) == 4
+    assert mi.attn_decode_num_splits(2, 8, 2, 128, 100, 4) == 4      # chunk 32 -> 4 chunks
+    assert mi.attn_decode_num_splits(2, 8, 2, 128, 100, 50) == 4     # never more than needed
+    assert mi.attn_decode_num_splits(2, 8, 2, 128, 1, 0) == 1
+    # automatic plan fills the machine but keeps >= 256 keys per chunk
+    s = mi.attn_decode_num_splits(64, 32, 8, 128, 8192, 0)
+    assert 1 <= s <= 32
+    assert mi.attn_decode_num_splits(1, 1, 1, 128, 1000, 0) == 4
+    assert mi.attn_decode_num_splits(0, 8, 2, 128, 100, 0) == 0      # invalid -> 0
+
+
+def test_decode_workspace_arithmetic(lib):
+    assert mi.attn_decode_workspace_bytes(2, 8, 2, 128, 100, 1) == 0
+    n = 2 * 8 * 4
+    want = (n * 128 * 4 + n * 4 + 255) // 256 * 256
+    assert mi.attn_decode_workspace_bytes(2, 8, 2, 128, 4096, 4) == want
+    assert mi.attn_decode_workspace_bytes(2, 8, 3, 128, 4096, 4) == 0  # invalid heads
+
+
+def test_binding_rejects_host_tensors(lib):
+    import torch
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mi.attn_fwd_prefill(x, x, x, x, None, True, 0.125)

@@ -1,0 +1,324 @@
+"""GPU parity: libmiattn (through the C-ABI binding) against the fp64 CPU oracle.
+
+Bar, for bf16 inputs with fp32 accumulation, O compared after upcasting the GPU's bf16
+output: max abs error <= 2e-2, mean abs error <= 2e-3, LSE max abs error <= 1e-3.
+Small shapes are compared element by element over the whole output; the full-size
+workloads are compared on sampled heads and rows the oracle computes one by one.
+Set MIATTN_PARITY_LOG=<path> to append every case's errors as JSON lines.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs as ai
+import io_aware_exact_attention_amd as mi
+from oracle import attention_decode, attention_prefill, attention_rows
+
+pytestmark = pytest.mark.gpu
+
+TOL_MAX, TOL_MEAN, TOL_LSE = 2e-2, 2e-3, 1e-3
+
+
+def dev(bits, dtype=torch.bfloat16):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    return t.cuda()
+
+
+def f64(bits):
+    return ai.bf16_bits_to_f64(bits)
+
+
+def log_case(label, **kv):
+    path = os.environ.get("MIATTN_PARITY_LOG")
+    print(label, kv, flush=True)
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"case": label, **kv}) + "\n")
+
+
+def check(label, o_gpu, lse_gpu, o_ref, lse_ref):
+    o = o_gpu.float().cpu().numpy().astype(np.float64)
+    l = lse_gpu.float().cpu().numpy().astype(np.float64)
+    assert o.shape == o_ref.shape and l.shape == lse_ref.shape
+    err = np.abs(o - o_ref)
+    fin = np.isfinite(lse_ref)
+    assert (np.isfinite(l) == fin).all(), f"{label}: LSE finiteness differs"
+    assert (l[~fin] == lse_ref[~fin]).all()
+    lerr = float(np.abs(l[fin] - lse_ref[fin]).max()) if fin.any() else 0.0
+    log_case(label, max_abs=float(err.max()), mean_abs=float(err.mean()), lse_max_abs=lerr)
+    assert np.isfinite(o).all(), f"{label}: non-finite output"
+    assert err.max() <= TOL_MAX, f"{label}: max abs {err.max():.3e}"
+    assert err.mean() <= TOL_MEAN, f"{label}: mean abs {err.mean():.3e}"
+    assert lerr <= TOL_LSE, f"{label}: lse max abs {lerr:.3e}"
+
+
+def run_prefill(q, k, v, causal, scale):
+    o, lse = mi.prefill(dev(q).reshape(q.shape), dev(k).reshape(k.shape),
+                        dev(v).reshape(v.shape), causal, scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# ------------------------------------------------------------------ prefill, whole outputs
+def test_prefill_tiny_config():
+    cfg = ai.CONFIGS["tiny_prefill"]
+    q, k, v = ai.prefill_inputs(cfg)
+    o, lse = run_prefill(q, k, v, cfg.causal, cfg.scale)
+    ro, rl = attention_prefill(f64(q), f64(k), f64(v), cfg.scale, cfg.causal)
+    check("tiny_prefill", o, lse, ro, rl)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("N", [1, 17, 63, 65, 127, 129, 1000])
+def test_prefill_ragged_lengths(N, causal, d):
+    q, k, v = ai.custom_prefill(seed=1000 + N, B=1, Hq=2, Hkv=2, Nq=N, Nk=N, d=d)
+    scale = 1 / math.sqrt(d)
+    o, lse = run_prefill(q, k, v, causal, scale)
+    ro, rl = attention_prefill(f64(q), f64(k), f64(v), scale, causal)
+    check(f"prefill N={N} causal={causal} d={d}", o, lse, ro, rl)
+
+
+@pytest.mark.parametrize("Nq,Nk", [(1, 300), (77, 300), (128, 1000), (200, 201), (5, 64)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_fewer_queries_than_keys(Nq, Nk, causal):
+    q, k, v = ai.custom_prefill(seed=2000 + Nq, B=1, Hq=2, Hkv=1, Nq=Nq, Nk=Nk, d=128)
+    o, lse = run_prefill(q, k, v, causal, 0.09)
+    ro, rl = attention_prefill(f64(q), f64(k), f64(v), 0.09, causal)
+    check(f"prefill Nq={Nq} Nk={Nk} causal={causal}", o, lse, ro, rl)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 1), (8, 2), (8, 8), (6, 3)])
+def test_prefill_gqa_and_batch(Hq, Hkv):
+    q, k, v = ai.custom_prefill(seed=3000 + Hq * 10 + Hkv, B=3, Hq=Hq, Hkv=Hkv, Nq=150, Nk=150,
+                                d=64)
+    o, lse = run_prefill(q, k, v, True, 0.125)
+    ro, rl = attention_prefill(f64(q), f64(k), f64(v), 0.125, True)
+    check(f"prefill GQA Hq={Hq} Hkv={Hkv} B=3", o, lse, ro, rl)
+    # GQA equals repeated-head MHA bit for bit (same arithmetic per head)
+    G = Hq // Hkv
+    o2, lse2 = run_prefill(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), True, 0.125)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, 0.6])
+def test_prefill_scale_values(scale):
+    q, k, v = ai.custom_prefill(seed=4000, B=1, Hq=2, Hkv=2, Nq=190, Nk=190, d=64)
+    o, lse = run_prefill(q, k, v, True, scale)
+    ro, rl = attention_prefill(f64(q), f64(k), f64(v), float(np.float32(scale)), True)
+    check(f"prefill scale={scale}", o, lse, ro, rl)
+
+
+def test_prefill_worked_example_and_first_row():
+    # q = e0, keys (0, e0), values (1, 5), scale ln 3: weights (1/4, 3/4), O = 4, LSE = ln 4
+    d = 64
+    q = np.zeros((1, 1, 2, d), np.float32)
+    q[0, 0, :, 0] = 1.0
+    k = np.zeros((1, 1, 2, d), np.float32)
+    k[0, 0, 1, 0] = 1.0
+    v = np.stack([np.ones(d), 5 * np.ones(d)]).astype(np.float32)[None, None]
+    qb, kb, vb = ai.to_bf16_bits(q), ai.to_bf16_bits(k), ai.to_bf16_bits(v)
+    o, lse = run_prefill(qb, kb, vb, True, float(np.float32(math.log(3.0))))
+    out = o.float().cpu().numpy()[0, 0]
+    # causal row 0 sees only key 0: exactly V[0]
+    assert (out[0] == 1.0).all()
+    assert np.abs(out[1] - 4.0).max() <= TOL_MAX
+    assert abs(float(lse[0, 0, 1]) - math.log(4.0)) <= TOL_LSE
+    assert abs(float(lse[0, 0, 0]) - 0.0) <= 1e-6
+
+
+def test_prefill_causal_first_row_is_exact_and_runs_are_deterministic():
+    q, k, v = ai.custom_prefill(seed=5000, B=2, Hq=4, Hkv=4, Nq=300, Nk=300, d=128)
+    o1, l1 = run_prefill(q, k, v, True, 0.088)
+    o2, l2 = run_prefill(q, k, v, True, 0.088)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    vv = dev(v).reshape(v.shape)
+    assert torch.equal(o1[:, :, 0], vv[:, :, 0])
+
+
+def test_prefill_constant_values():
+    q, k, _ = ai.custom_prefill(seed=5100, B=1, Hq=2, Hkv=2, Nq=260, Nk=260, d=64)
+    vrow = ai.to_bf16_bits(np.random.default_rng(1).standard_normal(64).astype(np.float32))
+    v = np.broadcast_to(vrow, (1, 2, 260, 64)).copy()
+    o, _ = run_prefill(q, k, v, True, 0.125)
+    ref = np.broadcast_to(f64(vrow), (1, 2, 260, 64))
+    assert np.abs(o.float().cpu().numpy() - ref).max() <= 1e-2
+
+
+# ------------------------------------------------------------------ prefill, full sizes
+def sampled_prefill_check(cfg, o, lse, q, k, v, heads_full, rows_per_head, seed):
+    """Compare whole heads in heads_full, and rows_per_head sampled rows of every head
+    (always including the first and last row)."""
+    rng = np.random.default_rng(seed)
+    go = o.float().cpu().numpy()
+    gl = lse.cpu().numpy()
+    errs, lerrs = [], []
+    for b in range(cfg.B):
+        for h in range(cfg.Hq):
+            if (b, h) in heads_full:
+                rows = np.arange(cfg.Nq)
+            else:
+                rows = np.unique(np.concatenate([[0, cfg.Nq - 1],
+                                                 rng.integers(0, cfg.Nq, rows_per_head)]))
+            kvh = h // (cfg.Hq // cfg.Hkv)
+            K, V = f64(k[b, kvh]), f64(v[b, kvh])
+            for i0 in range(0, len(rows), 1024):
+                r = rows[i0:i0 + 1024]
+                ro, rl = attention_rows(f64(q[b, h, r]), K, V, cfg.scale, cfg.causal, r, cfg.Nq)
+                errs.append(np.abs(go[b, h, r] - ro).ravel())
+                lerrs.append(np.abs(gl[b, h, r] - rl).ravel())
+    err = np.concatenate(errs)
+    lerr = np.concatenate(lerrs)
+    log_case(cfg.name + " (sampled)", max_abs=float(err.max()), mean_abs=float(err.mean()),
+             lse_max_abs=float(lerr.max()), n=int(err.size))
+    assert np.isfinite(go).all()
+    assert err.max() <= TOL_MAX and err.mean() <= TOL_MEAN and lerr.max() <= TOL_LSE
+
+
+@pytest.mark.parametrize("name", ["llama2_7b_prefill", "llama2_7b_prefill_noncausal"])
+def test_prefill_llama2_shape(name):
+    cfg = ai.CONFIGS[name]
+    q, k, v = ai.prefill_inputs(cfg)
+    o, lse = run_prefill(q, k, v, cfg.causal, cfg.scale)
+    sampled_prefill_check(cfg, o, lse, q, k, v, heads_full={(0, 0), (3, 31), (1, 17)},
+                          rows_per_head=16, seed=7)
+
+
+def test_prefill_long_context_32k():
+    cfg = ai.CONFIGS["long_prefill_32k"]
+    q, k, v = ai.prefill_inputs(cfg)
+    o, lse = run_prefill(q, k, v, cfg.causal, cfg.scale)
+    del q
+    qh = {h: ai.prefill_head(cfg, ai.T_Q, 0, h) for h in range(cfg.Hq)}
+    rng = np.random.default_rng(8)
+    go = o.float().cpu().numpy()
+    gl = lse.cpu().numpy()
+    errs, lerrs = [], []
+    for h in range(cfg.Hq):
+        n = 96 if h in (0, 31) else 6
+        rows = np.unique(np.concatenate([[0, 1, cfg.Nq - 2, cfg.Nq - 1],
+                                         rng.integers(0, cfg.Nq, n)]))
+        ro, rl = attention_rows(f64(qh[h][rows]), f64(k[0, h]), f64(v[0, h]), cfg.scale, True,
+                                rows, cfg.Nq)
+        errs.append(np.abs(go[0, h, rows] - ro).ravel())
+        lerrs.append(np.abs(gl[0, h, rows] - rl).ravel())
+    err, lerr = np.concatenate(errs), np.concatenate(lerrs)
+    log_case("long_prefill_32k (sampled)", max_abs=float(err.max()), mean_abs=float(err.mean()),
+             lse_max_abs=float(lerr.max()), n=int(err.size))
+    assert np.isfinite(go).all()
+    assert err.max() <= TOL_MAX and err.mean() <= TOL_MEAN and lerr.max() <= TOL_LSE
+
+
+# ------------------------------------------------------------------ decode
+def make_decode(B, Hq, Hkv, d, lens, seed, paged, extra_pages=3):
+    cfg = ai.DecodeCfg("case", B=B, Hq=Hq, Hkv=Hkv, d=d, seed=seed, paged=paged)
+    lens = np.asarray(lens, np.int32)
+    q = ai.decode_q(cfg)
+    maxlen = max(int(lens.max()), 1)
+    if paged:
+        lay = ai.paged_layout(lens, 16, seed, extra_pages=extra_pages)
+        kc = ai.build_paged_cache(cfg, ai.T_K, lens, lay)
+        vc = ai.build_paged_cache(cfg, ai.T_V, lens, lay)
+        table = lay.block_table
+    else:
+        kc = ai.build_contig_cache(cfg, ai.T_K, lens, maxlen)
+        vc = ai.build_contig_cache(cfg, ai.T_V, lens, maxlen)
+        table = None
+    return cfg, q, kc, vc, lens, table, maxlen
+
+
+def run_decode(q, kc, vc, lens, table, maxlen, scale, num_splits=0):
+    o, lse = mi.decode(dev(q).reshape(q.shape), dev(kc).reshape(kc.shape),
+                       dev(vc).reshape(vc.shape), torch.from_numpy(lens).cuda(), maxlen,
+                       block_table=None if table is None else torch.from_numpy(table).cuda(),
+                       scale=scale, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def decode_ref(q, kc, vc, lens, table, scale):
+    return attention_decode(f64(q), f64(kc), f64(vc), lens, scale, table, 16)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("splits", [1, 0, 3])
+def test_decode_edge_lengths(paged, d, splits):
+    lens = [0, 1, 15, 16, 17, 31, 33, 1000]
+    cfg, q, kc, vc, lens, table, maxlen = make_decode(8, 8, 2, d, lens, 600 + d, paged)
+    o, lse = run_decode(q, kc, vc, lens, table, maxlen, cfg.scale, splits)
+    ro, rl = decode_ref(q, kc, vc, lens, table, cfg.scale)
+    check(f"decode edge paged={paged} d={d} splits={splits}", o, lse, ro, rl)
+    assert (o[0] == 0).all() and torch.isinf(lse[0]).all()
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (32, 1), (10, 2), (64, 2)])
+def test_decode_group_sizes(Hq, Hkv):
+    lens = [300, 77, 1]
+    cfg, q, kc, vc, lens, table, maxlen = make_decode(3, Hq, Hkv, 128, lens, 700 + Hq, True)
+    o, lse = run_decode(q, kc, vc, lens, table, maxlen, cfg.scale, 2)
+    ro, rl = decode_ref(q, kc, vc, lens, table, cfg.scale)
+    check(f"decode Hq={Hq} Hkv={Hkv}", o, lse, ro, rl)
+
+
+def test_decode_paged_equals_contiguous_and_split_invariance():
+    lens = [5000, 2048, 333, 4097]
+    cfgc, q, kc, vc, lens_, _, maxlen = make_decode(4, 16, 4, 128, lens, 800, False)
+    cfgp, q2, kp, vp, _, table, _ = make_decode(4, 16, 4, 128, lens, 800, True)
+    assert (q == q2).all()
+    ref = decode_ref(q, kc, vc, lens_, None, cfgc.scale)
+    outs = {}
+    for s in (1, 0, 5, 40):
+        oc, lc = run_decode(q, kc, vc, lens_, None, maxlen, cfgc.scale, s)
+        op, lp = run_decode(q, kp, vp, lens_, table, maxlen, cfgc.scale, s)
+        assert torch.equal(oc, op) and torch.equal(lc, lp), f"paged != contiguous at splits={s}"
+        check(f"decode splits={s}", oc, lc, *ref)
+        outs[s] = oc.float()
+    for s in (0, 5, 40):
+        assert (outs[s] - outs[1]).abs().max().item() <= 2e-2
+
+
+def test_decode_is_last_row_of_causal_prefill():
+    n, H, d = 777, 4, 128
+    q, k, v = ai.custom_prefill(seed=900, B=1, Hq=H, Hkv=H, Nq=n, Nk=n, d=d)
+    op, lp = run_prefill(q, k, v, True, 0.088)
+    qd = q[:, :, -1]
+    od, ld = run_decode(qd, k, v, np.array([n], np.int32), None, n, 0.088, 3)
+    assert (od.float() - op[:, :, -1].float()).abs().max().item() <= 2e-2
+    assert (ld - lp[:, :, -1]).abs().max().item() <= 1e-3
+
+
+@pytest.fixture(scope="module")
+def cfg4_inputs():
+    cfg = ai.CONFIGS["gqa_decode_contig"]
+    lens = ai.decode_lengths(cfg)
+    q = ai.decode_q(cfg)
+    kc = ai.build_contig_cache(cfg, ai.T_K, lens, cfg.fixed_len)
+    vc = ai.build_contig_cache(cfg, ai.T_V, lens, cfg.fixed_len)
+    return cfg, q, kc, vc, lens
+
+
+def test_decode_gqa_contiguous_config(cfg4_inputs):
+    cfg, q, kc, vc, lens = cfg4_inputs
+    o, lse = run_decode(q, kc, vc, lens, None, cfg.fixed_len, cfg.scale)
+    o2, lse2 = run_decode(q, kc, vc, lens, None, cfg.fixed_len, cfg.scale)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    ro, rl = decode_ref(q, kc, vc, lens, None, cfg.scale)
+    check("gqa_decode_contig", o, lse, ro, rl)
+
+
+def test_decode_paged_config():
+    cfg = ai.CONFIGS["paged_gqa_decode"]
+    lens = ai.decode_lengths(cfg)
+    lay = ai.paged_layout(lens, cfg.page_size, cfg.seed)
+    q = ai.decode_q(cfg)
+    kp = ai.build_paged_cache(cfg, ai.T_K, lens, lay)
+    vp = ai.build_paged_cache(cfg, ai.T_V, lens, lay)
+    maxlen = int(lens.max())
+    o, lse = run_decode(q, kp, vp, lens, lay.block_table, maxlen, cfg.scale)
+    ro, rl = decode_ref(q, kp, vp, lens, lay.block_table, cfg.scale)
+    check("paged_gqa_decode", o, lse, ro, rl)
