@@ -96,9 +96,17 @@ void decode_split_kernel(DecodeParams a) {
   const uint16_t* vbase_c = a.vc + ((size_t)b * a.Hkv + kvh) * a.max_seqlen * D;
   const int32_t* table = PAGED ? a.block_table + (size_t)b * a.max_blocks : nullptr;
 
+  // Page ids of a 32-key block starting at tb (two 16-token pages, wave-uniform, so
+  // scalar loads).  They are fetched one block ahead of the K/V loads that use them.
+  auto block_pages = [&](int tb, int& p0, int& p1) {
+    if (PAGED && tb < t1) {
+      p0 = table[tb >> 4];
+      p1 = tb + 16 < t1 ? table[(tb >> 4) + 1] : p0;
+    }
+  };
   // one 32-key block: lane owns CPL chunks of K and of V (row = idx / (D/8))
   u32x4 kr[S::CPL], vr[S::CPL];
-  auto load_block = [&](int tb) {
+  auto load_block = [&](int tb, int p0, int p1) {
 #pragma unroll
     for (int i = 0; i < S::CPL; ++i) {
       const int cidx = lane + 64 * i;
@@ -107,7 +115,7 @@ void decode_split_kernel(DecodeParams a) {
       if (tok < t1) {
         size_t off;
         if (PAGED) {
-          const int page = table[tok >> 4];
+          const int page = (i * 64) / (D / 8) < 16 ? p0 : p1;  // row < 16 <=> first page
           off = (((size_t)page * a.Hkv + kvh) * 16 + (tok & 15)) * D + ch * 8;
           kr[i] = *(const u32x4*)(a.kc + off);
           vr[i] = *(const u32x4*)(a.vc + off);
@@ -149,14 +157,20 @@ void decode_split_kernel(DecodeParams a) {
 
   const int nblk = (t1 - t0 + S::BLK - 1) / S::BLK;
   int bi = wave;
-  if (bi < nblk) load_block(t0 + S::BLK * bi);
+  int pg0 = 0, pg1 = 0, npg0 = 0, npg1 = 0;
+  block_pages(t0 + S::BLK * bi, pg0, pg1);
+  block_pages(t0 + S::BLK * (bi + kDecodeWaves), npg0, npg1);
+  if (bi < nblk) load_block(t0 + S::BLK * bi, pg0, pg1);
   for (; bi < nblk; bi += kDecodeWaves) {
     const int tb = t0 + S::BLK * bi;
     store_block();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (bi + kDecodeWaves < nblk) load_block(tb + kDecodeWaves * S::BLK);
+    if (bi + kDecodeWaves < nblk) {
+      load_block(tb + kDecodeWaves * S::BLK, npg0, npg1);
+      block_pages(tb + 2 * kDecodeWaves * S::BLK, npg0, npg1);
+    }
 
     // S^T = K Q^T: two 16-key halves
     f32x4 s[2];

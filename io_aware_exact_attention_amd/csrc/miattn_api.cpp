@@ -24,7 +24,7 @@ struct Plan {
   int chunk;
 };
 
-constexpr int kAutoTargetWorkgroups = 2048;  // ~8 per compute unit on 256 CUs
+constexpr int kAutoTargetWorkgroups = 4096;  // ~16 per compute unit on 256 CUs
 constexpr int kMinChunk = 256;               // keys per chunk in the automatic plan
 constexpr int kMaxSplits = 1024;
 

@@ -1,17 +1,23 @@
 // Prefill: fused exact attention forward for many queries per sequence, gfx950.
 //
-// One workgroup (4 waves) owns BM = 128 consecutive queries of one (batch, head); each
-// wave owns 32 of them.  Key/value tiles of BN = 64 rows stream HBM -> registers -> LDS,
-// double-buffered so the loads of tile t+1 are in flight while tile t is computed.  Per
-// tile and wave:
+// One workgroup (8 waves, one workgroup per CU) owns BM = 256 queries of one
+// (batch, head); each wave owns 32 of them.  Key/value tiles of BN = 64 rows stream from
+// HBM straight into a 4-stage LDS ring (global_load_lds_dwordx4, issued two tiles ahead,
+// no register staging).  Per tile and wave:
 //   S^T = K_t Q^T       32x32x16 bf16 MFMA; K rows from LDS, Q^T held in registers.
 //                       Keys land in accumulator registers, queries on lanes, so the
-//                       row max / row sum of a query are mostly in-lane.
+//                       row max / row sum of a query are in-lane plus one exchange.
 //   online softmax      running max m and sum l per query; P = exp2(S*c - m*c)
-//                       rounded to bf16; l accumulates the rounded P.
+//                       rounded to bf16.
 //   O^T += V_t^T P^T    V^T read from LDS with the transposing LDS read, P^T straight
 //                       from the S^T accumulators (no LDS round trip).
 // The N x N score matrix never leaves registers.
+//
+// The 8 waves form two groups of 4 (one wave of each group per SIMD) that run half a
+// tile apart: while one group issues the MFMAs of a tile (P.V of the previous tile,
+// then Q.K^T of the current one), the other group does the softmax VALU work, so the
+// matrix cores and the vector ALUs of every SIMD are busy at the same time.  Slots are
+// separated by workgroup barriers.
 //
 // Method: page "FlashAttention 완전 정리" (cell-devlog), section "FlashAttention의 핵심
 // 아이디어 — Tiling": loop over Q blocks and K/V blocks in on-chip memory, reading Q, K,
@@ -20,8 +26,12 @@
 // partial result as each block arrives), with m, f, l as defined on the page "Flash
 // Attention: GPU 메모리_IO를 최적화하는..." (holysheep), section "Online Softmax".
 // Sequence-length parallelism (independent query-tile workgroups) follows the same
-// page's "FlashAttention 2" subsection; the load/compute overlap its "FlashAttention 3"
-// subsection describes is done here with a register-staged LDS double buffer.
+// page's "FlashAttention 2" subsection; the overlap of data movement with the matrix
+// units that its "FlashAttention 3" subsection (and the page "메모리 장벽을 넘어",
+// section "FlashAttention-3가 다른 이유") describes for Hopper is done here with LDS
+// DMA prefetch and the two-group schedule.
+
+#include <type_traits>
 
 #include "gfx950_common.h"
 #include "launch.h"
@@ -30,20 +40,29 @@ namespace miattn {
 
 template <int D>
 struct PrefillShape {
-  static constexpr int kWaves = 4;
-  static constexpr int BM = 32 * kWaves;       // queries per workgroup
-  static constexpr int BN = 64;                // keys per tile
-  static constexpr int KSTR = D * 2 + 16;      // LDS bytes per K row (pad: conflict-free b128 reads)
-  static constexpr int VSTR = D * 2 + 64;      // LDS bytes per V row (pad: conflict-free tr reads)
-  static constexpr int KTILE = BN * KSTR;
-  static constexpr int VTILE = BN * VSTR;
-  static constexpr int STAGE = KTILE + VTILE;
-  static constexpr int LDS = 2 * STAGE;
-  static constexpr int CHUNKS = BN * D / 8;    // 16-byte chunks per K (or V) tile
-  static constexpr int CPT = CHUNKS / (64 * kWaves);
-  static_assert(CHUNKS % (64 * kWaves) == 0, "tile must split evenly over threads");
+  static constexpr int kWaves = 8;
+  static constexpr int BM = 32 * kWaves;        // queries per workgroup
+  static constexpr int BN = 64;                 // keys per tile
+  static constexpr int ROWB = D * 2;            // bytes per K/V row in LDS (swizzled, unpadded)
+  static constexpr int CPR = D / 8;             // 16-byte chunks per row
+  static constexpr int TILE = BN * ROWB;        // bytes of one K (or V) tile
+  static constexpr int STAGES = 4;
+  static constexpr int STAGE = 2 * TILE;        // K tile then V tile
+  static constexpr int LDS = STAGES * STAGE;
+  static constexpr int DMA = TILE / 16 / (64 * kWaves);  // 16-byte loads per thread per tensor
+  static constexpr int LOADS_PER_TILE = 2 * DMA;
+  static_assert(TILE % (16 * 64 * kWaves) == 0, "tile must split evenly over threads");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
+
+// XOR applied to the 16-byte chunk index of row R.  Chosen so that both LDS read
+// patterns are free of bank conflicts: the K operand read (16 lanes, 16 different rows,
+// same chunk) and the transposing V read (4 consecutive rows x 4 consecutive chunks).
+template <int D>
+__device__ __forceinline__ int chunk_swizzle(int R) {
+  if constexpr (D == 128) return ((R & 3) << 2) | ((R >> 2) & 3);
+  else return (((R >> 1) & 1) << 2) | ((R >> 2) & 3);
+}
 
 // Row index within a 32-key block that the MFMA A operand of lane l loads, chosen so
 // that accumulator r of lane group g holds key 16*(r/8) + 8*g + r%8: with that order
@@ -52,16 +71,40 @@ __device__ __forceinline__ int swap_bits_2_3(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Workgroup barrier that is also a hard scheduling boundary: no instruction (memory or
+// ALU) is moved across it, so the MFMA and softmax phases of the two wave groups stay
+// where the schedule puts them.  The LDS DMA writes are ordered by explicit vmcnt waits
+// before it.
+__device__ __forceinline__ void block_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillParams a) {
   using S = PrefillShape<D>;
-  __shared__ __attribute__((aligned(16))) char smem[S::LDS];
+  __shared__ __attribute__((aligned(1024))) char smem[S::LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int g = lane >> 5;  // which half of the keys / head dim this lane's operands hold
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;   // ping-pong group
+  const int g = lane >> 5;     // which half of the keys / head dim this lane's operands hold
 
   // --- workgroup -> (query tile, head, batch); XCD-grouped, heaviest causal tiles first
   const int L = xcd_remap(blockIdx.x, a.total_wg);
@@ -78,16 +121,38 @@ void prefill_kernel(PrefillParams a) {
   const uint16_t* __restrict__ Kh = a.k + (size_t)(b * a.Hkv + kvh) * a.Nk * D;
   const uint16_t* __restrict__ Vh = a.v + (size_t)(b * a.Hkv + kvh) * a.Nk * D;
 
-  // keys this workgroup needs: everything, or up to the diagonal of its last query
+  // keys the workgroup needs: everything, or up to the diagonal of its last query
   int kend = a.Nk;
   if (CAUSAL) kend = min(a.Nk, min(m0 + S::BM, a.Nq) - 1 + off + 1);
   const int ntiles = (kend + S::BN - 1) / S::BN;
 
-  // keys this wave needs (it skips tiles wholly above its diagonal, and everything when
-  // all its rows are padding past Nq)
-  const int wrow0 = m0 + 32 * wave;
-  int wkend = 0;
-  if (wrow0 < a.Nq) wkend = CAUSAL ? min(a.Nk, min(wrow0 + 31, a.Nq - 1) + off + 1) : a.Nk;
+  // This wave's 32 query rows.  The two groups interleave 32-row blocks so that both
+  // reach the causal diagonal at about the same tile.
+  const int wrow0 = m0 + 32 * (2 * (wave & 3) + grp);
+  int wtiles = 0;  // tiles this wave computes (0 when all its rows are padding past Nq)
+  if (wrow0 < a.Nq) {
+    const int wk = CAUSAL ? min(a.Nk, min(wrow0 + 31, a.Nq - 1) + off + 1) : a.Nk;
+    wtiles = (wk + S::BN - 1) / S::BN;
+  }
+
+  // --- LDS DMA of one K/V tile: wave-instruction i of this wave fills 1 KB of the
+  // stage; lane l fetches the chunk that belongs at LDS position l of that KB.
+  auto issue_tile = [&](int j) {
+    const int n0 = j * S::BN;
+    char* st = smem + (j & (S::STAGES - 1)) * S::STAGE;
+#pragma unroll
+    for (int i = 0; i < S::DMA; ++i) {
+      const int blk = i * S::kWaves + wave;
+      const int p = blk * 64 + lane;
+      const int R = p / S::CPR;
+      const int c = (p % S::CPR) ^ chunk_swizzle<D>(R);
+      const int key = min(n0 + R, a.Nk - 1);  // ragged tail: a real row, masked later
+      const size_t goff = (size_t)key * D + c * 8;
+      __builtin_amdgcn_global_load_lds(Kh + goff, (lds_void*)(st + blk * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(Vh + goff, (lds_void*)(st + S::TILE + blk * 1024), 16,
+                                       0, 0);
+    }
+  };
 
   // --- Q^T operand: lane holds query row qrow, head-dim slots 16*s + 8*g .. +7
   const int qrow = wrow0 + (lane & 31);
@@ -104,149 +169,216 @@ void prefill_kernel(PrefillParams a) {
     }
   }
 
-  // --- K/V tile staging: thread owns CPT 16-byte chunks of each tile
-  u32x4 kreg[S::CPT], vreg[S::CPT];
-  auto load_tile = [&](int t) {
-    const int n0 = t * S::BN;
+  // Q loads are issued first, so the wait below covers exactly Q and tile 0.
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (ntiles > 0) issue_tile(0);
+  if (ntiles > 1) issue_tile(1);
+
+  // --- lane-constant LDS offsets (within a stage)
+  int koff[D / 16];  // K operand: row swap23(lane%32), logical chunk 2*st + g
+  {
+    const int R = swap_bits_2_3(lane & 31);
+    const int sw = chunk_swizzle<D>(R);
 #pragma unroll
-    for (int i = 0; i < S::CPT; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / (D / 8), ch = c % (D / 8);
-      const int key = n0 + row;
-      if (key < a.Nk) {
-        kreg[i] = *(const u32x4*)(Kh + (size_t)key * D + ch * 8);
-        vreg[i] = *(const u32x4*)(Vh + (size_t)key * D + ch * 8);
-      } else {  // ragged tail: zero rows (their scores are masked, 0 * V stays finite)
-        kreg[i] = u32x4{0, 0, 0, 0};
-        vreg[i] = u32x4{0, 0, 0, 0};
+    for (int st = 0; st < D / 16; ++st) koff[st] = R * S::ROWB + (((2 * st + g) ^ sw) << 4);
+  }
+  int voff[D / 32][2];  // V^T operand via transposing reads: rows 8g + 4h + (i16>>2)
+  {
+    const int i16 = lane & 15, q4 = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int R = 8 * (q4 >> 1) + 4 * h + (i16 >> 2);
+      const int sw = chunk_swizzle<D>(R);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int c = 4 * db + 2 * (q4 & 1) + ((i16 & 3) >> 1);
+        voff[db][h] = S::TILE + R * S::ROWB + ((c ^ sw) << 4) + ((i16 & 1) << 3);
       }
     }
-  };
-  auto store_tile = [&](int buf) {
-    char* kb = smem + buf * S::STAGE;
-    char* vb = kb + S::KTILE;
-#pragma unroll
-    for (int i = 0; i < S::CPT; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / (D / 8), ch = c % (D / 8);
-      *(u32x4*)(kb + row * S::KSTR + ch * 16) = kreg[i];
-      *(u32x4*)(vb + row * S::VSTR + ch * 16) = vreg[i];
-    }
-  };
+  }
 
-  const float c = a.c;  // |scale| * log2(e)
+  const float c = a.c;      // |scale| * log2(e)
   float m_run = -INFINITY;  // reference max (raw score units) of this lane's query
   float l_run = 0.f;        // sum of bf16-rounded P over this lane's half of the keys
   float l_ex = 0.f;         // sum of unrounded P (for the LSE)
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
+  f32x16 sacc[2] = {f32x16{}, f32x16{}};
+  uint32_t pk[2][8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pk[i][j] = 0;
 
-  // lane-constant parts of the LDS addresses
-  const int krow_l = swap_bits_2_3(lane & 31);
-  const int i16 = lane & 15, q4 = lane >> 4;
-  const int vrow_l = 8 * (q4 >> 1) + (i16 >> 2);
-  const int vcol_l = 16 * (q4 & 1) + 4 * (i16 & 3);
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const bool more = t + 1 < ntiles;
-    if (more) load_tile(t + 1);
-    const int n0 = t * S::BN;
-
-    if (n0 < wkend) {
-      const char* kb = smem + (t & 1) * S::STAGE;
-      const char* vb = kb + S::KTILE;
-
-      // S^T = K Q^T for two 32-key blocks
-      f32x16 s[2];
+  // P.V of tile j (V^T through transposing reads, P^T from registers)
+  auto pv = [&](int j) {
+    const char* st = smem + (j & (S::STAGES - 1)) * S::STAGE;
 #pragma unroll
-      for (int kb_ = 0; kb_ < 2; ++kb_) {
-        s[kb_] = f32x16{};
-        const char* kp = kb + (kb_ * 32 + krow_l) * S::KSTR + g * 16;
+    for (int t4 = 0; t4 < 4; ++t4) {
+      const u32x4 pw = {pk[t4 >> 1][4 * (t4 & 1) + 0], pk[t4 >> 1][4 * (t4 & 1) + 1],
+                        pk[t4 >> 1][4 * (t4 & 1) + 2], pk[t4 >> 1][4 * (t4 & 1) + 3]};
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-          const bf16x8 ka = *(const bf16x8*)(kp + st * 32);
-          s[kb_] = mfma_32x32x16(ka, qop[st], s[kb_]);
-        }
-      }
-
-      // causal mask on tiles crossing this wave's diagonal; ragged key tail
-      const bool masked = (n0 + S::BN > a.Nk) || (CAUSAL && n0 + S::BN - 1 > wrow0 + off);
-      const int lim = CAUSAL ? min(a.Nk - 1, qrow + off) : a.Nk - 1;  // last visible key
-      const int kbase = n0 + 8 * g;
-      if (masked) {
-#pragma unroll
-        for (int kb_ = 0; kb_ < 2; ++kb_)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (kbase + kb_ * 32 + 16 * (r >> 3) + (r & 7) > lim) s[kb_][r] = -INFINITY;
-      }
-
-      // online softmax: tile max, lazy rescale of the running state
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb_ = 0; kb_ < 2; ++kb_)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb_][r]);
-      mx = fmaxf(mx, wave_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const bool grow = (m_run == -INFINITY) || ((m_new - m_run) * c > kRescaleLog2);
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float alpha =
-            grow ? (m_run == -INFINITY ? 0.f : fast_exp2((m_run - m_new) * c)) : 1.f;
-        m_run = grow ? m_new : m_run;
-        l_run *= alpha;
-        l_ex *= alpha;
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
-      }
-      const float mc = m_run * c;
-
-      // P = exp2(S*c - m*c) -> bf16 pairs.  The sum that normalises O accumulates the
-      // rounded values (O is then an exact convex combination of the V rows under the
-      // weights the MFMA used); the LSE uses the sum of the unrounded values.
-      uint32_t pk[2][8];
-      float ex0 = 0.f, ex1 = 0.f;
-#pragma unroll
-      for (int kb_ = 0; kb_ < 2; ++kb_)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          float p0 = fast_exp2(fmaf(s[kb_][2 * j], c, -mc));
-          float p1 = fast_exp2(fmaf(s[kb_][2 * j + 1], c, -mc));
-          if (masked) {  // exact zeros for masked keys (also when c == 0)
-            const int k0 = kbase + kb_ * 32 + 16 * ((2 * j) >> 3) + ((2 * j) & 7);
-            p0 = k0 > lim ? 0.f : p0;
-            p1 = k0 + 1 > lim ? 0.f : p1;
-          }
-          pk[kb_][j] = pack_bf16x2(p0, p1);
-          l_run = add_bf16x2(pk[kb_][j], l_run);
-          ex0 += p0;
-          ex1 += p1;
-        }
-      l_ex += ex0 + ex1;
-
-      // O^T += V^T P^T, four 16-key steps
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-        const u32x4 pw = {pk[t4 >> 1][4 * (t4 & 1) + 0], pk[t4 >> 1][4 * (t4 & 1) + 1],
-                          pk[t4 >> 1][4 * (t4 & 1) + 2], pk[t4 >> 1][4 * (t4 & 1) + 3]};
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-        const char* vp = vb + (16 * t4 + vrow_l) * S::VSTR + vcol_l * 2;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16x4 lo = lds_read_tr(vp + db * 64);
-          const bf16x4 hi = lds_read_tr(vp + db * 64 + 4 * S::VSTR);
-          oacc[db] = mfma_32x32x16(concat(lo, hi), pb, oacc[db]);
-        }
+      for (int db = 0; db < D / 32; ++db) {
+        const bf16x4 lo = lds_read_tr(st + voff[db][0] + t4 * 16 * S::ROWB);
+        const bf16x4 hi = lds_read_tr(st + voff[db][1] + t4 * 16 * S::ROWB);
+        oacc[db] = mfma_32x32x16(concat(lo, hi), pb, oacc[db]);
       }
     }
+    // keep the transposing reads six MFMAs ahead (enough to cover LDS latency without
+    // running out of registers)
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * (D / 32) - 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+  };
 
-    if (more) store_tile((t + 1) & 1);
-    __syncthreads();
+  // S^T = K_j Q^T for the two 32-key halves of tile j
+  auto qk = [&](int j) {
+    const char* st = smem + (j & (S::STAGES - 1)) * S::STAGE;
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) {
+      const bf16x8 a0 = *(const bf16x8*)(st + koff[k]);
+      const bf16x8 a1 = *(const bf16x8*)(st + koff[k] + 32 * S::ROWB);
+      s0 = mfma_32x32x16(a0, qop[k], s0);
+      s1 = mfma_32x32x16(a1, qop[k], s1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * (D / 16) - 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    sacc[0] = s0;
+    sacc[1] = s1;
+  };
+
+  // online softmax of tile j held in sacc; MASK applies the causal diagonal and the
+  // ragged key tail (selects, no branches).
+  const int lim = CAUSAL ? min(a.Nk - 1, qrow + off) : a.Nk - 1;  // last visible key
+  auto softmax = [&](int j, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int kbase = j * S::BN + 8 * g;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = sacc[kb][r];
+        if (MASK) v = (kbase + kb * 32 + 16 * (r >> 3) + (r & 7) > lim) ? -INFINITY : v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, wave_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const bool grow = (m_run == -INFINITY) || ((m_new - m_run) * c > kRescaleLog2);
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float alpha =
+          grow ? (m_run == -INFINITY ? 0.f : fast_exp2((m_run - m_new) * c)) : 1.f;
+      m_run = grow ? m_new : m_run;
+      l_run *= alpha;
+      l_ex *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+    }
+    const float mc = m_run * c;
+    // P = exp2(S*c - m*c) -> bf16 pairs.  O is normalised by the sum of the rounded
+    // values (an exact convex combination under the weights the MFMA uses); the LSE by
+    // the sum of the unrounded values.
+    float ex0 = 0.f, ex1 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        float p0 = fast_exp2(fmaf(sacc[kb][2 * jj], c, -mc));
+        float p1 = fast_exp2(fmaf(sacc[kb][2 * jj + 1], c, -mc));
+        if (MASK) {  // exact zeros for masked keys (also when c == 0)
+          const int k0 = kbase + kb * 32 + 16 * ((2 * jj) >> 3) + ((2 * jj) & 7);
+          p0 = k0 > lim ? 0.f : p0;
+          p1 = k0 + 1 > lim ? 0.f : p1;
+        }
+        pk[kb][jj] = pack_bf16x2(p0, p1);
+        l_run = add_bf16x2(pk[kb][jj], l_run);
+        ex0 += p0;
+        ex1 += p1;
+      }
+    l_ex += ex0 + ex1;
+  };
+
+  // Slot bookkeeping shared by both groups.  Slot 2j: tile j+2 is prefetched into the
+  // stage tile j-2 used.  End of slot 2j+1: tile j+1 must be resident.
+  auto slot_begin = [&](int s) {
+    if ((s & 1) == 0 && (s >> 1) + 2 < ntiles) issue_tile((s >> 1) + 2);
+  };
+  auto slot_end = [&](int s) {
+    if (s & 1) {
+      const int jw = (s + 1) >> 1;
+      if (jw + 1 < ntiles) wait_vmcnt<S::LOADS_PER_TILE>();
+      else wait_vmcnt<0>();
+    }
+    block_barrier();
+  };
+
+  // First tile that needs masking for some row of the workgroup: the causal diagonal of
+  // its first query row, or the ragged end of the keys.
+  int jm = a.Nk / S::BN;
+  if (CAUSAL) jm = min(jm, (m0 + off + 1) / S::BN);
+  jm = min(jm, ntiles);
+
+  // tile 0 resident before slot 0
+  if (ntiles > 1) wait_vmcnt<S::LOADS_PER_TILE>(); else wait_vmcnt<0>();
+  block_barrier();
+
+  // Group 0: slot 2j = MFMA (P.V of j-1, Q.K^T of j), slot 2j+1 = softmax of j.
+  // Group 1 runs one slot behind: slot 2j = softmax of j-1, slot 2j+1 = MFMA.
+  // Unmasked tiles j < jm need no per-wave guards (every wave's rows see them whole).
+  std::integral_constant<bool, false> nomask;
+  std::integral_constant<bool, true> withmask;
+  if (grp == 0) {
+    int j = 0;
+    for (; j < jm; ++j) {
+      slot_begin(2 * j);
+      if (j >= 1) pv(j - 1);
+      qk(j);
+      slot_end(2 * j);
+      slot_begin(2 * j + 1);
+      softmax(j, nomask);
+      slot_end(2 * j + 1);
+    }
+    for (; j <= ntiles; ++j) {
+      slot_begin(2 * j);
+      if (j >= 1 && j - 1 < wtiles) pv(j - 1);
+      if (j < wtiles) qk(j);
+      slot_end(2 * j);
+      slot_begin(2 * j + 1);
+      if (j < wtiles) softmax(j, withmask);
+      slot_end(2 * j + 1);
+    }
+  } else {
+    int j = 0;
+    for (; j < jm; ++j) {
+      slot_begin(2 * j);
+      if (j >= 1) softmax(j - 1, nomask);
+      slot_end(2 * j);
+      slot_begin(2 * j + 1);
+      if (j >= 1) pv(j - 1);
+      qk(j);
+      slot_end(2 * j + 1);
+    }
+    for (; j <= ntiles; ++j) {
+      slot_begin(2 * j);
+      if (j >= 1 && j - 1 < wtiles) softmax(j - 1, withmask);
+      slot_end(2 * j);
+      slot_begin(2 * j + 1);
+      if (j >= 1 && j - 1 < wtiles) pv(j - 1);
+      if (j < wtiles) qk(j);
+      slot_end(2 * j + 1);
+    }
   }
 
   // --- epilogue: O = acc / l -> bf16; LSE = m*scale + ln l
@@ -271,12 +403,13 @@ void prefill_kernel(PrefillParams a) {
 
 template <int D, bool CAUSAL>
 static hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_kernel<D, CAUSAL>), dim3(p.total_wg), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((prefill_kernel<D, CAUSAL>), dim3(p.total_wg), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill(PrefillParams p, int d, int causal, hipStream_t stream) {
-  p.num_qtiles = (p.Nq + PrefillShape<128>::BM - 1) / PrefillShape<128>::BM;
+  constexpr int BM = PrefillShape<128>::BM;
+  p.num_qtiles = (p.Nq + BM - 1) / BM;
   p.total_wg = p.num_qtiles * p.Hq * p.B;
   if (d == 64) return causal ? launch_one<64, true>(p, stream) : launch_one<64, false>(p, stream);
   return causal ? launch_one<128, true>(p, stream) : launch_one<128, false>(p, stream);
