@@ -40,8 +40,18 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i
 // supplies the address of 4 consecutive bf16 holding row i/4, columns 4*(i%4)..+3 of a
 // 4x16 block; lane i receives column i of that block (rows 0..3).
-__device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
+//
+// The restrict-qualified pointer gives each such read an alias scope of its own.  The
+// compiler then does not make the read wait for every LDS DMA (global_load_lds) still in
+// flight; kernels that fill LDS by DMA order those writes and the reads themselves, with
+// explicit vmcnt waits followed by a workgroup barrier.
+__device__ __forceinline__ bf16x4 lds_read_tr(const char* __restrict__ p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+}
+
+// 16-byte LDS read (ds_read_b128) with the same alias-scope property as lds_read_tr.
+__device__ __forceinline__ bf16x8 lds_read_b128(const char* __restrict__ p) {
+  return *(const bf16x8*)p;
 }
 
 __device__ __forceinline__ bf16x8 concat(bf16x4 lo, bf16x4 hi) {
@@ -65,15 +75,5 @@ __device__ __forceinline__ float add_bf16x2(uint32_t x, float acc) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float wave_xor(float x, int m) { return __shfl_xor(x, m, 64); }
-
-// Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).  Give XCD x a
-// contiguous range of logical work ids so that neighbouring ids (same head, adjacent
-// query tiles) share one L2.  Bijective on [0, total).
-__device__ __forceinline__ int xcd_remap(int p, int total) {
-  const int per = total >> 3, rem = total & 7;
-  const int x = p & 7, k = p >> 3;
-  const int base = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
-  return base + k;
-}
 
 }  // namespace miattn

@@ -17,6 +17,7 @@ struct PrefillParams {
   int negate_q;   // scale < 0: Q's sign is flipped on load (exact) so c >= 0
   int num_qtiles; // filled by launch_prefill
   int total_wg;   // filled by launch_prefill
+  int head_group; // filled by launch_prefill: heads whose query tiles are interleaved
 };
 
 struct DecodeParams {

@@ -94,6 +94,37 @@ __device__ __forceinline__ void block_barrier() {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Order in which workgroups take (query tile, head) pairs.  Workgroup p runs on XCD
+// p % 8.  When the B*Hq heads split evenly over the 8 XCDs, XCD x owns a contiguous block
+// of them, so a head's K/V (and those of heads sharing a KV head) are read through one L2.
+// Within its block the XCD walks groups of head_group heads; inside a group the query
+// tiles go out by rank (rank 0 of every head in the group, then rank 1, ...).  Rank 0 is
+// the last query tile under causal masking, the one that sees the most keys, so each
+// group's long tiles start first and its short ones fill in behind them.  head_group is
+// sized so that a group's K/V fit in one XCD's L2.  With heads that do not split evenly
+// the same grouping runs over all heads, without the XCD blocks.
+struct WorkItem {
+  int qrank;
+  int bh;
+};
+
+__device__ __forceinline__ WorkItem prefill_work_item(int p, int BH, int nq, int hg) {
+  int nh = BH, k = p, hbase = 0;
+  if ((BH & 7) == 0) {
+    nh = BH >> 3;
+    k = p >> 3;
+    hbase = (p & 7) * nh;
+  }
+  const int gsize = hg * nq;
+  const int gidx = k / gsize;
+  const int r = k - gidx * gsize;
+  const int hcount = min(hg, nh - gidx * hg);
+  WorkItem w;
+  w.qrank = r / hcount;
+  w.bh = hbase + gidx * hg + (r - w.qrank * hcount);
+  return w;
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillParams a) {
@@ -106,13 +137,11 @@ void prefill_kernel(PrefillParams a) {
   const int grp = wave >> 2;   // ping-pong group
   const int g = lane >> 5;     // which half of the keys / head dim this lane's operands hold
 
-  // --- workgroup -> (query tile, head, batch); XCD-grouped, heaviest causal tiles first
-  const int L = xcd_remap(blockIdx.x, a.total_wg);
-  const int qi = L % a.num_qtiles;
-  const int bh = L / a.num_qtiles;
-  const int hq = bh % a.Hq;
-  const int b = bh / a.Hq;
-  const int qtile = CAUSAL ? (a.num_qtiles - 1 - qi) : qi;
+  // --- workgroup -> (query tile, head, batch)
+  const WorkItem wi = prefill_work_item(blockIdx.x, a.B * a.Hq, a.num_qtiles, a.head_group);
+  const int hq = wi.bh % a.Hq;
+  const int b = wi.bh / a.Hq;
+  const int qtile = CAUSAL ? (a.num_qtiles - 1 - wi.qrank) : wi.qrank;
   const int kvh = hq / (a.Hq / a.Hkv);
   const int m0 = qtile * S::BM;
   const int off = a.Nk - a.Nq;  // bottom-right causal alignment
@@ -243,8 +272,8 @@ void prefill_kernel(PrefillParams a) {
     f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
     for (int k = 0; k < D / 16; ++k) {
-      const bf16x8 a0 = *(const bf16x8*)(st + koff[k]);
-      const bf16x8 a1 = *(const bf16x8*)(st + koff[k] + 32 * S::ROWB);
+      const bf16x8 a0 = lds_read_b128(st + koff[k]);
+      const bf16x8 a1 = lds_read_b128(st + koff[k] + 32 * S::ROWB);
       s0 = mfma_32x32x16(a0, qop[k], s0);
       s1 = mfma_32x32x16(a1, qop[k], s1);
     }
@@ -411,6 +440,15 @@ hipError_t launch_prefill(PrefillParams p, int d, int causal, hipStream_t stream
   constexpr int BM = PrefillShape<128>::BM;
   p.num_qtiles = (p.Nq + BM - 1) / BM;
   p.total_wg = p.num_qtiles * p.Hq * p.B;
+  // Heads per dispatch group: as many as keep the group's K and V within 4 MiB (one
+  // XCD's L2), at least 1, at most the heads one XCD owns.
+  {
+    const int BH = p.B * p.Hq;
+    const int nh = (BH % 8 == 0) ? BH / 8 : BH;
+    const double kv_bytes = 2.0 * p.Nk * d * 2.0;
+    int hg = (int)((4.0 * 1024 * 1024) / kv_bytes);
+    p.head_group = hg < 1 ? 1 : (hg > nh ? nh : hg);
+  }
   if (d == 64) return causal ? launch_one<64, true>(p, stream) : launch_one<64, false>(p, stream);
   return causal ? launch_one<128, true>(p, stream) : launch_one<128, false>(p, stream);
 }
