@@ -69,7 +69,8 @@ typedef enum {
  *
  * Errors: INVALID_ARGUMENT for a null q/k/v/o, misalignment, any size < 1,
  * Hq % Hkv != 0, causal with Nq > Nk, non-finite scale; UNSUPPORTED for d not in
- * {64,128} or a grid beyond 2^31-1 workgroups; HIP if the launch fails.
+ * {64,128}, a grid beyond 2^31-1 workgroups, or Nk*d*2 beyond 2^31-1 bytes (one head's
+ * K must fit a 32-bit buffer range); HIP if the launch fails.
  */
 int attn_fwd_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,

@@ -16,6 +16,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
+// Word 3 of a buffer resource descriptor on gfx9-family chips: 32-bit data format, raw
+// (stride 0) addressing.  Buffer loads past num_records return zeros.
+constexpr int kBufferFlags = 0x00020000;
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // The running max used for exponentiation is only moved up when a row's true max
@@ -23,6 +27,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 // <= kRescaleLog2 and P <= 2^kRescaleLog2, far from fp32/bf16 overflow.  In exact
 // arithmetic the result does not depend on which reference max is used.
 constexpr float kRescaleLog2 = 8.0f;
+// Prefill variant of the same idea: a tile's weights are formed against the current
+// reference max and only redone against a fresh one when their sum exceeds 2^32 (or is
+// not finite).  Weights then stay below 2^32, so O and l cannot overflow for any input
+// that the exact softmax can handle.
+constexpr float kRedoBound = 4294967296.0f;
 
 // D = A(32x16) * B(16x32) + C, bf16 inputs, fp32 accumulate.
 // Lane l holds A[l%32][8*(l/32) .. +7], B[8*(l/32) .. +7][l%32] and
@@ -52,6 +61,19 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* __restrict__ p) {
 // 16-byte LDS read (ds_read_b128) with the same alias-scope property as lds_read_tr.
 __device__ __forceinline__ bf16x8 lds_read_b128(const char* __restrict__ p) {
   return *(const bf16x8*)p;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One 16-byte-per-lane LDS DMA (buffer_load_dwordx4 ... lds): lane l reads
+// base + voff[l] (bytes) and the wave's 1 KB lands contiguously at dst, lane l at
+// dst + 16*l.  The descriptor covers nbytes from base; reads beyond it return zeros.
+// Counted by vmcnt like any vector-memory load.
+__device__ __forceinline__ void lds_dma16(const void* base, int nbytes, uint32_t voff,
+                                          lds_void* dst) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, kBufferFlags);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 concat(bf16x4 lo, bf16x4 hi) {

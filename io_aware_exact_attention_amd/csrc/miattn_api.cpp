@@ -91,6 +91,8 @@ int attn_fwd_prefill(const void* q, const void* k, const void* v, void* o, float
   const long qtiles = (Nq + 127) / 128;
   if (qtiles * (long)Hq * B > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
   if ((long)B * Hq > 0x7fffffffL || (long)B * Hkv > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
+  // one head's K (or V) must fit a buffer descriptor's 32-bit byte range
+  if ((long)Nk * d * 2 > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
 
   miattn::PrefillParams p{};
   p.q = static_cast<const uint16_t*>(q);

@@ -92,8 +92,6 @@ __device__ __forceinline__ void block_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 // Order in which workgroups take (query tile, head) pairs.  Workgroup p runs on XCD
 // p % 8.  When the B*Hq heads split evenly over the 8 XCDs, XCD x owns a contiguous block
 // of them, so a head's K/V (and those of heads sharing a KV head) are read through one L2.
@@ -164,22 +162,29 @@ void prefill_kernel(PrefillParams a) {
     wtiles = (wk + S::BN - 1) / S::BN;
   }
 
-  // --- LDS DMA of one K/V tile: wave-instruction i of this wave fills 1 KB of the
-  // stage; lane l fetches the chunk that belongs at LDS position l of that KB.
+  // --- LDS DMA of one K/V tile (buffer_load ... lds): wave-instruction i of this wave
+  // fills 1 KB of the stage; lane l fetches the chunk that belongs at LDS position l of
+  // that KB.  The buffer descriptor of tile j starts at its first key row and covers the
+  // rows left, so rows past Nk read as zeros (their scores are masked).  The per-lane
+  // offsets are the same for every tile; all per-tile address work is scalar.
+  uint32_t dma_off[S::DMA];
+#pragma unroll
+  for (int i = 0; i < S::DMA; ++i) {
+    const int p = (i * S::kWaves + wave) * 64 + lane;
+    const int R = p / S::CPR;
+    dma_off[i] = R * S::ROWB + (((p % S::CPR) ^ chunk_swizzle<D>(R)) << 4);
+  }
   auto issue_tile = [&](int j) {
     const int n0 = j * S::BN;
     char* st = smem + (j & (S::STAGES - 1)) * S::STAGE;
+    const int nbytes = (a.Nk - n0) * (D * 2);
+    const uint16_t* kt = Kh + (size_t)n0 * D;
+    const uint16_t* vt = Vh + (size_t)n0 * D;
 #pragma unroll
     for (int i = 0; i < S::DMA; ++i) {
       const int blk = i * S::kWaves + wave;
-      const int p = blk * 64 + lane;
-      const int R = p / S::CPR;
-      const int c = (p % S::CPR) ^ chunk_swizzle<D>(R);
-      const int key = min(n0 + R, a.Nk - 1);  // ragged tail: a real row, masked later
-      const size_t goff = (size_t)key * D + c * 8;
-      __builtin_amdgcn_global_load_lds(Kh + goff, (lds_void*)(st + blk * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(Vh + goff, (lds_void*)(st + S::TILE + blk * 1024), 16,
-                                       0, 0);
+      lds_dma16(kt, nbytes, dma_off[i], (lds_void*)(st + blk * 1024));
+      lds_dma16(vt, nbytes, dma_off[i], (lds_void*)(st + S::TILE + blk * 1024));
     }
   };
 
@@ -228,8 +233,7 @@ void prefill_kernel(PrefillParams a) {
 
   const float c = a.c;      // |scale| * log2(e)
   float m_run = -INFINITY;  // reference max (raw score units) of this lane's query
-  float l_run = 0.f;        // sum of bf16-rounded P over this lane's half of the keys
-  float l_ex = 0.f;         // sum of unrounded P (for the LSE)
+  float l_ex = 0.f;         // sum of the unrounded weights over this lane's half of the keys
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
@@ -288,55 +292,57 @@ void prefill_kernel(PrefillParams a) {
     sacc[1] = s1;
   };
 
-  // online softmax of tile j held in sacc; MASK applies the causal diagonal and the
-  // ragged key tail (selects, no branches).
+  // Online softmax of tile j held in sacc; MASK applies the causal diagonal and the ragged
+  // key tail.  The weights are formed against the current reference max m_run first.  The
+  // max is only recomputed, the two lanes of a query exchange theirs and O and l are
+  // rescaled, when some weight of the tile exceeds 2^kRedoLog2 (the reference has fallen
+  // far behind the scores) or could not be formed at all.  On the first tile m_run is -inf,
+  // so every weight is +inf or NaN and that path runs.  Otherwise the weights stay at most
+  // 2^kRedoLog2, far inside the fp32 and bf16 range, and the result is the same softmax.
   const int lim = CAUSAL ? min(a.Nk - 1, qrow + off) : a.Nk - 1;  // last visible key
   auto softmax = [&](int j, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const int kbase = j * S::BN + 8 * g;
-    float mx = -INFINITY;
+    if (MASK) {
+      const int kbase = j * S::BN + 8 * g;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = sacc[kb][r];
-        if (MASK) v = (kbase + kb * 32 + 16 * (r >> 3) + (r & 7) > lim) ? -INFINITY : v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, wave_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const bool grow = (m_run == -INFINITY) || ((m_new - m_run) * c > kRescaleLog2);
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float alpha =
-          grow ? (m_run == -INFINITY ? 0.f : fast_exp2((m_run - m_new) * c)) : 1.f;
-      m_run = grow ? m_new : m_run;
-      l_run *= alpha;
+        for (int r = 0; r < 16; ++r)
+          sacc[kb][r] = (kbase + kb * 32 + 16 * (r >> 3) + (r & 7) > lim) ? -INFINITY : sacc[kb][r];
+    }
+    // P = exp2(S*c - m*c) -> bf16 pairs, and the tile's sum of the unrounded weights
+    auto weights = [&]() {
+      const float nmc = -(m_run * c);
+      float ex0 = 0.f, ex1 = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const float p0 = fast_exp2(fmaf(sacc[kb][2 * jj], c, nmc));
+          const float p1 = fast_exp2(fmaf(sacc[kb][2 * jj + 1], c, nmc));
+          pk[kb][jj] = pack_bf16x2(p0, p1);
+          ex0 += p0;
+          ex1 += p1;
+        }
+      return ex0 + ex1;
+    };
+    float ts = weights();
+    if (__builtin_amdgcn_ballot_w64(!(ts <= kRedoBound))) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+      mx = fmaxf(mx, wave_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_run == -INFINITY ? 0.f : fast_exp2((m_run - m_new) * c);
+      m_run = m_new;
       l_ex *= alpha;
 #pragma unroll
       for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+      ts = weights();
     }
-    const float mc = m_run * c;
-    // P = exp2(S*c - m*c) -> bf16 pairs.  O is normalised by the sum of the rounded
-    // values (an exact convex combination under the weights the MFMA uses); the LSE by
-    // the sum of the unrounded values.
-    float ex0 = 0.f, ex1 = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        float p0 = fast_exp2(fmaf(sacc[kb][2 * jj], c, -mc));
-        float p1 = fast_exp2(fmaf(sacc[kb][2 * jj + 1], c, -mc));
-        if (MASK) {  // exact zeros for masked keys (also when c == 0)
-          const int k0 = kbase + kb * 32 + 16 * ((2 * jj) >> 3) + ((2 * jj) & 7);
-          p0 = k0 > lim ? 0.f : p0;
-          p1 = k0 + 1 > lim ? 0.f : p1;
-        }
-        pk[kb][jj] = pack_bf16x2(p0, p1);
-        l_run = add_bf16x2(pk[kb][jj], l_run);
-        ex0 += p0;
-        ex1 += p1;
-      }
-    l_ex += ex0 + ex1;
+    l_ex += ts;
   };
 
   // Slot bookkeeping shared by both groups.  Slot 2j: tile j+2 is prefetched into the
@@ -411,8 +417,7 @@ void prefill_kernel(PrefillParams a) {
   }
 
   // --- epilogue: O = acc / l -> bf16; LSE = m*scale + ln l
-  const float l_tot = l_run + wave_xor(l_run, 32);
-  const float l_lse = l_ex + wave_xor(l_ex, 32);
+  const float l_tot = l_ex + wave_xor(l_ex, 32);
   if (qrow < a.Nq) {
     const float inv = 1.f / l_tot;
     uint16_t* orow = a.o + ((size_t)(b * a.Hq + hq) * a.Nq + qrow) * D;
@@ -426,7 +431,7 @@ void prefill_kernel(PrefillParams a) {
         *(u32x2*)(orow + dv) = w;
       }
     if (g == 0 && a.lse)
-      a.lse[(size_t)(b * a.Hq + hq) * a.Nq + qrow] = (m_run * c + log2f(l_lse)) * kLn2;
+      a.lse[(size_t)(b * a.Hq + hq) * a.Nq + qrow] = (m_run * c + log2f(l_tot)) * kLn2;
   }
 }
 
@@ -440,6 +445,10 @@ hipError_t launch_prefill(PrefillParams p, int d, int causal, hipStream_t stream
   constexpr int BM = PrefillShape<128>::BM;
   p.num_qtiles = (p.Nq + BM - 1) / BM;
   p.total_wg = p.num_qtiles * p.Hq * p.B;
+  // A zero scale makes every visible weight 1.  A tiny positive exponent scale gives the
+  // same fp32 weights (2^(tiny) rounds to 1) while keeping -inf * c = -inf for masked
+  // keys, so the kernel needs no separate zero-weight select.
+  if (!(p.c > 0.f)) p.c = 1e-30f;
   // Heads per dispatch group: as many as keep the group's K and V within 4 MiB (one
   // XCD's L2), at least 1, at most the heads one XCD owns.
   {

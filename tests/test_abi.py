@@ -61,6 +61,7 @@ def prefill(lib, q=P, k=P, v=P, o=P, lse=None, B=1, Hq=2, Hkv=1, Nq=4, Nk=4, d=6
     (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
     (dict(d=32), UNSUPPORTED), (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
     (dict(B=65536, Hq=65536, Hkv=1, Nq=128, Nk=128), UNSUPPORTED),
+    (dict(Nq=16, Nk=(1 << 23) + 1, d=128), UNSUPPORTED),
 ])
 def test_prefill_validation(lib, kw, status):
     assert prefill(lib, **kw) == status
