@@ -156,11 +156,6 @@ void prefill_kernel(PrefillParams a) {
   // This wave's 32 query rows.  The two groups interleave 32-row blocks so that both
   // reach the causal diagonal at about the same tile.
   const int wrow0 = m0 + 32 * (2 * (wave & 3) + grp);
-  int wtiles = 0;  // tiles this wave computes (0 when all its rows are padding past Nq)
-  if (wrow0 < a.Nq) {
-    const int wk = CAUSAL ? min(a.Nk, min(wrow0 + 31, a.Nq - 1) + off + 1) : a.Nk;
-    wtiles = (wk + S::BN - 1) / S::BN;
-  }
 
   // --- LDS DMA of one K/V tile (buffer_load ... lds): wave-instruction i of this wave
   // fills 1 KB of the stage; lane l fetches the chunk that belongs at LDS position l of
@@ -244,52 +239,73 @@ void prefill_kernel(PrefillParams a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) pk[i][j] = 0;
 
-  // P.V of tile j (V^T through transposing reads, P^T from registers)
-  auto pv = [&](int j) {
-    const char* st = smem + (j & (S::STAGES - 1)) * S::STAGE;
+  // --- MFMA slot: P.V of tile jpv (V^T through transposing reads, P^T from registers)
+  // then S^T = K Q^T of tile jqk (two 32-key halves).  The operand reads run kLead MFMAs
+  // ahead as one stream across both parts; the first kLead P.V operands are read during
+  // the preceding softmax slot, so the matrix core starts on arrival.
+  constexpr int NPV = 4 * (D / 32);  // P.V MFMAs per tile: 16-key steps x 32-dim blocks
+  constexpr int NQK = 2 * (D / 16);  // Q.K^T MFMAs per tile: 16-dim steps x key halves
+  constexpr int kLead = 6;
+  bf16x8 pre[kLead];
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      const u32x4 pw = {pk[t4 >> 1][4 * (t4 & 1) + 0], pk[t4 >> 1][4 * (t4 & 1) + 1],
-                        pk[t4 >> 1][4 * (t4 & 1) + 2], pk[t4 >> 1][4 * (t4 & 1) + 3]};
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const bf16x4 lo = lds_read_tr(st + voff[db][0] + t4 * 16 * S::ROWB);
-        const bf16x4 hi = lds_read_tr(st + voff[db][1] + t4 * 16 * S::ROWB);
-        oacc[db] = mfma_32x32x16(concat(lo, hi), pb, oacc[db]);
-      }
-    }
-    // keep the transposing reads six MFMAs ahead (enough to cover LDS latency without
-    // running out of registers)
-    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
-#pragma unroll
-    for (int i = 0; i < 4 * (D / 32) - 6; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+  for (int i = 0; i < kLead; ++i) pre[i] = bf16x8{};
+  auto stage = [&](int j) -> const char* { return smem + (j & (S::STAGES - 1)) * S::STAGE; };
+  auto pv_operand = [&](const char* st, int m) -> bf16x8 {
+    const int t4 = m / (D / 32), db = m % (D / 32);
+    return concat(lds_read_tr(st + voff[db][0] + t4 * 16 * S::ROWB),
+                  lds_read_tr(st + voff[db][1] + t4 * 16 * S::ROWB));
   };
-
-  // S^T = K_j Q^T for the two 32-key halves of tile j
-  auto qk = [&](int j) {
-    const char* st = smem + (j & (S::STAGES - 1)) * S::STAGE;
+  auto qk_operand = [&](const char* st, int m) -> bf16x8 {
+    return lds_read_b128(st + koff[m >> 1] + (m & 1) * 32 * S::ROWB);
+  };
+  auto prefetch_pv = [&](int j) {
+    const char* st = stage(j);
+#pragma unroll
+    for (int i = 0; i < kLead; ++i) pre[i] = pv_operand(st, i);
+  };
+  auto mfma_slot = [&](int jpv, int jqk, auto pv_tag, auto qk_tag) {
+    constexpr bool DO_PV = decltype(pv_tag)::value;
+    constexpr bool DO_QK = decltype(qk_tag)::value;
+    constexpr int P0 = DO_PV ? NPV : 0;
+    constexpr int M = P0 + (DO_QK ? NQK : 0);
+    const char* sv = stage(jpv);
+    const char* sk = stage(jqk);
+    auto load = [&](int m) -> bf16x8 {
+      if (m < P0) return pv_operand(sv, m);
+      return qk_operand(sk, m - P0);
+    };
+    bf16x8 ops[M];
+#pragma unroll
+    for (int m = 0; m < kLead; ++m) ops[m] = DO_PV ? pre[m] : load(m);
     f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
-    for (int k = 0; k < D / 16; ++k) {
-      const bf16x8 a0 = lds_read_b128(st + koff[k]);
-      const bf16x8 a1 = lds_read_b128(st + koff[k] + 32 * S::ROWB);
-      s0 = mfma_32x32x16(a0, qop[k], s0);
-      s1 = mfma_32x32x16(a1, qop[k], s1);
+    for (int m = 0; m < M; ++m) {
+      if (m + kLead < M) ops[m + kLead] = load(m + kLead);
+      if (m < P0) {
+        const int t4 = m / (D / 32), db = m % (D / 32);
+        const u32x4 pw = {pk[t4 >> 1][4 * (t4 & 1) + 0], pk[t4 >> 1][4 * (t4 & 1) + 1],
+                          pk[t4 >> 1][4 * (t4 & 1) + 2], pk[t4 >> 1][4 * (t4 & 1) + 3]};
+        oacc[db] = mfma_32x32x16(ops[m], __builtin_bit_cast(bf16x8, pw), oacc[db]);
+      } else {
+        const int q = m - P0;
+        if (q & 1) s1 = mfma_32x32x16(ops[m], qop[q >> 1], s1);
+        else s0 = mfma_32x32x16(ops[m], qop[q >> 1], s0);
+      }
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    // issue order: [the first kLead Q.K^T reads when nothing was prefetched], then per MFMA
+    // m the reads of operand m + kLead (two transposing reads for P.V, one for Q.K^T)
+    if (!DO_PV) __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * (D / 16) - 8; ++i) {
+    for (int m = 0; m < M; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      const int n = m + kLead;
+      if (n < P0) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      else if (n < M) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    sacc[0] = s0;
-    sacc[1] = s1;
+    if (DO_QK) {
+      sacc[0] = s0;
+      sacc[1] = s1;
+    }
   };
 
   // Online softmax of tile j held in sacc; MASK applies the causal diagonal and the ragged
@@ -369,51 +385,65 @@ void prefill_kernel(PrefillParams a) {
   if (ntiles > 1) wait_vmcnt<S::LOADS_PER_TILE>(); else wait_vmcnt<0>();
   block_barrier();
 
-  // Group 0: slot 2j = MFMA (P.V of j-1, Q.K^T of j), slot 2j+1 = softmax of j.
-  // Group 1 runs one slot behind: slot 2j = softmax of j-1, slot 2j+1 = MFMA.
-  // Unmasked tiles j < jm need no per-wave guards (every wave's rows see them whole).
-  std::integral_constant<bool, false> nomask;
-  std::integral_constant<bool, true> withmask;
+  // Group 0: slot 2j = MFMA (P.V of j-1, Q.K^T of j); slot 2j+1 = softmax of j and the
+  // first P.V operands of j.  Group 1 runs one slot behind.  The loops carry no per-wave
+  // conditions: a wave whose rows end before the workgroup's last tile computes those
+  // tiles fully masked (P = 0).  The first and last tiles are peeled.  Both groups pass
+  // 2n+2 barriers.
+  std::integral_constant<bool, false> no;
+  std::integral_constant<bool, true> yes;
+  const int n = ntiles;
+  const int j1 = max(1, min(jm, n));  // softmax of tiles [1, j1) needs no mask
   if (grp == 0) {
-    int j = 0;
-    for (; j < jm; ++j) {
+    slot_begin(0);
+    mfma_slot(0, 0, no, yes);
+    slot_end(0);
+    slot_begin(1);
+    prefetch_pv(0);
+    softmax(0, yes);
+    slot_end(1);
+    auto iter = [&](int j, auto mask_tag) {
       slot_begin(2 * j);
-      if (j >= 1) pv(j - 1);
-      qk(j);
+      mfma_slot(j - 1, j, yes, yes);
       slot_end(2 * j);
       slot_begin(2 * j + 1);
-      softmax(j, nomask);
+      prefetch_pv(j);
+      softmax(j, mask_tag);
       slot_end(2 * j + 1);
-    }
-    for (; j <= ntiles; ++j) {
-      slot_begin(2 * j);
-      if (j >= 1 && j - 1 < wtiles) pv(j - 1);
-      if (j < wtiles) qk(j);
-      slot_end(2 * j);
-      slot_begin(2 * j + 1);
-      if (j < wtiles) softmax(j, withmask);
-      slot_end(2 * j + 1);
-    }
+    };
+    for (int j = 1; j < j1; ++j) iter(j, no);
+    for (int j = j1; j < n; ++j) iter(j, yes);
+    slot_begin(2 * n);
+    mfma_slot(n - 1, 0, yes, no);
+    slot_end(2 * n);
+    slot_begin(2 * n + 1);
+    slot_end(2 * n + 1);
   } else {
-    int j = 0;
-    for (; j < jm; ++j) {
+    slot_begin(0);
+    slot_end(0);
+    slot_begin(1);
+    mfma_slot(0, 0, no, yes);
+    slot_end(1);
+    // iteration j runs the softmax of tile j-1: masked for tile 0 and tiles >= j1
+    auto iter = [&](int j, auto mask_tag) {
       slot_begin(2 * j);
-      if (j >= 1) softmax(j - 1, nomask);
+      prefetch_pv(j - 1);
+      softmax(j - 1, mask_tag);
       slot_end(2 * j);
       slot_begin(2 * j + 1);
-      if (j >= 1) pv(j - 1);
-      qk(j);
+      mfma_slot(j - 1, j, yes, yes);
       slot_end(2 * j + 1);
-    }
-    for (; j <= ntiles; ++j) {
-      slot_begin(2 * j);
-      if (j >= 1 && j - 1 < wtiles) softmax(j - 1, withmask);
-      slot_end(2 * j);
-      slot_begin(2 * j + 1);
-      if (j >= 1 && j - 1 < wtiles) pv(j - 1);
-      if (j < wtiles) qk(j);
-      slot_end(2 * j + 1);
-    }
+    };
+    if (n > 1) iter(1, yes);
+    for (int j = 2; j < min(j1 + 1, n); ++j) iter(j, no);
+    for (int j = max(j1 + 1, 2); j < n; ++j) iter(j, yes);
+    slot_begin(2 * n);
+    prefetch_pv(n - 1);
+    softmax(n - 1, yes);
+    slot_end(2 * n);
+    slot_begin(2 * n + 1);
+    mfma_slot(n - 1, 0, yes, no);
+    slot_end(2 * n + 1);
   }
 
   // --- epilogue: O = acc / l -> bf16; LSE = m*scale + ln l
