@@ -91,55 +91,59 @@ void decode_split_kernel(DecodeParams a) {
     }
   }
 
-  const size_t kv_stride_tok = (size_t)D;
   const uint16_t* kbase_c = a.kc + ((size_t)b * a.Hkv + kvh) * a.max_seqlen * D;
   const uint16_t* vbase_c = a.vc + ((size_t)b * a.Hkv + kvh) * a.max_seqlen * D;
   const int32_t* table = PAGED ? a.block_table + (size_t)b * a.max_blocks : nullptr;
 
   // Page ids of a 32-key block starting at tb (two 16-token pages, wave-uniform, so
-  // scalar loads).  They are fetched one block ahead of the K/V loads that use them.
+  // scalar loads).  They are fetched well ahead of the K/V loads that use them.
   auto block_pages = [&](int tb, int& p0, int& p1) {
     if (PAGED && tb < t1) {
       p0 = table[tb >> 4];
       p1 = tb + 16 < t1 ? table[(tb >> 4) + 1] : p0;
     }
   };
-  // one 32-key block: lane owns CPL chunks of K and of V (row = idx / (D/8))
-  u32x4 kr[S::CPL], vr[S::CPL];
-  auto load_block = [&](int tb, int p0, int p1) {
+  // One 32-key block = two 16-token groups (a page of the paged cache, 16 consecutive
+  // rows of the contiguous one).  Each group is read through a buffer descriptor whose
+  // range ends at the chunk's last key, so rows past it read as zeros.  Lane l owns the
+  // 16-byte chunks l + 64*i of the block: offset 16*l + 1024*(i mod CPL/2) within group
+  // i / (CPL/2).
+  constexpr int HALF = S::CPL / 2;
+  auto load_block = [&](u32x4 (&kr)[S::CPL], u32x4 (&vr)[S::CPL], int tb, int p0, int p1) {
 #pragma unroll
-    for (int i = 0; i < S::CPL; ++i) {
-      const int cidx = lane + 64 * i;
-      const int row = cidx / (D / 8), ch = cidx % (D / 8);
-      const int tok = tb + row;
-      if (tok < t1) {
-        size_t off;
-        if (PAGED) {
-          const int page = (i * 64) / (D / 8) < 16 ? p0 : p1;  // row < 16 <=> first page
-          off = (((size_t)page * a.Hkv + kvh) * 16 + (tok & 15)) * D + ch * 8;
-          kr[i] = *(const u32x4*)(a.kc + off);
-          vr[i] = *(const u32x4*)(a.vc + off);
-        } else {
-          off = (size_t)tok * kv_stride_tok + ch * 8;
-          kr[i] = *(const u32x4*)(kbase_c + off);
-          vr[i] = *(const u32x4*)(vbase_c + off);
-        }
+    for (int h = 0; h < 2; ++h) {
+      const int tg = tb + 16 * h;
+      const int rows = max(0, min(16, t1 - tg));
+      const uint16_t* kg;
+      const uint16_t* vg;
+      if (PAGED) {
+        const size_t off = ((size_t)(h ? p1 : p0) * a.Hkv + kvh) * 16 * D;
+        kg = a.kc + off;
+        vg = a.vc + off;
       } else {
-        kr[i] = u32x4{0, 0, 0, 0};
-        vr[i] = u32x4{0, 0, 0, 0};
+        kg = kbase_c + (size_t)tg * D;
+        vg = vbase_c + (size_t)tg * D;
+      }
+      const int nbytes = rows * D * 2;
+#pragma unroll
+      for (int i = 0; i < HALF; ++i) {
+        kr[h * HALF + i] = buffer_load16(kg, nbytes, lane * 16 + 1024 * i);
+        vr[h * HALF + i] = buffer_load16(vg, nbytes, lane * 16 + 1024 * i);
       }
     }
   };
 
   char* kls = smem + wave * S::WAVE_LDS;
   char* vls = kls + S::BLK * S::KSTR;
-  auto store_block = [&]() {
+  // chunk l + 64*i is row l/(D/8) + i*RPI, column chunk l%(D/8)
+  constexpr int RPI = 64 / (D / 8);
+  char* kst = kls + (lane / (D / 8)) * S::KSTR + (lane % (D / 8)) * 16;
+  char* vst = vls + (lane / (D / 8)) * S::VSTR + (lane % (D / 8)) * 16;
+  auto store_block = [&](const u32x4 (&kr)[S::CPL], const u32x4 (&vr)[S::CPL]) {
 #pragma unroll
     for (int i = 0; i < S::CPL; ++i) {
-      const int cidx = lane + 64 * i;
-      const int row = cidx / (D / 8), ch = cidx % (D / 8);
-      *(u32x4*)(kls + row * S::KSTR + ch * 16) = kr[i];
-      *(u32x4*)(vls + row * S::VSTR + ch * 16) = vr[i];
+      *(u32x4*)(kst + i * RPI * S::KSTR) = kr[i];
+      *(u32x4*)(vst + i * RPI * S::VSTR) = vr[i];
     }
   };
 
@@ -156,22 +160,13 @@ void decode_split_kernel(DecodeParams a) {
   const char* vp_l = vls + (4 * g4 + (i16 >> 2)) * S::VSTR + 4 * (i16 & 3) * 2;
 
   const int nblk = (t1 - t0 + S::BLK - 1) / S::BLK;
-  int bi = wave;
-  int pg0 = 0, pg1 = 0, npg0 = 0, npg1 = 0;
-  block_pages(t0 + S::BLK * bi, pg0, pg1);
-  block_pages(t0 + S::BLK * (bi + kDecodeWaves), npg0, npg1);
-  if (bi < nblk) load_block(t0 + S::BLK * bi, pg0, pg1);
-  for (; bi < nblk; bi += kDecodeWaves) {
-    const int tb = t0 + S::BLK * bi;
-    store_block();
+  auto wave_sync = [&]() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (bi + kDecodeWaves < nblk) {
-      load_block(tb + kDecodeWaves * S::BLK, npg0, npg1);
-      block_pages(tb + 2 * kDecodeWaves * S::BLK, npg0, npg1);
-    }
-
+  };
+  // S^T, online softmax and O^T += V^T P^T for the block staged in this wave's LDS
+  auto compute = [&](int tb) {
     // S^T = K Q^T: two 16-key halves
     f32x4 s[2];
 #pragma unroll
@@ -232,9 +227,36 @@ void decode_split_kernel(DecodeParams a) {
       const bf16x4 hi = lds_read_tr(vp_l + db * 32 + 16 * S::VSTR);
       oacc[db] = mfma_16x16x32(concat(lo, hi), pb, oacc[db]);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // The wave takes blocks wave, wave + W, wave + 2W, ... with two blocks in flight: while
+  // one is consumed, the next two are loading into registers (sets A and B alternate).
+  constexpr int W = kDecodeWaves;
+  auto tbk = [&](int i) { return t0 + S::BLK * i; };
+  u32x4 kA[S::CPL], vA[S::CPL], kB[S::CPL], vB[S::CPL];
+  int bi = wave;
+  int pa0 = 0, pa1 = 0, pb0 = 0, pb1 = 0, pn0 = 0, pn1 = 0;
+  block_pages(tbk(bi), pa0, pa1);
+  block_pages(tbk(bi + W), pb0, pb1);
+  if (bi < nblk) load_block(kA, vA, tbk(bi), pa0, pa1);
+  if (bi + W < nblk) load_block(kB, vB, tbk(bi + W), pb0, pb1);
+  block_pages(tbk(bi + 2 * W), pn0, pn1);  // pages of the next block to load
+  while (bi < nblk) {
+    store_block(kA, vA);
+    wave_sync();
+    if (bi + 2 * W < nblk) load_block(kA, vA, tbk(bi + 2 * W), pn0, pn1);
+    block_pages(tbk(bi + 3 * W), pn0, pn1);
+    compute(tbk(bi));
+    wave_sync();
+    bi += W;
+    if (bi >= nblk) break;
+    store_block(kB, vB);
+    wave_sync();
+    if (bi + 2 * W < nblk) load_block(kB, vB, tbk(bi + 2 * W), pn0, pn1);
+    block_pages(tbk(bi + 3 * W), pn0, pn1);
+    compute(tbk(bi));
+    wave_sync();
+    bi += W;
   }
 
   // ---- merge the four waves' states (LDS reused as fp32 scratch)
@@ -286,41 +308,56 @@ void decode_split_kernel(DecodeParams a) {
   }
 }
 
-// One wave per (batch, query head) row: combine the row's non-empty chunks.
+// One workgroup per (batch, query head) row combines the row's non-empty chunks.  Thread
+// (sub, dv) of the kMergeThreads sums chunks sub, sub + kMergeSub, ... for head-dim dv, so
+// a thread issues few, independent loads; the row's chunk LSEs are staged in LDS first
+// and the kMergeSub partial sums are combined in LDS.
+constexpr int kMergeThreads = 512;
+
 template <int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams a) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.B * a.Hq) return;
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParams a) {
+  constexpr int kMergeSub = kMergeThreads / D;
+  __shared__ float s_lse[kDecodeMaxSplits];
+  __shared__ float s_acc[kMergeSub][D];
+  __shared__ float s_w[kMergeSub];
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
   const int b = row / a.Hq;
   const int len = min(a.seqlens[b], a.max_seqlen);
   const int n = min(a.num_splits, (len + a.chunk - 1) / a.chunk);
   uint16_t* orow = a.o + (size_t)row * D;
   if (n <= 0) {
-    for (int dv = lane; dv < D; dv += 64) orow[dv] = 0;
-    if (lane == 0 && a.lse) a.lse[row] = -INFINITY;
+    if (tid < D) orow[tid] = 0;
+    if (tid == 0 && a.lse) a.lse[row] = -INFINITY;
     return;
   }
   const float* lrow = a.ws_lse + (size_t)row * a.num_splits;
   const float* prow = a.ws_o + (size_t)row * a.num_splits * D;
+  for (int s = tid; s < n; s += kMergeThreads) s_lse[s] = lrow[s];
+  __syncthreads();
   float M = -INFINITY;
-  for (int s = lane; s < n; s += 64) M = fmaxf(M, lrow[s]);
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, wave_xor(M, m));
-  float W = 0.f;
-  float acc[D / 64];
-#pragma unroll
-  for (int i = 0; i < D / 64; ++i) acc[i] = 0.f;
-  for (int s = 0; s < n; ++s) {
-    const float w = fast_exp2((lrow[s] - M) * kLog2e);
+  for (int s = 0; s < n; ++s) M = fmaxf(M, s_lse[s]);
+  const int sub = tid / D, dv = tid % D;
+  float acc = 0.f, W = 0.f;
+#pragma unroll 8
+  for (int s = sub; s < n; s += kMergeSub) {
+    const float w = fast_exp2((s_lse[s] - M) * kLog2e);
     W += w;
-#pragma unroll
-    for (int i = 0; i < D / 64; ++i) acc[i] += w * prow[(size_t)s * D + lane + 64 * i];
+    acc += w * prow[(size_t)s * D + dv];
   }
+  s_acc[sub][dv] = acc;
+  if (dv == 0) s_w[sub] = W;
+  __syncthreads();
+  if (tid < D) {
+    float t = 0.f, wt = 0.f;
 #pragma unroll
-  for (int i = 0; i < D / 64; ++i)
-    orow[lane + 64 * i] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i] / W));
-  if (lane == 0 && a.lse) a.lse[row] = M + logf(W);
+    for (int k = 0; k < kMergeSub; ++k) {
+      t += s_acc[k][tid];
+      wt += s_w[k];
+    }
+    orow[tid] = __builtin_bit_cast(uint16_t, (__bf16)(t / wt));
+    if (tid == 0 && a.lse) a.lse[row] = M + logf(wt);
+  }
 }
 
 template <int D>
@@ -333,7 +370,7 @@ static hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.num_splits == 1) return e;
   const int rows = p.B * p.Hq;
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((rows + 3) / 4), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(rows), dim3(kMergeThreads), 0, stream, p);
   return hipGetLastError();
 }
 

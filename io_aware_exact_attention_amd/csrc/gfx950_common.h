@@ -76,6 +76,14 @@ __device__ __forceinline__ void lds_dma16(const void* base, int nbytes, uint32_t
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
 }
 
+// 16-byte buffer load into registers: reads base + off (bytes) when off < nbytes, else
+// returns zeros.
+__device__ __forceinline__ u32x4 buffer_load16(const void* base, int nbytes, int off) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, kBufferFlags);
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 __device__ __forceinline__ bf16x8 concat(bf16x4 lo, bf16x4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }

@@ -43,6 +43,7 @@ constexpr int kDecodeHeadsPerGroup = 16;
 // Keys one decode wave consumes per step; chunks are multiples of it.
 constexpr int kDecodeBlock = 32;
 constexpr int kDecodeWaves = 4;
+constexpr int kDecodeMaxSplits = 1024;  // chunks per sequence, at most
 
 hipError_t launch_prefill(PrefillParams p, int d, int causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t stream);

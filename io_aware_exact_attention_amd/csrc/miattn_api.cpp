@@ -24,9 +24,9 @@ struct Plan {
   int chunk;
 };
 
-constexpr int kAutoTargetWorkgroups = 4096;  // ~16 per compute unit on 256 CUs
-constexpr int kMinChunk = 256;               // keys per chunk in the automatic plan
-constexpr int kMaxSplits = 1024;
+constexpr int kTargetChunk = 1024;      // keys per chunk in the automatic plan
+constexpr int kMinWorkgroups = 2048;    // ~8 per compute unit on 256 CUs
+constexpr int kMinChunk = 256;          // smallest chunk the plan uses to reach that
 
 bool decode_sizes_ok(int B, int Hq, int Hkv, int d, int max_seqlen) {
   if (B < 1 || Hq < 1 || Hkv < 1 || max_seqlen < 1) return false;
@@ -40,13 +40,18 @@ Plan plan_decode(int B, int Hq, int Hkv, int max_seqlen, int num_splits) {
   const int ngroups = (G + miattn::kDecodeHeadsPerGroup - 1) / miattn::kDecodeHeadsPerGroup;
   int want = num_splits;
   if (want <= 0) {
+    // chunks of ~kTargetChunk keys; shorter ones (down to kMinChunk) only when the grid
+    // would otherwise have fewer than kMinWorkgroups workgroups
     const long base = (long)B * Hkv * ngroups;
-    long s = (kAutoTargetWorkgroups + base - 1) / base;
-    const long cap = (max_seqlen + kMinChunk - 1) / kMinChunk;
-    if (s > cap) s = cap;
+    long s = ((long)max_seqlen + kTargetChunk - 1) / kTargetChunk;
+    if (base * s < kMinWorkgroups) {
+      const long cap = ((long)max_seqlen + kMinChunk - 1) / kMinChunk;
+      s = (kMinWorkgroups + base - 1) / base;
+      if (s > cap) s = cap;
+    }
     want = (int)(s < 1 ? 1 : s);
   }
-  if (want > kMaxSplits) want = kMaxSplits;
+  if (want > miattn::kDecodeMaxSplits) want = miattn::kDecodeMaxSplits;
   const int blk = miattn::kDecodeBlock;
   long chunk = ((long)max_seqlen + want - 1) / want;
   chunk = (chunk + blk - 1) / blk * blk;
@@ -140,7 +145,8 @@ int attn_fwd_decode(const void* q, const void* kcache, const void* vcache,
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   const int G = Hq / Hkv;
   const int ngroups = (G + miattn::kDecodeHeadsPerGroup - 1) / miattn::kDecodeHeadsPerGroup;
-  if (B > 65535 || (long)Hkv * ngroups > 65535) return ATTN_ERR_UNSUPPORTED;
+  if (B > 65535 || (long)Hkv * ngroups > 65535 || (long)B * Hq > 0x7fffffffL)
+    return ATTN_ERR_UNSUPPORTED;
 
   const Plan pl = plan_decode(B, Hq, Hkv, max_seqlen, num_splits);
   const size_t need = workspace_for(B, Hq, d, pl);
