@@ -99,6 +99,7 @@ class DecodeCfg:
     page_size: int = 16
     fixed_len: int = 0            # every sequence this long (contiguous workload)
     len_range: tuple = (0, 0)     # inclusive uniform range of lengths (paged workload)
+    chunk: int = 0                # chunked prefill: new tokens (queries) per sequence
 
     @property
     def scale(self) -> float:
@@ -123,6 +124,11 @@ CONFIGS = {
     # Paged GQA decode, 16-token pages, lengths uniform in [1024, 131072].
     "paged_gqa_decode": DecodeCfg("paged_gqa_decode", B=8, Hq=32, Hkv=8, d=128, seed=5,
                                   paged=True, page_size=16, len_range=(1024, 131072)),
+    # Chunked prefill against a paged cache: 512 new tokens per sequence appended to
+    # contexts (which already hold them) of 2048..16384 tokens, Llama-2-style GQA heads.
+    "chunked_prefill_paged": DecodeCfg("chunked_prefill_paged", B=8, Hq=32, Hkv=8, d=128,
+                                       seed=6, paged=True, page_size=16,
+                                       len_range=(2048, 16384), chunk=512),
 }
 
 
@@ -279,3 +285,19 @@ def decode_bytes(cfg: DecodeCfg, lengths: np.ndarray) -> int:
 
 def decode_flops(cfg: DecodeCfg, lengths: np.ndarray) -> int:
     return 4 * cfg.d * cfg.Hq * int(np.sum(lengths, dtype=np.int64))
+
+
+def chunk_q(cfg: DecodeCfg) -> np.ndarray:
+    """Chunked-prefill queries [B, Hq, chunk, d] bf16 bits."""
+    q = np.empty((cfg.B, cfg.Hq, cfg.chunk, cfg.d), np.uint16)
+    for b in range(cfg.B):
+        for h in range(cfg.Hq):
+            q[b, h] = normal_bf16(cfg.seed, T_Q, b, h, (cfg.chunk, cfg.d))
+    return q
+
+
+def chunk_prefill_flops(cfg: DecodeCfg, lengths: np.ndarray, causal: bool = True) -> int:
+    """Algorithmic FLOPs of a chunked prefill: 4*d per visible pair, the chunk's queries
+    being the last ``chunk`` positions of each sequence."""
+    pairs = sum(visible_pairs(cfg.chunk, int(n), causal) for n in lengths)
+    return 4 * cfg.d * cfg.Hq * pairs

@@ -77,6 +77,37 @@ int attn_fwd_prefill(const void* q, const void* k, const void* v, void* o, float
                      hipStream_t stream);
 
 /*
+ * Chunked (append) prefill against a paged KV cache: the Nq newest tokens of every
+ * sequence attend to that sequence's whole cached context, which already holds their
+ * own keys and values as its last Nq tokens.  This is the prefill step of chunked
+ * prefill / continuous batching (page "Transformers optimization overview", section on
+ * continuous batching) over a paged cache (page "메모리 장벽을 넘어" (tiptinker),
+ * section "2. FlashInfer", PagedAttention integration).  Query i of sequence b sits at
+ * position kv_lens[b] - Nq + i; causal != 0 lets it see keys 0 .. that position.
+ *
+ *   q      [B, Hq, Nq, d] bf16, 16-byte aligned
+ *   kcache, vcache [num_pages, Hkv, page_size, d] bf16, 16-byte aligned, page_size == 16
+ *   block_table [B, max_blocks_per_seq] int32, DEVICE memory: token t of sequence b is
+ *          slot t % 16 of page block_table[b, t / 16].  Entries for tokens < kv_lens[b]
+ *          must lie in [0, num_pages); other entries are never read.
+ *   kv_lens [B] int32, DEVICE memory, each in [Nq, max_kv_len] (not read on the host)
+ *   o      [B, Hq, Nq, d] bf16 (written), 16-byte aligned
+ *   lse    [B, Hq, Nq] fp32 (written) or NULL
+ *   Needs max_blocks_per_seq >= ceil(max_kv_len / 16).  Cache rows at or past
+ *   kv_lens[b] are never read.
+ *
+ * Errors: INVALID_ARGUMENT for a null required pointer, misalignment, any size < 1,
+ * Hq % Hkv != 0, Nq > max_kv_len, max_blocks_per_seq too small, non-finite scale;
+ * UNSUPPORTED for d not in {64,128}, page_size != 16 or a grid beyond 2^31-1
+ * workgroups; HIP if the launch fails.
+ */
+int attn_fwd_prefill_paged(const void* q, const void* kcache, const void* vcache,
+                           const int32_t* block_table, const int32_t* kv_lens, void* o,
+                           float* lse, int B, int Hq, int Hkv, int Nq, int d, int max_kv_len,
+                           int page_size, int max_blocks_per_seq, int num_pages, int causal,
+                           float scale, hipStream_t stream);
+
+/*
  * Decode: one query per sequence against the sequence's KV cache, split along the
  * KV length into chunks whose partial results are merged by log-sum-exp.
  *

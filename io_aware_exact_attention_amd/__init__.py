@@ -52,6 +52,8 @@ def load_library():
     lib.attn_fwd_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
                                      vp]
     lib.attn_fwd_prefill.restype = i32
+    lib.attn_fwd_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp] + [i32] * 10 + [f32, vp]
+    lib.attn_fwd_prefill_paged.restype = i32
     lib.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                     i32, f32, i32, vp, ctypes.c_size_t, vp]
     lib.attn_fwd_decode.restype = i32
@@ -125,6 +127,54 @@ def prefill(q, k, v, causal: bool = True, scale: float | None = None):
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     attn_fwd_prefill(q, k, v, o, lse, causal, scale)
+    return o, lse
+
+
+def attn_fwd_prefill_paged(q, kcache, vcache, block_table, kv_lens, o, lse, max_kv_len: int,
+                           causal: bool, scale: float, page_size: int = 16,
+                           num_pages: int | None = None, stream=None) -> None:
+    """Chunked prefill against a paged cache.  q/o [B,Hq,Nq,d] bf16; caches
+    [num_pages,Hkv,16,d] bf16; block_table int32 [B, max_blocks] and kv_lens int32 [B]
+    (device), each kv_lens[b] in [Nq, max_kv_len]; lse [B,Hq,Nq] fp32 or None."""
+    lib = load_library()
+    _check(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    _check(kcache, "kcache", torch.bfloat16, 4, dev)
+    _check(vcache, "vcache", torch.bfloat16, 4, dev)
+    _check(o, "o", torch.bfloat16, 4, dev)
+    _check(block_table, "block_table", torch.int32, 2, dev)
+    _check(kv_lens, "kv_lens", torch.int32, 1, dev)
+    B, Hq, Nq, d = q.shape
+    if tuple(vcache.shape) != tuple(kcache.shape) or tuple(o.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q/o or kcache/vcache")
+    if kcache.shape[2] != page_size or kcache.shape[3] != d:
+        raise ValueError("paged caches must be [num_pages, Hkv, page_size, d]")
+    if block_table.shape[0] != B or kv_lens.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks] and kv_lens [B]")
+    if lse is not None:
+        _check(lse, "lse", torch.float32, 3, dev)
+        if tuple(lse.shape) != (B, Hq, Nq):
+            raise ValueError("lse must be [B, Hq, Nq]")
+    if num_pages is None:
+        num_pages = kcache.shape[0]
+    st = lib.attn_fwd_prefill_paged(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(block_table),
+                                    _ptr(kv_lens), _ptr(o), _ptr(lse), B, Hq, kcache.shape[1], Nq,
+                                    d, int(max_kv_len), int(page_size), int(block_table.shape[1]),
+                                    int(num_pages), 1 if causal else 0, float(scale),
+                                    _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_prefill_paged")
+
+
+def prefill_paged(q, kcache, vcache, block_table, kv_lens, max_kv_len: int, causal: bool = True,
+                  scale: float | None = None):
+    """Allocate O and LSE and run attn_fwd_prefill_paged.  scale None means 1/sqrt(d)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    attn_fwd_prefill_paged(q, kcache, vcache, block_table, kv_lens, o, lse, max_kv_len, causal,
+                           scale)
     return o, lse
 
 

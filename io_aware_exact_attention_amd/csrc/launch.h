@@ -18,6 +18,12 @@ struct PrefillParams {
   int num_qtiles; // filled by launch_prefill
   int total_wg;   // filled by launch_prefill
   int head_group; // filled by launch_prefill: heads whose query tiles are interleaved
+  // Paged K/V (block_table non-null): k, v are [pages, Hkv, 16, d] pools, sequence b has
+  // kv_lens[b] keys (its last Nq are the queries' own positions) in pages
+  // block_table[b, 0 .. max_blocks); Nk is then the largest kv_lens value.
+  const int32_t* block_table;
+  const int32_t* kv_lens;
+  int max_blocks;
 };
 
 struct DecodeParams {

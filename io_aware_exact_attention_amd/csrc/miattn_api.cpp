@@ -113,6 +113,42 @@ int attn_fwd_prefill(const void* q, const void* k, const void* v, void* o, float
                                                                              : ATTN_ERR_HIP;
 }
 
+int attn_fwd_prefill_paged(const void* q, const void* kcache, const void* vcache,
+                           const int32_t* block_table, const int32_t* kv_lens, void* o,
+                           float* lse, int B, int Hq, int Hkv, int Nq, int d, int max_kv_len,
+                           int page_size, int max_blocks_per_seq, int num_pages, int causal,
+                           float scale, hipStream_t stream) {
+  if (!q || !kcache || !vcache || !block_table || !kv_lens || !o) return ATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(kcache, 16) || !aligned(vcache, 16) || !aligned(o, 16) ||
+      !aligned(block_table, 4) || !aligned(kv_lens, 4))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (lse && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || d < 1 || max_kv_len < 1 || num_pages < 1)
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (Hq % Hkv || Nq > max_kv_len || !std::isfinite(scale)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (page_size != 16) return ATTN_ERR_UNSUPPORTED;
+  if (max_blocks_per_seq < (max_kv_len + 15) / 16) return ATTN_ERR_INVALID_ARGUMENT;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  const long qtiles = (Nq + 127) / 128;
+  if (qtiles * (long)Hq * B > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
+
+  miattn::PrefillParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(kcache);
+  p.v = static_cast<const uint16_t*>(vcache);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = max_kv_len;
+  p.c = std::fabs(scale) * 1.4426950408889634f;
+  p.negate_q = scale < 0.f;
+  p.block_table = block_table;
+  p.kv_lens = kv_lens;
+  p.max_blocks = max_blocks_per_seq;
+  (void)hipGetLastError();
+  return miattn::launch_prefill(p, d, causal ? 1 : 0, stream) == hipSuccess ? ATTN_OK
+                                                                             : ATTN_ERR_HIP;
+}
+
 int attn_decode_num_splits(int B, int Hq, int Hkv, int d, int max_seqlen, int num_splits) {
   if (!decode_sizes_ok(B, Hq, Hkv, d, max_seqlen) || num_splits < 0) return 0;
   return plan_decode(B, Hq, Hkv, max_seqlen, num_splits).splits;

@@ -123,7 +123,7 @@ __device__ __forceinline__ WorkItem prefill_work_item(int p, int BH, int nq, int
   return w;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillParams a) {
   using S = PrefillShape<D>;
@@ -142,15 +142,18 @@ void prefill_kernel(PrefillParams a) {
   const int qtile = CAUSAL ? (a.num_qtiles - 1 - wi.qrank) : wi.qrank;
   const int kvh = hq / (a.Hq / a.Hkv);
   const int m0 = qtile * S::BM;
-  const int off = a.Nk - a.Nq;  // bottom-right causal alignment
+  // Keys of this sequence: Nk, or (paged cache) its own context length, which includes
+  // the Nq new queries as its last tokens.
+  const int nk = PAGED ? a.kv_lens[b] : a.Nk;
+  const int off = nk - a.Nq;  // bottom-right causal alignment
 
   const uint16_t* __restrict__ Qh = a.q + (size_t)(b * a.Hq + hq) * a.Nq * D;
-  const uint16_t* __restrict__ Kh = a.k + (size_t)(b * a.Hkv + kvh) * a.Nk * D;
-  const uint16_t* __restrict__ Vh = a.v + (size_t)(b * a.Hkv + kvh) * a.Nk * D;
+  const uint16_t* __restrict__ Kh = PAGED ? a.k : a.k + (size_t)(b * a.Hkv + kvh) * a.Nk * D;
+  const uint16_t* __restrict__ Vh = PAGED ? a.v : a.v + (size_t)(b * a.Hkv + kvh) * a.Nk * D;
 
   // keys the workgroup needs: everything, or up to the diagonal of its last query
-  int kend = a.Nk;
-  if (CAUSAL) kend = min(a.Nk, min(m0 + S::BM, a.Nq) - 1 + off + 1);
+  int kend = nk;
+  if (CAUSAL) kend = min(nk, min(m0 + S::BM, a.Nq) - 1 + off + 1);
   const int ntiles = (kend + S::BN - 1) / S::BN;
 
   // This wave's 32 query rows.  The two groups interleave 32-row blocks so that both
@@ -169,17 +172,51 @@ void prefill_kernel(PrefillParams a) {
     const int R = p / S::CPR;
     dma_off[i] = R * S::ROWB + (((p % S::CPR) ^ chunk_swizzle<D>(R)) << 4);
   }
+  // Paged cache [pages, Hkv, 16, D]: each 1 KB DMA block (RPB rows) lies inside one
+  // 16-token page and gets its own descriptor.  The page ids of a tile's blocks are read
+  // with scalar loads one tile ahead of its DMA.
+  constexpr int RPB = 1024 / S::ROWB;
+  // The table is read through the constant address space: it does not change during the
+  // kernel, and wave-uniform loads from there are scalar loads.
+  typedef __attribute__((address_space(4))) const int32_t const_i32;
+  const_i32* tbl = (const_i32*)(PAGED ? a.block_table + (size_t)b * a.max_blocks : nullptr);
+  int pg_next[S::DMA];
+  auto fetch_pages = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < S::DMA; ++i) {
+      const int tok0 = j * S::BN + (i * S::kWaves + wave) * RPB;
+      pg_next[i] = tok0 < nk ? tbl[tok0 >> 4] : 0;
+    }
+  };
+  if (PAGED) fetch_pages(0);
   auto issue_tile = [&](int j) {
     const int n0 = j * S::BN;
     char* st = smem + (j & (S::STAGES - 1)) * S::STAGE;
-    const int nbytes = (a.Nk - n0) * (D * 2);
-    const uint16_t* kt = Kh + (size_t)n0 * D;
-    const uint16_t* vt = Vh + (size_t)n0 * D;
+    if (PAGED) {
+      int pg[S::DMA];
 #pragma unroll
-    for (int i = 0; i < S::DMA; ++i) {
-      const int blk = i * S::kWaves + wave;
-      lds_dma16(kt, nbytes, dma_off[i], (lds_void*)(st + blk * 1024));
-      lds_dma16(vt, nbytes, dma_off[i], (lds_void*)(st + S::TILE + blk * 1024));
+      for (int i = 0; i < S::DMA; ++i) pg[i] = pg_next[i];
+      fetch_pages(j + 1);
+#pragma unroll
+      for (int i = 0; i < S::DMA; ++i) {
+        const int blk = i * S::kWaves + wave;
+        const int tok0 = n0 + blk * RPB;
+        const int rows = max(0, min(RPB, nk - tok0));
+        const size_t off = ((size_t)pg[i] * a.Hkv + kvh) * 16 * D + (size_t)(tok0 & 15) * D;
+        const uint32_t lo = dma_off[i] - blk * 1024;  // offset within the block
+        lds_dma16(Kh + off, rows * S::ROWB, lo, (lds_void*)(st + blk * 1024));
+        lds_dma16(Vh + off, rows * S::ROWB, lo, (lds_void*)(st + S::TILE + blk * 1024));
+      }
+    } else {
+      const int nbytes = (nk - n0) * (D * 2);
+      const uint16_t* kt = Kh + (size_t)n0 * D;
+      const uint16_t* vt = Vh + (size_t)n0 * D;
+#pragma unroll
+      for (int i = 0; i < S::DMA; ++i) {
+        const int blk = i * S::kWaves + wave;
+        lds_dma16(kt, nbytes, dma_off[i], (lds_void*)(st + blk * 1024));
+        lds_dma16(vt, nbytes, dma_off[i], (lds_void*)(st + S::TILE + blk * 1024));
+      }
     }
   };
 
@@ -315,7 +352,7 @@ void prefill_kernel(PrefillParams a) {
   // far behind the scores) or could not be formed at all.  On the first tile m_run is -inf,
   // so every weight is +inf or NaN and that path runs.  Otherwise the weights stay at most
   // 2^kRedoLog2, far inside the fp32 and bf16 range, and the result is the same softmax.
-  const int lim = CAUSAL ? min(a.Nk - 1, qrow + off) : a.Nk - 1;  // last visible key
+  const int lim = CAUSAL ? min(nk - 1, qrow + off) : nk - 1;  // last visible key
   auto softmax = [&](int j, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     if (MASK) {
@@ -377,7 +414,7 @@ void prefill_kernel(PrefillParams a) {
 
   // First tile that needs masking for some row of the workgroup: the causal diagonal of
   // its first query row, or the ragged end of the keys.
-  int jm = a.Nk / S::BN;
+  int jm = nk / S::BN;
   if (CAUSAL) jm = min(jm, (m0 + off + 1) / S::BN);
   jm = min(jm, ntiles);
 
@@ -467,7 +504,10 @@ void prefill_kernel(PrefillParams a) {
 
 template <int D, bool CAUSAL>
 static hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_kernel<D, CAUSAL>), dim3(p.total_wg), dim3(512), 0, stream, p);
+  if (p.block_table)
+    hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, true>), dim3(p.total_wg), dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, false>), dim3(p.total_wg), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -159,6 +159,40 @@ def attention_decode(q: np.ndarray, kcache: np.ndarray, vcache: np.ndarray,
     return o, lse
 
 
+def attention_prefill_paged(q: np.ndarray, kpool: np.ndarray, vpool: np.ndarray,
+                            block_table: np.ndarray, kv_lens: np.ndarray, scale: float,
+                            causal: bool, page_size: int = 16, row_block: int = 1024):
+    """Chunked (append) prefill against a paged cache: the Nq queries of sequence b are its
+    last Nq tokens and attend to its first kv_lens[b] cached keys (chunked prefill in the
+    continuous-batching section of the page "Transformers optimization overview"; the
+    paged cache of the page "메모리 장벽을 넘어" (tiptinker), section "2. FlashInfer").
+
+    q [B,Hq,Nq,d]; pools [num_pages,Hkv,page_size,d]; block_table [B, max_blocks];
+    kv_lens [B] with Nq <= kv_lens[b].  Causal alignment is bottom-right, so query i sees
+    keys 0 .. kv_lens[b] - Nq + i.  Returns O [B,Hq,Nq,d], LSE [B,Hq,Nq] (float64).
+    """
+    B, Hq, Nq, d = q.shape
+    Hkv = kpool.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    o = np.empty((B, Hq, Nq, d))
+    lse = np.empty((B, Hq, Nq))
+    for b in range(B):
+        n = int(kv_lens[b])
+        if n < Nq:
+            raise ValueError("each kv_lens[b] must be >= Nq")
+        for kvh in range(Hkv):
+            K = gather_paged(kpool, block_table, b, kvh, n, page_size)
+            V = gather_paged(vpool, block_table, b, kvh, n, page_size)
+            for h in range(kvh * G, (kvh + 1) * G):
+                for i0 in range(0, Nq, row_block):
+                    rows = np.arange(i0, min(Nq, i0 + row_block))
+                    o[b, h, rows], lse[b, h, rows] = attention_rows(
+                        q[b, h, rows], K, V, scale, causal, rows, Nq)
+    return o, lse
+
+
 # ---------------------------------------------------------------------------
 # Combining partial results over disjoint key sets
 # ---------------------------------------------------------------------------

@@ -29,8 +29,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["attn_fwd_prefill", "attn_fwd_decode",
-                                           "attn_decode_workspace_bytes",
+    assert declared_functions() == sorted(["attn_fwd_prefill", "attn_fwd_prefill_paged",
+                                           "attn_fwd_decode", "attn_decode_workspace_bytes",
                                            "attn_decode_num_splits", "attn_status_string"])
 
 
@@ -65,6 +65,29 @@ def prefill(lib, q=P, k=P, v=P, o=P, lse=None, B=1, Hq=2, Hkv=1, Nq=4, Nk=4, d=6
 ])
 def test_prefill_validation(lib, kw, status):
     assert prefill(lib, **kw) == status
+
+
+def prefill_paged(lib, q=P, kc=P, vc=P, table=P, kv_lens=P, o=P, lse=None, B=2, Hq=8, Hkv=2,
+                  Nq=16, d=128, max_kv=100, page_size=16, max_blocks=7, num_pages=10, causal=1,
+                  scale=0.1):
+    return lib.attn_fwd_prefill_paged(q, kc, vc, table, kv_lens, o, lse, B, Hq, Hkv, Nq, d, max_kv,
+                                      page_size, max_blocks, num_pages, causal,
+                                      ctypes.c_float(scale), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(kc=None), INVALID), (dict(vc=None), INVALID),
+    (dict(table=None), INVALID), (dict(kv_lens=None), INVALID), (dict(o=None), INVALID),
+    (dict(q=MIS), INVALID), (dict(kv_lens=ctypes.c_void_p(4098)), INVALID),
+    (dict(lse=ctypes.c_void_p(4098)), INVALID), (dict(B=0), INVALID), (dict(Nq=0), INVALID),
+    (dict(Hq=6, Hkv=4), INVALID), (dict(max_kv=0), INVALID), (dict(Nq=101), INVALID),
+    (dict(num_pages=0), INVALID), (dict(max_blocks=6), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(d=80), UNSUPPORTED),
+    (dict(page_size=32), UNSUPPORTED),
+    (dict(B=65536, Hq=65536, Hkv=1), UNSUPPORTED),
+])
+def test_prefill_paged_validation(lib, kw, status):
+    assert prefill_paged(lib, **kw) == status
 
 
 def decode(lib, q=P, kc=P, vc=P, table=None, seqlens=P, o=P, lse=None, B=2, Hq=8, Hkv=2, d=128,

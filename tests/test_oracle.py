@@ -11,8 +11,9 @@ import os
 import numpy as np
 import pytest
 
-from oracle import (attention_decode, attention_prefill, attention_probabilities, attention_rows,
-                    brute_force_attention, merge_partials, online_attention, softmax_rows)
+from oracle import (attention_decode, attention_prefill, attention_prefill_paged,
+                    attention_probabilities, attention_rows, brute_force_attention,
+                    merge_partials, online_attention, softmax_rows)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -339,3 +340,89 @@ def test_merge_with_empty_split_is_identity():
     assert l == 0.3
     r, l = merge_partials(o, np.array([-np.inf, -np.inf]))
     assert (r == 0).all() and l == -np.inf
+
+
+# ----------------------------------------------------------- chunked prefill, paged cache
+def _chunk_case(seed=70, B=3, Hq=4, Hkv=2, d=4, lens=(9, 5, 14), Nq=5, ps=4):
+    q_full, kc, vc, lens = _decode_case(seed=seed, B=B, Hq=Hq, Hkv=Hkv, d=d, lens=lens, ps=ps)
+    rng = np.random.default_rng(seed + 1)
+    q = rng.standard_normal((B, Hq, Nq, d))
+    return q, kc, vc, lens
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_chunk_rows_equal_bottom_rows_of_full_prefill(causal):
+    # the chunk's queries are the last Nq tokens: their rows of a full prefill over the
+    # whole sequence (queries for every position) must equal the chunked result
+    q, kc, vc, lens = _chunk_case()
+    kp, table = _to_paged(kc, lens, 4, 3)
+    vp, _ = _to_paged(vc, lens, 4, 3)
+    o, lse = attention_prefill_paged(q, kp, vp, table, lens, 0.8, causal, page_size=4)
+    rng = np.random.default_rng(5)
+    Nq = q.shape[2]
+    for b, n in enumerate(lens):
+        qf = rng.standard_normal((1, 4, n, 4))
+        qf[0, :, n - Nq:] = q[b]
+        of, lf = attention_prefill(qf, kc[b:b + 1, :, :n], vc[b:b + 1, :, :n], 0.8, causal)
+        np.testing.assert_allclose(o[b], of[0, :, n - Nq:], atol=1e-13)
+        np.testing.assert_allclose(lse[b], lf[0, :, n - Nq:], atol=1e-13)
+
+
+def test_chunk_last_row_is_paged_decode():
+    q, kc, vc, lens = _chunk_case(seed=72)
+    kp, table = _to_paged(kc, lens, 4, 4)
+    vp, _ = _to_paged(vc, lens, 4, 4)
+    o, lse = attention_prefill_paged(q, kp, vp, table, lens, 0.6, True, page_size=4)
+    od, ld = attention_decode(q[:, :, -1], kp, vp, lens, 0.6, block_table=table, page_size=4)
+    np.testing.assert_allclose(o[:, :, -1], od, atol=1e-14)
+    np.testing.assert_allclose(lse[:, :, -1], ld, atol=1e-14)
+
+
+def test_chunk_first_row_of_a_whole_sequence_is_first_value():
+    # kv_lens == Nq: the chunk is the whole sequence and causal row 0 sees key 0 only
+    q, kc, vc, _ = _chunk_case(seed=74)
+    lens = np.array([5, 5, 5], np.int32)
+    kp, table = _to_paged(kc, lens, 4, 5)
+    vp, _ = _to_paged(vc, lens, 4, 5)
+    o, lse = attention_prefill_paged(q, kp, vp, table, lens, 0.9, True, page_size=4)
+    for b in range(3):
+        for h in range(4):
+            np.testing.assert_array_equal(o[b, h, 0], vc[b, h // 2, 0])
+            assert lse[b, h, 0] == pytest.approx(0.9 * q[b, h, 0] @ kc[b, h // 2, 0], abs=1e-14)
+
+
+def test_chunk_equal_keys_give_mean_of_visible_values():
+    q, kc, vc, lens = _chunk_case(seed=76)
+    Nq = q.shape[2]
+    kc[:] = np.where(np.isnan(kc), np.nan, 0.25)  # every live key row equal
+    kp, table = _to_paged(kc, lens, 4, 6)
+    vp, _ = _to_paged(vc, lens, 4, 6)
+    o, lse = attention_prefill_paged(q, kp, vp, table, lens, 1.0, True, page_size=4)
+    for b, n in enumerate(lens):
+        for h in range(4):
+            for i in range(Nq):
+                vis = n - Nq + i + 1
+                np.testing.assert_allclose(o[b, h, i], vc[b, h // 2, :vis].mean(axis=0), atol=1e-13)
+                assert lse[b, h, i] == pytest.approx(q[b, h, i].sum() * 0.25 + math.log(vis),
+                                                     abs=1e-13)
+
+
+def test_chunk_page_order_is_irrelevant_and_padding_unread():
+    q, kc, vc, lens = _chunk_case(seed=78)
+    outs = []
+    for seed in (7, 8):
+        kp, table = _to_paged(kc, lens, 4, seed)
+        vp, _ = _to_paged(vc, lens, 4, seed)
+        outs.append(attention_prefill_paged(q, kp, vp, table, lens, 0.5, True, page_size=4))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    np.testing.assert_array_equal(outs[0][1], outs[1][1])
+    assert np.isfinite(outs[0][0]).all()
+
+
+def test_chunk_rejects_context_shorter_than_chunk():
+    q, kc, vc, lens = _chunk_case(seed=80)
+    kp, table = _to_paged(kc, lens, 4, 9)
+    vp, _ = _to_paged(vc, lens, 4, 9)
+    with pytest.raises(ValueError):
+        attention_prefill_paged(q, kp, vp, table, np.array([4, 5, 14], np.int32), 0.5, True,
+                                page_size=4)

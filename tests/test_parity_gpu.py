@@ -16,7 +16,8 @@ import torch
 
 import attn_inputs as ai
 import io_aware_exact_attention_amd as mi
-from oracle import attention_decode, attention_prefill, attention_rows
+from oracle import (attention_decode, attention_prefill, attention_prefill_paged,
+                    attention_rows, gather_paged)
 
 pytestmark = pytest.mark.gpu
 
@@ -322,3 +323,76 @@ def test_decode_paged_config():
     o, lse = run_decode(q, kp, vp, lens, lay.block_table, maxlen, cfg.scale)
     ro, rl = decode_ref(q, kp, vp, lens, lay.block_table, cfg.scale)
     check("paged_gqa_decode", o, lse, ro, rl)
+
+
+# ------------------------------------------------------------------ chunked prefill, paged cache
+def make_chunk(B, Hq, Hkv, d, lens, Nq, seed, extra_pages=3):
+    """Chunk queries plus a paged cache whose unused slots and pages hold NaN."""
+    cfg = ai.DecodeCfg("chunk", B=B, Hq=Hq, Hkv=Hkv, d=d, seed=seed, paged=True, chunk=Nq)
+    lens = np.asarray(lens, np.int32)
+    q = ai.chunk_q(cfg)
+    lay = ai.paged_layout(lens, 16, seed, extra_pages=extra_pages)
+    kc = ai.build_paged_cache(cfg, ai.T_K, lens, lay)
+    vc = ai.build_paged_cache(cfg, ai.T_V, lens, lay)
+    return cfg, q, kc, vc, lens, lay.block_table
+
+
+def run_chunk(q, kc, vc, lens, table, causal, scale):
+    o, lse = mi.prefill_paged(dev(q).reshape(q.shape), dev(kc).reshape(kc.shape),
+                              dev(vc).reshape(vc.shape), torch.from_numpy(table).cuda(),
+                              torch.from_numpy(lens).cuda(), int(lens.max()), causal, scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("Nq,lens", [(1, (1, 17, 300)), (77, (77, 200, 1000)),
+                                     (256, (256, 300, 1031)), (300, (300, 301, 700))])
+def test_prefill_paged_chunks(d, causal, Nq, lens):
+    cfg, q, kc, vc, lens, table = make_chunk(3, 4, 2, d, lens, Nq, seed=2000 + Nq + d)
+    scale = 1 / math.sqrt(d)
+    o, lse = run_chunk(q, kc, vc, lens, table, causal, scale)
+    ro, rl = attention_prefill_paged(f64(q), f64(kc), f64(vc), table, lens, scale, causal)
+    check(f"prefill_paged d={d} causal={causal} Nq={Nq} lens={tuple(int(x) for x in lens)}",
+          o, lse, ro, rl)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_paged_equals_contiguous_prefill(causal):
+    # one sequence: the same key/value rows through the paged and the contiguous kernel
+    cfg, q, kc, vc, lens, table = make_chunk(1, 8, 2, 128, (1000,), 333, seed=2100)
+    o_p, l_p = run_chunk(q, kc, vc, lens, table, causal, 0.088)
+    k = np.stack([np.stack([gather_paged(kc, table, 0, h, 1000, 16) for h in range(2)])])
+    v = np.stack([np.stack([gather_paged(vc, table, 0, h, 1000, 16) for h in range(2)])])
+    o_c, l_c = run_prefill(q, k, v, causal, 0.088)
+    assert torch.equal(o_p, o_c) and torch.equal(l_p, l_c)
+
+
+def test_chunked_prefill_paged_config():
+    cfg = ai.CONFIGS["chunked_prefill_paged"]
+    lens = ai.decode_lengths(cfg)
+    q = ai.chunk_q(cfg)
+    lay = ai.paged_layout(lens, 16, cfg.seed)
+    kc = ai.build_paged_cache(cfg, ai.T_K, lens, lay)
+    vc = ai.build_paged_cache(cfg, ai.T_V, lens, lay)
+    o, lse = run_chunk(q, kc, vc, lens, lay.block_table, True, cfg.scale)
+    go = o.float().cpu().numpy().astype(np.float64)
+    gl = lse.float().cpu().numpy().astype(np.float64)
+    G = cfg.Hq // cfg.Hkv
+    errs, lerrs = [], []
+    for b in range(cfg.B):  # one query head per sequence, every row of it
+        h = (5 * b + 3) % cfg.Hq
+        kvh = h // G
+        n = int(lens[b])
+        K = f64(gather_paged(kc, lay.block_table, b, kvh, n, 16))
+        V = f64(gather_paged(vc, lay.block_table, b, kvh, n, 16))
+        rows = np.arange(cfg.chunk)
+        ro, rl = attention_rows(f64(q[b, h]), K, V, cfg.scale, True, rows, cfg.chunk)
+        errs.append(np.abs(go[b, h] - ro))
+        lerrs.append(np.abs(gl[b, h] - rl))
+    err, lerr = np.concatenate([e.ravel() for e in errs]), np.concatenate(lerrs)
+    log_case("chunked_prefill_paged (sampled)", max_abs=float(err.max()),
+             mean_abs=float(err.mean()), lse_max_abs=float(lerr.max()), n=int(err.size))
+    assert np.isfinite(go).all()
+    assert err.max() <= TOL_MAX and err.mean() <= TOL_MEAN and lerr.max() <= TOL_LSE
