@@ -309,6 +309,28 @@ def main():
         gbs = ai.decode_bytes(cfg, clens) / (avg * 1e-6) / 1e9
         extra["gqa_decode_contig"] = {"us": round(avg, 2), "us_min": round(mn, 2),
                                       "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        del cq, ckc, cvc, cseq, co, cl, cws
+        torch.cuda.empty_cache()
+        # chunked prefill against a paged cache (512 new tokens per sequence)
+        cfg = ai.CONFIGS["chunked_prefill_paged"]
+        plens = ai.decode_lengths(cfg)
+        lay = ai.paged_layout(plens, cfg.page_size, cfg.seed)
+        pq = to_dev(ai.chunk_q(cfg))
+        pkc = to_dev(ai.build_paged_cache(cfg, ai.T_K, plens, lay, pad_bits=np.uint16(0)))
+        pvc = to_dev(ai.build_paged_cache(cfg, ai.T_V, plens, lay, pad_bits=np.uint16(0)))
+        ptab = torch.from_numpy(lay.block_table).cuda()
+        plen_d = torch.from_numpy(plens).cuda()
+        po = torch.empty_like(pq)
+        pl = torch.empty(pq.shape[:3], dtype=torch.float32, device="cuda")
+        pmax = int(plens.max())
+        avg, med, mn = time_kernel(
+            lambda: mi.attn_fwd_prefill_paged(pq, pkc, pvc, ptab, plen_d, po, pl, pmax, True,
+                                              cfg.scale, stream=stream), args.steps, args.warmup)
+        tf = ai.chunk_prefill_flops(cfg, plens) / (avg * 1e-6) / 1e12
+        extra["chunked_prefill_paged"] = {"us": round(avg, 2), "us_min": round(mn, 2),
+                                          "TFLOP/s": round(tf, 2),
+                                          "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                                          "chunk": cfg.chunk, "kv_lens": [int(x) for x in plens]}
         out["other_workloads"] = extra
 
     if args.copy_mib > 0:
