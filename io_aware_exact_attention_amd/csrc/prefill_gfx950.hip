@@ -123,6 +123,50 @@ __device__ __forceinline__ WorkItem prefill_work_item(int p, int BH, int nq, int
   return w;
 }
 
+// Work order for chunked prefill over a paged cache, where contexts differ in length.
+// When Hq splits over the 8 XCDs, XCD x owns query heads [x*Hq/8, (x+1)*Hq/8) of every
+// sequence (with grouped heads that keeps one KV head's pages in one L2), and within the
+// XCD the sequences go out longest context first.  Sequences are ranked by kv_lens with
+// one load per lane and cross-lane reads (up to 64 sequences; beyond that, batch order).
+struct PagedItem {
+  int b, hq, qrank;
+};
+
+__device__ __forceinline__ int sequence_of_rank(int r, int B, const int32_t* kv_lens, int lane) {
+  if (B > 64) return r;
+  const int mine = lane < B ? kv_lens[lane] : -1;
+  int rank = 0;
+  for (int j = 0; j < B; ++j) {
+    const int o = __builtin_amdgcn_readlane(mine, j);
+    rank += (o > mine) || (o == mine && j < lane);
+  }
+  const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < B && rank == r);
+  return (int)__builtin_ctzll(hit);
+}
+
+__device__ __forceinline__ PagedItem paged_work_item(int p, int B, int Hq, int nq,
+                                                     const int32_t* kv_lens, int lane) {
+  int r, hq, qr;
+  if ((Hq & 7) == 0) {
+    const int hpx = Hq >> 3;
+    const int k = p >> 3;
+    r = k / (hpx * nq);
+    const int rem = k - r * (hpx * nq);
+    hq = (p & 7) * hpx + rem / nq;
+    qr = rem % nq;
+  } else {
+    r = p / (Hq * nq);
+    const int rem = p - r * (Hq * nq);
+    hq = rem / nq;
+    qr = rem % nq;
+  }
+  PagedItem it;
+  it.b = sequence_of_rank(r, B, kv_lens, lane);
+  it.hq = hq;
+  it.qrank = qr;
+  return it;
+}
+
 template <int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillParams a) {
@@ -136,10 +180,19 @@ void prefill_kernel(PrefillParams a) {
   const int g = lane >> 5;     // which half of the keys / head dim this lane's operands hold
 
   // --- workgroup -> (query tile, head, batch)
-  const WorkItem wi = prefill_work_item(blockIdx.x, a.B * a.Hq, a.num_qtiles, a.head_group);
-  const int hq = wi.bh % a.Hq;
-  const int b = wi.bh / a.Hq;
-  const int qtile = CAUSAL ? (a.num_qtiles - 1 - wi.qrank) : wi.qrank;
+  int hq, b, qrank;
+  if (PAGED) {
+    const PagedItem pi = paged_work_item(blockIdx.x, a.B, a.Hq, a.num_qtiles, a.kv_lens, lane);
+    hq = pi.hq;
+    b = pi.b;
+    qrank = pi.qrank;
+  } else {
+    const WorkItem wi = prefill_work_item(blockIdx.x, a.B * a.Hq, a.num_qtiles, a.head_group);
+    hq = wi.bh % a.Hq;
+    b = wi.bh / a.Hq;
+    qrank = wi.qrank;
+  }
+  const int qtile = CAUSAL ? (a.num_qtiles - 1 - qrank) : qrank;
   const int kvh = hq / (a.Hq / a.Hkv);
   const int m0 = qtile * S::BM;
   // Keys of this sequence: Nk, or (paged cache) its own context length, which includes
