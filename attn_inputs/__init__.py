@@ -11,7 +11,10 @@ full-size workload can be regenerated on its own (the oracle checks sampled
 heads of the large workloads without drawing the whole tensor).
 
 Value recipe (all workloads): i.i.d. float32 N(0, 1) draws, optionally multiplied
-by a constant in float32, rounded to bfloat16 with round-to-nearest-even.
+by a constant in float32, rounded to bfloat16 with round-to-nearest-even.  An FP8
+KV cache holds the same draws divided (in float32) by a per-tensor scale and rounded
+to OCP FP8 E4M3 codes (round-to-nearest-even, saturating at +-448); the value a code
+stands for is that scale times the code's E4M3 value.
 """
 from __future__ import annotations
 
@@ -24,6 +27,14 @@ import numpy as np
 T_Q, T_K, T_V, T_LEN, T_PERM = 0, 1, 2, 3, 4
 
 BF16_NAN = np.uint16(0x7FC0)
+E4M3_NAN = np.uint8(0x7F)
+
+# Per-tensor scales of the FP8 KV caches: a code c of the K (V) cache stands for
+# FP8_K_SCALE * e4m3(c) (FP8_V_SCALE * e4m3(c)).  Chosen so that N(0, 1) draws use the
+# E4M3 range up to about 8 (6) standard deviations; the two differ so that a swapped
+# pair of scales shows.
+FP8_K_SCALE = float(np.float32(8.0 / 448.0))
+FP8_V_SCALE = float(np.float32(6.0 / 448.0))
 
 
 # ----------------------------------------------------------------------------
@@ -53,6 +64,29 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return bf16_bits_to_f32(bits).astype(np.float64)
 
 
+def to_e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to OCP FP8 E4M3 codes (1 sign, 4 exponent bits with bias 7,
+    3 mantissa bits; no infinities), round to nearest with ties to even, magnitudes
+    above 448 (the largest finite E4M3 value) saturating to 448.
+
+    Normal range (|x| >= 2^-6): the float32 mantissa is rounded to 3 bits by adding a
+    bias below bit 20, as for bfloat16 above, and the exponent re-biased.  Subnormal
+    range: the code is the integer rint(|x| * 2^9), in units of 2^-9.  Returns uint8
+    codes; NaN is never produced (inputs are finite draws).
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    a = np.minimum(np.abs(x), np.float32(448.0))
+    u = a.view(np.uint32)
+    lsb = (u >> np.uint32(20)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFFF) + lsb) & np.uint32(0xFFF00000)
+    exp = (r >> np.uint32(23)).astype(np.int32) - 127
+    normal_code = ((exp + 7) << 3) | ((r >> np.uint32(20)) & np.uint32(7)).astype(np.int32)
+    sub_code = np.rint(a.astype(np.float64) * 512.0).astype(np.int32)
+    code = np.where(a < np.float32(2.0 ** -6), sub_code, normal_code)
+    sign = np.signbit(x).astype(np.int32) << 7
+    return (code | sign).astype(np.uint8)
+
+
 def _stream(seed: int, tensor: int, b: int = 0, h: int = 0) -> np.random.Generator:
     return np.random.default_rng(np.random.SeedSequence([seed, tensor, b, h]))
 
@@ -63,6 +97,13 @@ def normal_bf16(seed: int, tensor: int, b: int, h: int, shape, mult: float = 1.0
     if mult != 1.0:
         x *= np.float32(mult)
     return to_bf16_bits(x)
+
+
+def normal_e4m3(seed: int, tensor: int, b: int, h: int, shape, scale: float) -> np.ndarray:
+    """One head's slice of an FP8 cache: the float32 N(0,1) draws of ``normal_bf16`` (same
+    stream), divided by ``scale`` in float32, as E4M3 codes."""
+    x = _stream(seed, tensor, b, h).standard_normal(shape, dtype=np.float32)
+    return to_e4m3_codes(x / np.float32(scale))
 
 
 # ----------------------------------------------------------------------------
@@ -100,6 +141,7 @@ class DecodeCfg:
     fixed_len: int = 0            # every sequence this long (contiguous workload)
     len_range: tuple = (0, 0)     # inclusive uniform range of lengths (paged workload)
     chunk: int = 0                # chunked prefill: new tokens (queries) per sequence
+    kv_fp8: bool = False          # K/V cache as E4M3 codes with FP8_K_SCALE / FP8_V_SCALE
 
     @property
     def scale(self) -> float:
@@ -124,6 +166,10 @@ CONFIGS = {
     # Paged GQA decode, 16-token pages, lengths uniform in [1024, 131072].
     "paged_gqa_decode": DecodeCfg("paged_gqa_decode", B=8, Hq=32, Hkv=8, d=128, seed=5,
                                   paged=True, page_size=16, len_range=(1024, 131072)),
+    # The paged decode workload (same lengths and page layout) over an FP8 E4M3 cache.
+    "paged_gqa_decode_fp8": DecodeCfg("paged_gqa_decode_fp8", B=8, Hq=32, Hkv=8, d=128,
+                                      seed=5, paged=True, page_size=16,
+                                      len_range=(1024, 131072), kv_fp8=True),
     # Chunked prefill against a paged cache: 512 new tokens per sequence appended to
     # contexts (which already hold them) of 2048..16384 tokens, Llama-2-style GQA heads.
     "chunked_prefill_paged": DecodeCfg("chunked_prefill_paged", B=8, Hq=32, Hkv=8, d=128,
@@ -183,8 +229,23 @@ def decode_q(cfg: DecodeCfg) -> np.ndarray:
     return q
 
 
+def kv_scale(cfg: DecodeCfg, tensor: int) -> float:
+    """Per-tensor scale of an FP8 cache (1.0 for a bf16 cache)."""
+    if not cfg.kv_fp8:
+        return 1.0
+    return FP8_K_SCALE if tensor == T_K else FP8_V_SCALE
+
+
+def kv_pad(cfg: DecodeCfg):
+    """NaN of the cache's element type: fills slots that must never be read."""
+    return E4M3_NAN if cfg.kv_fp8 else BF16_NAN
+
+
 def decode_kv_logical(cfg: DecodeCfg, tensor: int, b: int, kvh: int, length: int) -> np.ndarray:
-    """The first ``length`` cached K (or V) rows of sequence b, KV head kvh: [length, d] bits."""
+    """The first ``length`` cached K (or V) rows of sequence b, KV head kvh: [length, d]
+    bf16 bits, or E4M3 codes for an FP8 cache."""
+    if cfg.kv_fp8:
+        return normal_e4m3(cfg.seed, tensor, b, kvh, (length, cfg.d), kv_scale(cfg, tensor))
     return normal_bf16(cfg.seed, tensor, b, kvh, (length, cfg.d))
 
 
@@ -215,9 +276,11 @@ def paged_layout(lengths: np.ndarray, page_size: int, seed: int, max_blocks: int
 
 
 def build_contig_cache(cfg: DecodeCfg, tensor: int, lengths: np.ndarray, max_len: int,
-                       pad_bits=BF16_NAN) -> np.ndarray:
-    """[B, Hkv, max_len, d] bits; slots at or past lengths[b] hold ``pad_bits``."""
-    c = np.full((cfg.B, cfg.Hkv, max_len, cfg.d), pad_bits, np.uint16)
+                       pad_bits=None) -> np.ndarray:
+    """[B, Hkv, max_len, d] bits (uint16 bf16, or uint8 E4M3 codes for an FP8 cache);
+    slots at or past lengths[b] hold ``pad_bits`` (default: the element type's NaN)."""
+    pad = kv_pad(cfg) if pad_bits is None else pad_bits
+    c = np.full((cfg.B, cfg.Hkv, max_len, cfg.d), pad, type(kv_pad(cfg)))
     for b in range(cfg.B):
         n = int(lengths[b])
         for h in range(cfg.Hkv):
@@ -226,17 +289,20 @@ def build_contig_cache(cfg: DecodeCfg, tensor: int, lengths: np.ndarray, max_len
 
 
 def build_paged_cache(cfg: DecodeCfg, tensor: int, lengths: np.ndarray, layout: PagedLayout,
-                      pad_bits=BF16_NAN) -> np.ndarray:
-    """[num_pages, Hkv, page_size, d] bits; unused slots and pages hold ``pad_bits``."""
+                      pad_bits=None) -> np.ndarray:
+    """[num_pages, Hkv, page_size, d] bits (as in build_contig_cache); unused slots and
+    pages hold ``pad_bits`` (default: the element type's NaN)."""
     ps = layout.page_size
-    pool = np.full((layout.num_pages, cfg.Hkv, ps, cfg.d), pad_bits, np.uint16)
+    pad = kv_pad(cfg) if pad_bits is None else pad_bits
+    etype = type(kv_pad(cfg))
+    pool = np.full((layout.num_pages, cfg.Hkv, ps, cfg.d), pad, etype)
     for b in range(cfg.B):
         n = int(lengths[b])
         nblk = (n + ps - 1) // ps
         pages = layout.block_table[b, :nblk]
         for h in range(cfg.Hkv):
             rows = decode_kv_logical(cfg, tensor, b, h, n)
-            padded = np.full((nblk * ps, cfg.d), pad_bits, np.uint16)
+            padded = np.full((nblk * ps, cfg.d), pad, etype)
             padded[:n] = rows
             pool[pages, h] = padded.reshape(nblk, ps, cfg.d)
     return pool
@@ -273,7 +339,7 @@ def decode_bytes(cfg: DecodeCfg, lengths: np.ndarray) -> int:
     """Algorithmic HBM bytes of one decode step: K and V of the live tokens, Q, O,
     LSE, the lengths and (paged) the live block-table entries."""
     tot = int(np.sum(lengths, dtype=np.int64))
-    kv = 2 * tot * cfg.Hkv * cfg.d * 2
+    kv = 2 * tot * cfg.Hkv * cfg.d * (1 if cfg.kv_fp8 else 2)
     qo = 2 * cfg.B * cfg.Hq * cfg.d * 2
     lse = cfg.B * cfg.Hq * 4
     lens = cfg.B * 4

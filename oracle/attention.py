@@ -159,6 +159,57 @@ def attention_decode(q: np.ndarray, kcache: np.ndarray, vcache: np.ndarray,
     return o, lse
 
 
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) KV cache
+# ---------------------------------------------------------------------------
+def e4m3_value(codes: np.ndarray) -> np.ndarray:
+    """float64 value of OCP FP8 E4M3 codes (the 8-bit format of a compressed KV cache,
+    page "메모리 장벽을 넘어" (tiptinker), section "2. FlashInfer"; the pages do not spell
+    the format out, so the OCP 8-bit floating point definition is used): bit 7 sign,
+    bits 6..3 exponent e with bias 7, bits 2..0 mantissa m;
+      e == 0:            (-1)^s * (m / 8) * 2^-6      (zero and subnormals)
+      e == 15 and m == 7: NaN                          (no infinities)
+      otherwise:          (-1)^s * (1 + m / 8) * 2^(e - 7)."""
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (c & 0x7 == 7), np.nan, mag)
+    return sign * mag
+
+
+def attention_decode_fp8(q: np.ndarray, kcodes: np.ndarray, vcodes: np.ndarray,
+                         seqlens: np.ndarray, scale: float, k_scale: float, v_scale: float,
+                         block_table: np.ndarray | None = None, page_size: int = 16):
+    """Decode over an FP8 KV cache with one scale per tensor: the cached K is
+    k_scale * e4m3_value(kcodes) and V is v_scale * e4m3_value(vcodes) (per-tensor
+    scaling is a reading: the pages give no scale convention).  The caches are laid out
+    as in attention_decode (codes instead of values); only the live rows of each
+    (sequence, KV head) are dequantised, then attention is the plain definition.
+    Returns O [B,Hq,d], LSE [B,Hq] (float64)."""
+    B, Hq, d = q.shape
+    Hkv = kcodes.shape[1]
+    G = Hq // Hkv
+    o = np.zeros((B, Hq, d))
+    lse = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        n = int(seqlens[b])
+        if n == 0:
+            continue
+        for kvh in range(Hkv):
+            if block_table is None:
+                kc, vc = kcodes[b, kvh, :n], vcodes[b, kvh, :n]
+            else:
+                kc = gather_paged(kcodes, block_table, b, kvh, n, page_size)
+                vc = gather_paged(vcodes, block_table, b, kvh, n, page_size)
+            K = k_scale * e4m3_value(kc)
+            V = v_scale * e4m3_value(vc)
+            hs = slice(kvh * G, (kvh + 1) * G)
+            o[b, hs], lse[b, hs] = attention_rows(q[b, hs], K, V, scale, False, np.arange(G), G)
+    return o, lse
+
+
 def attention_prefill_paged(q: np.ndarray, kpool: np.ndarray, vpool: np.ndarray,
                             block_table: np.ndarray, kv_lens: np.ndarray, scale: float,
                             causal: bool, page_size: int = 16, row_block: int = 1024):

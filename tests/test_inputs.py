@@ -84,3 +84,57 @@ def test_config_work_figures():
     assert ai.prefill_flops(ai.CONFIGS["long_prefill_32k"]) == 8_796_361_457_664
     c4 = ai.CONFIGS["gqa_decode_contig"]
     assert ai.decode_bytes(c4, ai.decode_lengths(c4)) == 2_148_540_672
+
+
+# ----------------------------------------------------------------------------- FP8 E4M3 codes
+def _torch_e4m3(x):
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_rounding_matches_torch():
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal(400_000) * np.exp(rng.uniform(-14, 7, 400_000))).astype(np.float32)
+    x = np.clip(x, -448, 448)
+    np.testing.assert_array_equal(ai.to_e4m3_codes(x), _torch_e4m3(x))
+    # exact midpoints between neighbouring finite codes: ties go to the even code
+    vals = torch.arange(127, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    mid = (vals[:-1] + vals[1:]) / 2
+    assert (mid.astype(np.float32).astype(np.float64) == mid).all()
+    both = np.concatenate([mid, -mid]).astype(np.float32)
+    codes = ai.to_e4m3_codes(both)
+    np.testing.assert_array_equal(codes, _torch_e4m3(both))
+    assert (codes % 2 == 0).all()
+
+
+def test_e4m3_saturates_and_keeps_signed_zero():
+    x = np.array([448.0, 460.0, 1e6, -1e6, 0.0, -0.0, 2.0 ** -10, 2.0 ** -9], np.float32)
+    np.testing.assert_array_equal(ai.to_e4m3_codes(x),
+                                  np.array([0x7E, 0x7E, 0x7E, 0xFE, 0, 0x80, 0, 1], np.uint8))
+
+
+def test_fp8_cache_quantises_the_bf16_workload_draws():
+    cfg = ai.DecodeCfg("t", B=2, Hq=4, Hkv=2, d=8, seed=11, paged=True, len_range=(3, 40),
+                       kv_fp8=True)
+    lens = ai.decode_lengths(cfg)
+    rows = ai.decode_kv_logical(cfg, ai.T_V, 1, 1, int(lens[1]))
+    x = np.random.default_rng(np.random.SeedSequence([11, ai.T_V, 1, 1])).standard_normal(
+        (int(lens[1]), 8), dtype=np.float32)
+    assert rows.dtype == np.uint8
+    np.testing.assert_array_equal(rows, _torch_e4m3(x / np.float32(ai.FP8_V_SCALE)))
+    lay = ai.paged_layout(lens, 16, cfg.seed)
+    pool = ai.build_paged_cache(cfg, ai.T_V, lens, lay)
+    assert pool.dtype == np.uint8
+    for t in range(int(lens[1])):
+        np.testing.assert_array_equal(pool[lay.block_table[1, t // 16], 1, t % 16], rows[t])
+    # unused slots of a partly filled page hold the E4M3 NaN code
+    n = int(lens[1])
+    if n % 16:
+        assert (pool[lay.block_table[1, n // 16], 1, n % 16:] == 0x7F).all()
+    assert ai.kv_scale(cfg, ai.T_K) == ai.FP8_K_SCALE != ai.FP8_V_SCALE
+    base = ai.CONFIGS["paged_gqa_decode"]
+    f8 = ai.CONFIGS["paged_gqa_decode_fp8"]
+    np.testing.assert_array_equal(ai.decode_lengths(base), ai.decode_lengths(f8))
+    lb = ai.decode_lengths(base)
+    kv = 2 * int(lb.sum()) * base.Hkv * base.d
+    assert ai.decode_bytes(base, lb) - ai.decode_bytes(f8, lb) == kv

@@ -263,7 +263,8 @@ def _to_paged(kc, lens, ps, perm_seed):
     P = sum(nblk) + 2
     perm = np.random.default_rng(perm_seed).permutation(P)
     table = np.full((B, max(nblk)), -1, np.int32)
-    pool = np.full((P, Hkv, ps, d), np.nan)
+    pad = 0x7F if kc.dtype == np.uint8 else np.nan   # never-read slots hold NaN
+    pool = np.full((P, Hkv, ps, d), pad, kc.dtype)
     off = 0
     for b, n in enumerate(lens):
         table[b, :nblk[b]] = perm[off:off + nblk[b]]
@@ -426,3 +427,89 @@ def test_chunk_rejects_context_shorter_than_chunk():
     with pytest.raises(ValueError):
         attention_prefill_paged(q, kp, vp, table, np.array([4, 5, 14], np.int32), 0.5, True,
                                 page_size=4)
+
+
+# ----------------------------------------------------------------------------- FP8 KV cache
+def test_e4m3_values_match_torch_for_every_code():
+    import torch
+    from oracle import e4m3_value
+    codes = np.arange(256, dtype=np.uint8)
+    ours = e4m3_value(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert (np.isnan(ours) == np.isnan(ref)).all()
+    assert np.flatnonzero(np.isnan(ours)).tolist() == [0x7F, 0xFF]
+    fin = ~np.isnan(ref)
+    np.testing.assert_array_equal(ours[fin], ref[fin])
+    assert (np.signbit(ours[fin]) == np.signbit(ref[fin])).all()
+
+
+def test_e4m3_closed_forms():
+    from oracle import e4m3_value
+    cases = {0x38: 1.0, 0xB8: -1.0, 0x7E: 448.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9,
+             0x08: 2.0 ** -6, 0x3C: 1.5, 0x40: 2.0, 0x00: 0.0, 0x77: 240.0}
+    got = e4m3_value(np.array(list(cases), np.uint8))
+    np.testing.assert_array_equal(got, np.array(list(cases.values())))
+    assert np.signbit(e4m3_value(np.array([0x80], np.uint8)))[0]
+    # every finite code is a round trip through the (independent) input encoder
+    import attn_inputs as ai
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    np.testing.assert_array_equal(ai.to_e4m3_codes(e4m3_value(codes).astype(np.float32)), codes)
+
+
+def _fp8_case(seed, B=3, Hq=4, Hkv=2, d=5, lens=(6, 0, 9)):
+    rng = np.random.default_rng(seed)
+    nmax = max(lens)
+    q = rng.standard_normal((B, Hq, d))
+    codes = [c for c in range(256) if c & 0x7F != 0x7F]
+    kc = rng.choice(codes, (B, Hkv, nmax + 2, d)).astype(np.uint8)
+    vc = rng.choice(codes, (B, Hkv, nmax + 2, d)).astype(np.uint8)
+    for b, n in enumerate(lens):       # slots past the length hold the NaN code
+        kc[b, :, n:] = 0x7F
+        vc[b, :, n:] = 0xFF
+    return q, kc, vc, np.array(lens, np.int32)
+
+
+def test_fp8_decode_matches_brute_force_on_torch_dequantised_cache():
+    import torch
+    from oracle import attention_decode_fp8
+    q, kc, vc, lens = _fp8_case(71)
+    ks, vs = 0.0173, 0.031
+    o, lse = attention_decode_fp8(q, kc, vc, lens, 0.45, ks, vs)
+    deq = lambda c: torch.from_numpy(c).view(torch.float8_e4m3fn).double().numpy()
+    assert (o[1] == 0).all() and (lse[1] == -np.inf).all()
+    for b, n in enumerate(lens):
+        if n == 0:
+            continue
+        for h in range(4):
+            K = (ks * deq(kc[b, h // 2, :n])).tolist()
+            V = (vs * deq(vc[b, h // 2, :n])).tolist()
+            bo, bl = brute_force_attention([q[b, h].tolist()], K, V, 0.45, False)
+            np.testing.assert_allclose(o[b, h], bo[0], rtol=1e-12, atol=1e-14)
+            assert lse[b, h] == pytest.approx(bl[0], abs=1e-12)
+
+
+def test_fp8_scales_fold_into_the_softmax_scale_and_the_output():
+    from oracle import attention_decode_fp8
+    q, kc, vc, lens = _fp8_case(72)
+    o0, l0 = attention_decode_fp8(q, kc, vc, lens, 0.3 * 0.02, 1.0, 1.0)
+    o1, l1 = attention_decode_fp8(q, kc, vc, lens, 0.3, 0.02, 1.0)
+    np.testing.assert_allclose(o1, o0, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l1, l0, rtol=1e-12, atol=1e-13)
+    o2, l2 = attention_decode_fp8(q, kc, vc, lens, 0.3, 0.02, 0.125)
+    np.testing.assert_allclose(o2, 0.125 * o1, rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(l2, l1)
+    # the two scales are not interchangeable
+    o3, _ = attention_decode_fp8(q, kc, vc, lens, 0.3, 0.125, 0.02)
+    assert np.abs(o3 - o2).max() > 1e-3
+
+
+def test_fp8_paged_equals_contiguous():
+    from oracle import attention_decode_fp8
+    q, kc, vc, lens = _fp8_case(73, lens=(7, 4, 13))
+    o0, l0 = attention_decode_fp8(q, kc, vc, lens, 0.6, 0.05, 0.07)
+    kp, table = _to_paged(kc, lens, 4, 3)
+    vp, _ = _to_paged(vc, lens, 4, 3)
+    o1, l1 = attention_decode_fp8(q, kp, vp, lens, 0.6, 0.05, 0.07, block_table=table,
+                                  page_size=4)
+    np.testing.assert_array_equal(o1, o0)
+    np.testing.assert_array_equal(l1, l0)
