@@ -118,7 +118,11 @@ def decode_setup(name):
         kc = ai.build_contig_cache(cfg, ai.T_K, lens, maxlen, pad_bits=np.uint16(0))
         vc = ai.build_contig_cache(cfg, ai.T_V, lens, maxlen, pad_bits=np.uint16(0))
         table = None
-    dq, dkc, dvc = to_dev(q), to_dev(kc), to_dev(vc)
+    dq = to_dev(q)
+    if cfg.kv_fp8:   # E4M3 codes stay bytes
+        dkc, dvc = torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda()
+    else:
+        dkc, dvc = to_dev(kc), to_dev(vc)
     del kc, vc
     o = torch.empty_like(dq)
     lse = torch.empty((cfg.B, cfg.Hq), dtype=torch.float32, device="cuda")
@@ -310,6 +314,20 @@ def main():
         extra["gqa_decode_contig"] = {"us": round(avg, 2), "us_min": round(mn, 2),
                                       "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
         del cq, ckc, cvc, cseq, co, cl, cws
+        torch.cuda.empty_cache()
+        # the paged decode workload over an FP8 E4M3 cache (same lengths and pages)
+        cfg, flens, fmax, (fq, fkc, fvc, ftab, fseq, fo, fl) = decode_setup("paged_gqa_decode_fp8")
+        fws = mi.decode_workspace(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, fmax, 0)
+        avg, med, mn = time_kernel(
+            lambda: mi.attn_fwd_decode_fp8(fq, fkc, fvc, ftab, fseq, fo, fl, fmax, cfg.scale,
+                                           ai.FP8_K_SCALE, ai.FP8_V_SCALE, 0, fws,
+                                           stream=stream), args.steps, args.warmup)
+        gbs = ai.decode_bytes(cfg, flens) / (avg * 1e-6) / 1e9
+        extra["paged_gqa_decode_fp8"] = {"us": round(avg, 2), "us_min": round(mn, 2),
+                                         "GB/s": round(gbs, 1),
+                                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                         "speedup_vs_bf16_cache": round(d_avg / avg, 3)}
+        del fq, fkc, fvc, ftab, fseq, fo, fl, fws
         torch.cuda.empty_cache()
         # chunked prefill against a paged cache (512 new tokens per sequence)
         cfg = ai.CONFIGS["chunked_prefill_paged"]

@@ -143,7 +143,32 @@ int attn_fwd_decode(const void* q, const void* kcache, const void* vcache,
                     int max_blocks_per_seq, int num_pages, float scale, int num_splits,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Number of KV chunks attn_fwd_decode uses for these arguments (num_splits 0 = auto).
+/*
+ * Decode over an FP8 KV cache: attn_fwd_decode with K and V stored as OCP FP8 E4M3 codes
+ * (1 byte per element: sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities; codes 0x7F and 0xFF are NaN) and one scale per tensor, so the cached key
+ * is k_scale * e4m3(code) and the cached value v_scale * e4m3(code).  Compressed (FP8)
+ * KV caches, which halve the bytes decode streams: page "메모리 장벽을 넘어: LLM 연산자
+ * 가속 라이브러리 심층 분석" (tiptinker), section "2. FlashInfer".
+ *
+ *   kcache, vcache  uint8 codes in the layouts of attn_fwd_decode ([B, Hkv, max_seqlen, d]
+ *                   contiguous, or [num_pages, Hkv, 16, d] paged), 16-byte aligned.
+ *   k_scale, v_scale  finite and > 0.
+ *   All other arguments, the chunking (attn_decode_num_splits), the workspace
+ *   (attn_decode_workspace_bytes) and the outputs are those of attn_fwd_decode.
+ *
+ * Errors: those of attn_fwd_decode, plus INVALID_ARGUMENT for a non-finite or
+ * non-positive k_scale or v_scale, or when |scale| * k_scale overflows float.
+ */
+int attn_fwd_decode_fp8(const void* q, const void* kcache, const void* vcache,
+                        const int32_t* block_table, const int32_t* seqlens, void* o,
+                        float* lse, int B, int Hq, int Hkv, int d, int max_seqlen,
+                        int page_size, int max_blocks_per_seq, int num_pages, float scale,
+                        float k_scale, float v_scale, int num_splits, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/* Number of KV chunks attn_fwd_decode (and attn_fwd_decode_fp8) uses for these arguments
+ * (num_splits 0 = auto).
  * Returns 0 for invalid arguments.  Pure host arithmetic; no HIP call. */
 int attn_decode_num_splits(int B, int Hq, int Hkv, int d, int max_seqlen, int num_splits);
 

@@ -57,6 +57,9 @@ def load_library():
     lib.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                     i32, f32, i32, vp, ctypes.c_size_t, vp]
     lib.attn_fwd_decode.restype = i32
+    lib.attn_fwd_decode_fp8.argtypes = [vp] * 7 + [i32] * 8 + [f32, f32, f32, i32, vp,
+                                                               ctypes.c_size_t, vp]
+    lib.attn_fwd_decode_fp8.restype = i32
     lib.attn_decode_workspace_bytes.argtypes = [i32] * 6
     lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_decode_num_splits.argtypes = [i32] * 6
@@ -187,17 +190,16 @@ def attn_decode_num_splits(B, Hq, Hkv, d, max_seqlen, num_splits=0) -> int:
     return int(load_library().attn_decode_num_splits(B, Hq, Hkv, d, max_seqlen, num_splits))
 
 
-def attn_fwd_decode(q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen: int,
-                    scale: float, num_splits: int = 0, workspace=None, page_size: int = 16,
-                    num_pages: int | None = None, stream=None) -> None:
-    """q/o [B,Hq,d] bf16; lse [B,Hq] fp32 or None; seqlens int32 [B] (device).
-    block_table None: caches [B,Hkv,max_seqlen,d]; else caches [num_pages,Hkv,16,d] and
-    block_table int32 [B, max_blocks]."""
-    lib = load_library()
+def _decode_args(q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen, workspace,
+                 page_size, num_pages, cache_dtypes):
+    """Checks shared by both decode entry points; returns the size arguments."""
     _check(q, "q", torch.bfloat16, 3)
     dev = q.device
-    _check(kcache, "kcache", torch.bfloat16, 4, dev)
-    _check(vcache, "vcache", torch.bfloat16, 4, dev)
+    for name, t in (("kcache", kcache), ("vcache", vcache)):
+        if isinstance(t, torch.Tensor) and t.dtype in cache_dtypes:
+            _check(t, name, t.dtype, 4, dev)
+        else:
+            _check(t, name, cache_dtypes[0], 4, dev)
     _check(o, "o", torch.bfloat16, 3, dev)
     _check(seqlens, "seqlens", torch.int32, 1, dev)
     B, Hq, d = q.shape
@@ -231,12 +233,45 @@ def attn_fwd_decode(q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen:
         if workspace.device != dev or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous tensor on q's device")
         ws_bytes = workspace.numel() * workspace.element_size()
+    return B, Hq, Hkv, d, max_blocks, num_pages, ws_bytes
+
+
+def attn_fwd_decode(q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen: int,
+                    scale: float, num_splits: int = 0, workspace=None, page_size: int = 16,
+                    num_pages: int | None = None, stream=None) -> None:
+    """q/o [B,Hq,d] bf16; lse [B,Hq] fp32 or None; seqlens int32 [B] (device).
+    block_table None: caches [B,Hkv,max_seqlen,d]; else caches [num_pages,Hkv,16,d] and
+    block_table int32 [B, max_blocks]."""
+    lib = load_library()
+    B, Hq, Hkv, d, max_blocks, num_pages, ws_bytes = _decode_args(
+        q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen, workspace, page_size,
+        num_pages, (torch.bfloat16,))
     st = lib.attn_fwd_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(block_table),
                              _ptr(seqlens), _ptr(o), _ptr(lse), B, Hq, Hkv, d, int(max_seqlen),
                              int(page_size), int(max_blocks), int(num_pages), float(scale),
                              int(num_splits), _ptr(workspace), ws_bytes, _stream_handle(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_decode")
+
+
+def attn_fwd_decode_fp8(q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen: int,
+                        scale: float, k_scale: float, v_scale: float, num_splits: int = 0,
+                        workspace=None, page_size: int = 16, num_pages: int | None = None,
+                        stream=None) -> None:
+    """attn_fwd_decode over an FP8 cache: kcache/vcache hold OCP E4M3 codes (torch.uint8
+    or torch.float8_e4m3fn) standing for k_scale * e4m3(code) and v_scale * e4m3(code)."""
+    lib = load_library()
+    B, Hq, Hkv, d, max_blocks, num_pages, ws_bytes = _decode_args(
+        q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen, workspace, page_size,
+        num_pages, (torch.uint8, torch.float8_e4m3fn))
+    st = lib.attn_fwd_decode_fp8(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(block_table),
+                                 _ptr(seqlens), _ptr(o), _ptr(lse), B, Hq, Hkv, d,
+                                 int(max_seqlen), int(page_size), int(max_blocks),
+                                 int(num_pages), float(scale), float(k_scale), float(v_scale),
+                                 int(num_splits), _ptr(workspace), ws_bytes,
+                                 _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_decode_fp8")
 
 
 def decode_workspace(B, Hq, Hkv, d, max_seqlen, num_splits=0, device="cuda"):
@@ -260,6 +295,24 @@ def decode(q, kcache, vcache, seqlens, max_seqlen: int, block_table=None,
     return o, lse
 
 
-__all__ = ["attn_fwd_prefill", "attn_fwd_decode", "attn_decode_workspace_bytes",
+def decode_fp8(q, kcache, vcache, seqlens, max_seqlen: int, k_scale: float, v_scale: float,
+               block_table=None, scale: float | None = None, num_splits: int = 0,
+               workspace=None):
+    """Allocate O, LSE (and the workspace when not given) and run attn_fwd_decode_fp8."""
+    B, Hq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, kcache.shape[1], d, max_seqlen, num_splits, q.device)
+    attn_fwd_decode_fp8(q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen, scale,
+                        k_scale, v_scale, num_splits, workspace)
+    return o, lse
+
+
+__all__ = ["attn_fwd_prefill", "attn_fwd_decode", "attn_fwd_decode_fp8",
+           "attn_decode_workspace_bytes", "decode_fp8",
            "attn_decode_num_splits", "attn_status_string", "prefill", "decode",
+           "attn_fwd_prefill_paged", "prefill_paged",
            "decode_workspace", "load_library", "AttnError", "LIB_PATH"]

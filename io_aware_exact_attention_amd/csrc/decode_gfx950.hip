@@ -12,6 +12,13 @@
 // LSE; otherwise it writes its chunk's normalised fp32 output and log-sum-exp, and the
 // merge kernel combines the chunks of a row by log-sum-exp.
 //
+// FP8 cache (F8): K and V hold OCP E4M3 codes with one scale per tensor.  A block is read
+// with the same 16-byte buffer loads (half as many) and each code is widened to bf16 in
+// registers before the LDS store, which is exact, so the LDS and MFMA path is the bf16
+// one.  The K scale is folded into the exponent scale c by the host; the V scale
+// multiplies the normalised output.  Compressed (FP8) KV caches: page "메모리 장벽을
+// 넘어" (tiptinker), section "2. FlashInfer".
+//
 // Method: decode as a single query against the growing K/V cache, paged KV caches and a
 // decode kernel separate from prefill: page "메모리 장벽을 넘어: LLM 연산자 가속 라이브러리
 // 심층 분석" (tiptinker), section "2. FlashInfer".  The online softmax is the one of the
@@ -37,10 +44,24 @@ struct DecodeShape {
   static_assert(RED <= LDS, "reduction scratch fits in the staging LDS");
 };
 
-template <int D, bool PAGED>
+// Four E4M3 codes (byte k of x is code k) as four bf16, code k in element k:
+// v_cvt_scalef32_pk_bf16_fp8 with unit scale on the low, then the high code pair.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t x) {
+  const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
+  const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true);
+  return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
+#ifndef MIATTN_DECODE_SETS_F8
+#define MIATTN_DECODE_SETS_F8 3
+#endif
+constexpr int kDecodeSetsF8 = MIATTN_DECODE_SETS_F8;  // FP8 blocks in flight per wave
+
+template <int D, bool PAGED, bool F8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_split_kernel(DecodeParams a) {
   using S = DecodeShape<D>;
+  constexpr int EB = F8 ? 1 : 2;  // bytes per cached element
   constexpr int NH = kDecodeHeadsPerGroup;
   __shared__ __attribute__((aligned(16))) char smem[S::LDS];
 
@@ -91,40 +112,58 @@ void decode_split_kernel(DecodeParams a) {
     }
   }
 
-  const uint16_t* kbase_c = a.kc + ((size_t)b * a.Hkv + kvh) * a.max_seqlen * D;
-  const uint16_t* vbase_c = a.vc + ((size_t)b * a.Hkv + kvh) * a.max_seqlen * D;
+  const char* kbase_c = (const char*)a.kc + ((size_t)b * a.Hkv + kvh) * a.max_seqlen * D * EB;
+  const char* vbase_c = (const char*)a.vc + ((size_t)b * a.Hkv + kvh) * a.max_seqlen * D * EB;
   const int32_t* table = PAGED ? a.block_table + (size_t)b * a.max_blocks : nullptr;
 
-  // Page ids of a 32-key block starting at tb (two 16-token pages, wave-uniform, so
-  // scalar loads).  They are fetched well ahead of the K/V loads that use them.
-  auto block_pages = [&](int tb, int& p0, int& p1) {
-    if (PAGED && tb < t1) {
-      p0 = table[tb >> 4];
-      p1 = tb + 16 < t1 ? table[(tb >> 4) + 1] : p0;
+  // The wave takes the chunk's 32-key blocks wave, wave + W, wave + 2W, ...; block i
+  // starts at key tbk(i).
+  constexpr int W = kDecodeWaves;
+  auto tbk = [&](int i) { return t0 + S::BLK * i; };
+
+  // Page ids of the wave's blocks come from one vector load per window of 32 blocks:
+  // lane 2*j + h holds the page of 16-token group h of the window's j-th block (0 past
+  // the chunk end).  A block's two ids are then read with v_readlane, which keeps page
+  // lookups out of the scalar-load counter that every LDS wait also drains.
+  int pg_lane = 0;
+  int pg_win = -1;
+  auto block_pages = [&](int i, int& p0, int& p1) {
+    if (PAGED) {
+      const int j = (i - wave) / W;  // the wave's j-th block (i = wave + W*j)
+      if ((j >> 5) != pg_win) {
+        pg_win = j >> 5;
+        const int tg = tbk(wave + W * (32 * pg_win + (lane >> 1))) + 16 * (lane & 1);
+        pg_lane = tg < t1 ? table[tg >> 4] : 0;
+      }
+      p0 = __builtin_amdgcn_readlane(pg_lane, 2 * (j & 31));
+      p1 = __builtin_amdgcn_readlane(pg_lane, 2 * (j & 31) + 1);
     }
   };
   // One 32-key block = two 16-token groups (a page of the paged cache, 16 consecutive
   // rows of the contiguous one).  Each group is read through a buffer descriptor whose
   // range ends at the chunk's last key, so rows past it read as zeros.  Lane l owns the
-  // 16-byte chunks l + 64*i of the block: offset 16*l + 1024*(i mod CPL/2) within group
-  // i / (CPL/2).
-  constexpr int HALF = S::CPL / 2;
-  auto load_block = [&](u32x4 (&kr)[S::CPL], u32x4 (&vr)[S::CPL], int tb, int p0, int p1) {
+  // 16-byte chunks l + 64*i of the block: offset 16*l + 1024*(i mod LC/2) within group
+  // i / (LC/2).  LC, the loaded chunks per lane and tensor, is half as large for codes.
+  constexpr int LC = F8 ? S::CPL / 2 : S::CPL;
+  constexpr int HALF = LC / 2;
+  auto load_block = [&](u32x4 (&kr)[LC], u32x4 (&vr)[LC], int tb, int p0, int p1) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int tg = tb + 16 * h;
       const int rows = max(0, min(16, t1 - tg));
-      const uint16_t* kg;
-      const uint16_t* vg;
+      const char* kg;
+      const char* vg;
       if (PAGED) {
-        const size_t off = ((size_t)(h ? p1 : p0) * a.Hkv + kvh) * 16 * D;
-        kg = a.kc + off;
-        vg = a.vc + off;
+        const size_t off = ((size_t)(h ? p1 : p0) * a.Hkv + kvh) * 16 * D * EB;
+        kg = (const char*)a.kc + off;
+        vg = (const char*)a.vc + off;
       } else {
-        kg = kbase_c + (size_t)tg * D;
-        vg = vbase_c + (size_t)tg * D;
+        kg = kbase_c + (size_t)tg * D * EB;
+        vg = vbase_c + (size_t)tg * D * EB;
       }
-      const int nbytes = rows * D * 2;
+      // wave-uniform by construction; readfirstlane keeps it in an SGPR so the descriptor
+      // is scalar (a descriptor the compiler sees in VGPRs costs a loop per load)
+      const int nbytes = __builtin_amdgcn_readfirstlane(rows * D * EB);
 #pragma unroll
       for (int i = 0; i < HALF; ++i) {
         kr[h * HALF + i] = buffer_load16(kg, nbytes, lane * 16 + 1024 * i);
@@ -139,11 +178,27 @@ void decode_split_kernel(DecodeParams a) {
   constexpr int RPI = 64 / (D / 8);
   char* kst = kls + (lane / (D / 8)) * S::KSTR + (lane % (D / 8)) * 16;
   char* vst = vls + (lane / (D / 8)) * S::VSTR + (lane % (D / 8)) * 16;
-  auto store_block = [&](const u32x4 (&kr)[S::CPL], const u32x4 (&vr)[S::CPL]) {
+  // codes: chunk l + 64*i is row l/(D/16) + i*RPI8, codes 16*(l%(D/16)) .. +15, which
+  // widen to the two bf16 chunks 2*(l%(D/16)) and 2*(l%(D/16)) + 1 of that row
+  constexpr int RPI8 = 64 / (D / 16);
+  char* kst8 = kls + (lane / (D / 16)) * S::KSTR + (lane % (D / 16)) * 32;
+  char* vst8 = vls + (lane / (D / 16)) * S::VSTR + (lane % (D / 16)) * 32;
+  auto widen_store = [&](char* dst, const u32x4& w) {
+    const u32x2 c0 = e4m3x4_to_bf16x4(w[0]), c1 = e4m3x4_to_bf16x4(w[1]);
+    const u32x2 c2 = e4m3x4_to_bf16x4(w[2]), c3 = e4m3x4_to_bf16x4(w[3]);
+    *(u32x4*)dst = u32x4{c0[0], c0[1], c1[0], c1[1]};
+    *(u32x4*)(dst + 16) = u32x4{c2[0], c2[1], c3[0], c3[1]};
+  };
+  auto store_block = [&](const u32x4 (&kr)[LC], const u32x4 (&vr)[LC]) {
 #pragma unroll
-    for (int i = 0; i < S::CPL; ++i) {
-      *(u32x4*)(kst + i * RPI * S::KSTR) = kr[i];
-      *(u32x4*)(vst + i * RPI * S::VSTR) = vr[i];
+    for (int i = 0; i < LC; ++i) {
+      if (F8) {
+        widen_store(kst8 + i * RPI8 * S::KSTR, kr[i]);
+        widen_store(vst8 + i * RPI8 * S::VSTR, vr[i]);
+      } else {
+        *(u32x4*)(kst + i * RPI * S::KSTR) = kr[i];
+        *(u32x4*)(vst + i * RPI * S::VSTR) = vr[i];
+      }
     }
   };
 
@@ -229,36 +284,34 @@ void decode_split_kernel(DecodeParams a) {
     }
   };
 
-  // The wave takes blocks wave, wave + W, wave + 2W, ... with two blocks in flight: while
-  // one is consumed, the next two are loading into registers (sets A and B alternate).
-  constexpr int W = kDecodeWaves;
-  auto tbk = [&](int i) { return t0 + S::BLK * i; };
-  u32x4 kA[S::CPL], vA[S::CPL], kB[S::CPL], vB[S::CPL];
+  // The wave takes blocks wave, wave + W, wave + 2W, ... with NS blocks in flight: while
+  // one is consumed, the next NS are loading into registers (the NS register sets rotate).
+  // Codes take half the registers of bf16, so the FP8 instance keeps more blocks in flight.
+  constexpr int NS = F8 ? kDecodeSetsF8 : 2;
+  u32x4 kr[NS][LC], vr[NS][LC];
   int bi = wave;
-  int pa0 = 0, pa1 = 0, pb0 = 0, pb1 = 0, pn0 = 0, pn1 = 0;
-  block_pages(tbk(bi), pa0, pa1);
-  block_pages(tbk(bi + W), pb0, pb1);
-  if (bi < nblk) load_block(kA, vA, tbk(bi), pa0, pa1);
-  if (bi + W < nblk) load_block(kB, vB, tbk(bi + W), pb0, pb1);
-  block_pages(tbk(bi + 2 * W), pn0, pn1);  // pages of the next block to load
-  while (bi < nblk) {
-    store_block(kA, vA);
-    wave_sync();
-    if (bi + 2 * W < nblk) load_block(kA, vA, tbk(bi + 2 * W), pn0, pn1);
-    block_pages(tbk(bi + 3 * W), pn0, pn1);
-    compute(tbk(bi));
-    wave_sync();
-    bi += W;
-    if (bi >= nblk) break;
-    store_block(kB, vB);
-    wave_sync();
-    if (bi + 2 * W < nblk) load_block(kB, vB, tbk(bi + 2 * W), pn0, pn1);
-    block_pages(tbk(bi + 3 * W), pn0, pn1);
-    compute(tbk(bi));
-    wave_sync();
-    bi += W;
+  int pn0 = 0, pn1 = 0;  // pages of the next block to load
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    block_pages(bi + s * W, pn0, pn1);
+    if (bi + s * W < nblk) load_block(kr[s], vr[s], tbk(bi + s * W), pn0, pn1);
+  }
+  block_pages(bi + NS * W, pn0, pn1);
+  for (;;) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (bi >= nblk) goto merge;
+      store_block(kr[s], vr[s]);
+      wave_sync();
+      if (bi + NS * W < nblk) load_block(kr[s], vr[s], tbk(bi + NS * W), pn0, pn1);
+      block_pages(bi + (NS + 1) * W, pn0, pn1);
+      compute(tbk(bi));
+      wave_sync();
+      bi += W;
+    }
   }
 
+merge:
   // ---- merge the four waves' states (LDS reused as fp32 scratch)
   float l_col = l_run + wave_xor(l_run, 16);
   l_col += wave_xor(l_col, 32);
@@ -295,7 +348,7 @@ void decode_split_kernel(DecodeParams a) {
       Esum += al * red_e[w * NH + h];
       acc += al * red_o[(w * NH + h) * D + dv];
     }
-    const float out = acc / Lsum;
+    const float out = F8 ? acc / Lsum * a.v_scale : acc / Lsum;
     const float lse_nat = (M * c + log2f(Esum)) * kLn2;
     const size_t row = (size_t)b * a.Hq + kvh * a.G + grp * NH + h;
     if (a.num_splits == 1) {
@@ -360,13 +413,13 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
   }
 }
 
-template <int D>
+template <int D, bool F8>
 static hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid(p.num_splits, p.Hkv * p.ngroups, p.B);
   if (p.block_table)
-    hipLaunchKernelGGL((decode_split_kernel<D, true>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_split_kernel<D, true, F8>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_split_kernel<D, false>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_split_kernel<D, false, F8>), grid, dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.num_splits == 1) return e;
   const int rows = p.B * p.Hq;
@@ -375,7 +428,8 @@ static hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t stream) {
-  return d == 64 ? launch_d<64>(p, stream) : launch_d<128>(p, stream);
+  if (p.kv_fp8) return d == 64 ? launch_d<64, true>(p, stream) : launch_d<128, true>(p, stream);
+  return d == 64 ? launch_d<64, false>(p, stream) : launch_d<128, false>(p, stream);
 }
 
 }  // namespace miattn

@@ -28,8 +28,8 @@ struct PrefillParams {
 
 struct DecodeParams {
   const uint16_t* q;
-  const uint16_t* kc;
-  const uint16_t* vc;
+  const void* kc;  // bf16, or E4M3 codes when kv_fp8
+  const void* vc;
   const int32_t* block_table;  // null: contiguous cache
   const int32_t* seqlens;
   uint16_t* o;
@@ -40,8 +40,10 @@ struct DecodeParams {
   int max_seqlen;  // row count of the contiguous cache
   int max_blocks;  // block-table row length (paged)
   int num_splits, chunk;
-  float c;
+  float c;        // |scale| * log2(e), times the K scale of an FP8 cache
   int negate_q;
+  int kv_fp8;     // K/V caches hold E4M3 codes
+  float v_scale;  // FP8 cache: multiplies the normalised output
 };
 
 // Query heads sharing one KV head that a decode workgroup serves at once.

@@ -66,6 +66,63 @@ size_t workspace_for(int B, int Hq, int d, const Plan& pl) {
   return (bytes + 255) / 256 * 256;
 }
 
+// Both decode entry points: the cache element type (bf16 or E4M3 codes) changes the
+// kernel instance, the exponent scale (times k_scale) and the output scale (v_scale).
+int decode_impl(const void* q, const void* kcache, const void* vcache,
+                const int32_t* block_table, const int32_t* seqlens, void* o, float* lse, int B,
+                int Hq, int Hkv, int d, int max_seqlen, int page_size, int max_blocks_per_seq,
+                int num_pages, float scale, bool fp8, float k_scale, float v_scale,
+                int num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !kcache || !vcache || !seqlens || !o) return ATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(kcache, 16) || !aligned(vcache, 16) || !aligned(o, 16) ||
+      !aligned(seqlens, 4))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (lse && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (!decode_sizes_ok(B, Hq, Hkv, d, max_seqlen) || d < 1) return ATTN_ERR_INVALID_ARGUMENT;
+  if (num_splits < 0 || !std::isfinite(scale)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (block_table) {
+    if (!aligned(block_table, 4) || num_pages < 1) return ATTN_ERR_INVALID_ARGUMENT;
+    if (page_size != 16) return ATTN_ERR_UNSUPPORTED;
+    if (max_blocks_per_seq < (max_seqlen + page_size - 1) / page_size)
+      return ATTN_ERR_INVALID_ARGUMENT;
+  }
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  const int G = Hq / Hkv;
+  const int ngroups = (G + miattn::kDecodeHeadsPerGroup - 1) / miattn::kDecodeHeadsPerGroup;
+  if (B > 65535 || (long)Hkv * ngroups > 65535 || (long)B * Hq > 0x7fffffffL)
+    return ATTN_ERR_UNSUPPORTED;
+
+  const Plan pl = plan_decode(B, Hq, Hkv, max_seqlen, num_splits);
+  const size_t need = workspace_for(B, Hq, d, pl);
+  if (need) {
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return ATTN_ERR_WORKSPACE;
+  }
+
+  miattn::DecodeParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.kc = kcache;
+  p.vc = vcache;
+  p.block_table = block_table;
+  p.seqlens = seqlens;
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.ws_o = need ? static_cast<float*>(workspace) : nullptr;
+  p.ws_lse = need ? p.ws_o + (size_t)B * Hq * pl.splits * d : nullptr;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = G; p.ngroups = ngroups;
+  p.max_seqlen = max_seqlen;
+  p.max_blocks = block_table ? max_blocks_per_seq : 0;
+  p.num_splits = pl.splits;
+  p.chunk = pl.chunk;
+  p.c = std::fabs(scale) * 1.4426950408889634f;
+  if (fp8) p.c *= k_scale;
+  if (!std::isfinite(p.c)) return ATTN_ERR_INVALID_ARGUMENT;
+  p.negate_q = scale < 0.f;
+  p.kv_fp8 = fp8;
+  p.v_scale = v_scale;
+  (void)hipGetLastError();
+  return miattn::launch_decode(p, d, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -165,50 +222,23 @@ int attn_fwd_decode(const void* q, const void* kcache, const void* vcache,
                     int B, int Hq, int Hkv, int d, int max_seqlen, int page_size,
                     int max_blocks_per_seq, int num_pages, float scale, int num_splits,
                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!q || !kcache || !vcache || !seqlens || !o) return ATTN_ERR_INVALID_ARGUMENT;
-  if (!aligned(q, 16) || !aligned(kcache, 16) || !aligned(vcache, 16) || !aligned(o, 16) ||
-      !aligned(seqlens, 4))
+  return decode_impl(q, kcache, vcache, block_table, seqlens, o, lse, B, Hq, Hkv, d, max_seqlen,
+                     page_size, max_blocks_per_seq, num_pages, scale, false, 1.f, 1.f,
+                     num_splits, workspace, workspace_bytes, stream);
+}
+
+int attn_fwd_decode_fp8(const void* q, const void* kcache, const void* vcache,
+                        const int32_t* block_table, const int32_t* seqlens, void* o,
+                        float* lse, int B, int Hq, int Hkv, int d, int max_seqlen,
+                        int page_size, int max_blocks_per_seq, int num_pages, float scale,
+                        float k_scale, float v_scale, int num_splits, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || !(k_scale > 0.f) ||
+      !(v_scale > 0.f))
     return ATTN_ERR_INVALID_ARGUMENT;
-  if (lse && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARGUMENT;
-  if (!decode_sizes_ok(B, Hq, Hkv, d, max_seqlen) || d < 1) return ATTN_ERR_INVALID_ARGUMENT;
-  if (num_splits < 0 || !std::isfinite(scale)) return ATTN_ERR_INVALID_ARGUMENT;
-  if (block_table) {
-    if (!aligned(block_table, 4) || num_pages < 1) return ATTN_ERR_INVALID_ARGUMENT;
-    if (page_size != 16) return ATTN_ERR_UNSUPPORTED;
-    if (max_blocks_per_seq < (max_seqlen + page_size - 1) / page_size)
-      return ATTN_ERR_INVALID_ARGUMENT;
-  }
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  const int G = Hq / Hkv;
-  const int ngroups = (G + miattn::kDecodeHeadsPerGroup - 1) / miattn::kDecodeHeadsPerGroup;
-  if (B > 65535 || (long)Hkv * ngroups > 65535 || (long)B * Hq > 0x7fffffffL)
-    return ATTN_ERR_UNSUPPORTED;
-
-  const Plan pl = plan_decode(B, Hq, Hkv, max_seqlen, num_splits);
-  const size_t need = workspace_for(B, Hq, d, pl);
-  if (need) {
-    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return ATTN_ERR_WORKSPACE;
-  }
-
-  miattn::DecodeParams p{};
-  p.q = static_cast<const uint16_t*>(q);
-  p.kc = static_cast<const uint16_t*>(kcache);
-  p.vc = static_cast<const uint16_t*>(vcache);
-  p.block_table = block_table;
-  p.seqlens = seqlens;
-  p.o = static_cast<uint16_t*>(o);
-  p.lse = lse;
-  p.ws_o = need ? static_cast<float*>(workspace) : nullptr;
-  p.ws_lse = need ? p.ws_o + (size_t)B * Hq * pl.splits * d : nullptr;
-  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = G; p.ngroups = ngroups;
-  p.max_seqlen = max_seqlen;
-  p.max_blocks = block_table ? max_blocks_per_seq : 0;
-  p.num_splits = pl.splits;
-  p.chunk = pl.chunk;
-  p.c = std::fabs(scale) * 1.4426950408889634f;
-  p.negate_q = scale < 0.f;
-  (void)hipGetLastError();
-  return miattn::launch_decode(p, d, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  return decode_impl(q, kcache, vcache, block_table, seqlens, o, lse, B, Hq, Hkv, d, max_seqlen,
+                     page_size, max_blocks_per_seq, num_pages, scale, true, k_scale, v_scale,
+                     num_splits, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

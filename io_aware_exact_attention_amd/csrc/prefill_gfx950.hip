@@ -254,11 +254,12 @@ void prefill_kernel(PrefillParams a) {
       for (int i = 0; i < S::DMA; ++i) {
         const int blk = i * S::kWaves + wave;
         const int tok0 = n0 + blk * RPB;
-        const int rows = max(0, min(RPB, nk - tok0));
+        // wave-uniform; readfirstlane keeps the byte count, and so the descriptor, scalar
+        const int nbytes = __builtin_amdgcn_readfirstlane(max(0, min(RPB, nk - tok0)) * S::ROWB);
         const size_t off = ((size_t)pg[i] * a.Hkv + kvh) * 16 * D + (size_t)(tok0 & 15) * D;
         const uint32_t lo = dma_off[i] - blk * 1024;  // offset within the block
-        lds_dma16(Kh + off, rows * S::ROWB, lo, (lds_void*)(st + blk * 1024));
-        lds_dma16(Vh + off, rows * S::ROWB, lo, (lds_void*)(st + S::TILE + blk * 1024));
+        lds_dma16(Kh + off, nbytes, lo, (lds_void*)(st + blk * 1024));
+        lds_dma16(Vh + off, nbytes, lo, (lds_void*)(st + S::TILE + blk * 1024));
       }
     } else {
       const int nbytes = (nk - n0) * (D * 2);

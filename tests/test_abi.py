@@ -30,7 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["attn_fwd_prefill", "attn_fwd_prefill_paged",
-                                           "attn_fwd_decode", "attn_decode_workspace_bytes",
+                                           "attn_fwd_decode", "attn_fwd_decode_fp8",
+                                           "attn_decode_workspace_bytes",
                                            "attn_decode_num_splits", "attn_status_string"])
 
 
@@ -112,6 +113,33 @@ def decode(lib, q=P, kc=P, vc=P, table=None, seqlens=P, o=P, lse=None, B=2, Hq=8
 ])
 def test_decode_validation(lib, kw, status):
     assert decode(lib, **kw) == status
+
+
+def decode_fp8(lib, k_scale=0.02, v_scale=0.03, **kw):
+    a = dict(q=P, kc=P, vc=P, table=None, seqlens=P, o=P, lse=None, B=2, Hq=8, Hkv=2, d=128,
+             max_seqlen=100, page_size=16, max_blocks=7, num_pages=10, scale=0.1, splits=1,
+             ws=None, ws_bytes=0)
+    a.update(kw)
+    return lib.attn_fwd_decode_fp8(a["q"], a["kc"], a["vc"], a["table"], a["seqlens"], a["o"],
+                                   a["lse"], a["B"], a["Hq"], a["Hkv"], a["d"], a["max_seqlen"],
+                                   a["page_size"], a["max_blocks"], a["num_pages"],
+                                   ctypes.c_float(a["scale"]), ctypes.c_float(k_scale),
+                                   ctypes.c_float(v_scale), a["splits"], a["ws"], a["ws_bytes"],
+                                   None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k_scale=0.0), INVALID), (dict(k_scale=-0.5), INVALID),
+    (dict(v_scale=0.0), INVALID), (dict(v_scale=-1.0), INVALID),
+    (dict(k_scale=float("nan")), INVALID), (dict(v_scale=float("inf")), INVALID),
+    (dict(scale=1e30, k_scale=1e30), INVALID),          # |scale| * k_scale overflows
+    # every check of attn_fwd_decode applies as well
+    (dict(kc=None), INVALID), (dict(vc=MIS), INVALID), (dict(Hq=6, Hkv=4), INVALID),
+    (dict(d=80), UNSUPPORTED), (dict(table=P, page_size=8), UNSUPPORTED),
+    (dict(table=P, max_blocks=6), INVALID), (dict(max_seqlen=4096, splits=4), WORKSPACE),
+])
+def test_decode_fp8_validation(lib, kw, status):
+    assert decode_fp8(lib, **kw) == status
 
 
 def test_decode_split_plan(lib):

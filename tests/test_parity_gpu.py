@@ -16,8 +16,8 @@ import torch
 
 import attn_inputs as ai
 import io_aware_exact_attention_amd as mi
-from oracle import (attention_decode, attention_prefill, attention_prefill_paged,
-                    attention_rows, gather_paged)
+from oracle import (attention_decode, attention_decode_fp8, attention_prefill,
+                    attention_prefill_paged, attention_rows, gather_paged)
 
 pytestmark = pytest.mark.gpu
 
@@ -215,8 +215,8 @@ def test_prefill_long_context_32k():
 
 
 # ------------------------------------------------------------------ decode
-def make_decode(B, Hq, Hkv, d, lens, seed, paged, extra_pages=3):
-    cfg = ai.DecodeCfg("case", B=B, Hq=Hq, Hkv=Hkv, d=d, seed=seed, paged=paged)
+def make_decode(B, Hq, Hkv, d, lens, seed, paged, extra_pages=3, fp8=False):
+    cfg = ai.DecodeCfg("case", B=B, Hq=Hq, Hkv=Hkv, d=d, seed=seed, paged=paged, kv_fp8=fp8)
     lens = np.asarray(lens, np.int32)
     q = ai.decode_q(cfg)
     maxlen = max(int(lens.max()), 1)
@@ -323,6 +323,112 @@ def test_decode_paged_config():
     o, lse = run_decode(q, kp, vp, lens, lay.block_table, maxlen, cfg.scale)
     ro, rl = decode_ref(q, kp, vp, lens, lay.block_table, cfg.scale)
     check("paged_gqa_decode", o, lse, ro, rl)
+
+
+# ------------------------------------------------------------------ decode over an FP8 cache
+def run_decode_fp8(q, kc, vc, lens, table, maxlen, scale, k_scale=ai.FP8_K_SCALE,
+                   v_scale=ai.FP8_V_SCALE, num_splits=0):
+    o, lse = mi.decode_fp8(dev(q).reshape(q.shape), torch.from_numpy(kc).cuda(),
+                           torch.from_numpy(vc).cuda(), torch.from_numpy(lens).cuda(), maxlen,
+                           k_scale, v_scale,
+                           block_table=None if table is None else torch.from_numpy(table).cuda(),
+                           scale=scale, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def decode_fp8_ref(q, kc, vc, lens, table, scale, k_scale=ai.FP8_K_SCALE,
+                   v_scale=ai.FP8_V_SCALE):
+    return attention_decode_fp8(f64(q), kc, vc, lens, scale, k_scale, v_scale, table, 16)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("splits", [1, 0, 3])
+def test_decode_fp8_edge_lengths(paged, d, splits):
+    lens = [0, 1, 15, 16, 17, 31, 33, 1000]
+    cfg, q, kc, vc, lens, table, maxlen = make_decode(8, 8, 2, d, lens, 1600 + d, paged, fp8=True)
+    assert kc.dtype == np.uint8
+    o, lse = run_decode_fp8(q, kc, vc, lens, table, maxlen, cfg.scale, num_splits=splits)
+    ro, rl = decode_fp8_ref(q, kc, vc, lens, table, cfg.scale)
+    check(f"decode fp8 edge paged={paged} d={d} splits={splits}", o, lse, ro, rl)
+    assert (o[0] == 0).all() and torch.isinf(lse[0]).all()
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(32, 1), (10, 2)])
+def test_decode_fp8_group_sizes(Hq, Hkv):
+    cfg, q, kc, vc, lens, table, maxlen = make_decode(3, Hq, Hkv, 128, [300, 77, 1], 1700 + Hq,
+                                                      True, fp8=True)
+    o, lse = run_decode_fp8(q, kc, vc, lens, table, maxlen, cfg.scale, num_splits=2)
+    ro, rl = decode_fp8_ref(q, kc, vc, lens, table, cfg.scale)
+    check(f"decode fp8 Hq={Hq} Hkv={Hkv}", o, lse, ro, rl)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_decode_fp8_unit_scales_equal_bf16_decode_of_widened_cache(paged):
+    """With unit scales the FP8 path must give the bf16 path's bits on the bf16 widening of
+    the same codes (E4M3 values are exact in bf16), which pins the widening and its byte
+    order; every code except the two NaNs occurs in the random cache."""
+    cfg, q, kc, vc, lens, table, maxlen = make_decode(4, 16, 4, 128, [700, 64, 1, 2100], 1800,
+                                                      paged, fp8=True)
+    rng = np.random.default_rng(5)
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    live = kc != 0x7F
+    kc = np.where(live, rng.choice(codes, kc.shape), kc).astype(np.uint8)
+    vc = np.where(live, rng.choice(codes, vc.shape), vc).astype(np.uint8)
+    widen = lambda c: torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.bfloat16).cuda()
+    for s in (1, 0, 7):
+        o8, l8 = run_decode_fp8(q, kc, vc, lens, table, maxlen, 0.01, 1.0, 1.0, s)
+        ob, lb = mi.decode(dev(q).reshape(q.shape), widen(kc), widen(vc),
+                           torch.from_numpy(lens).cuda(), maxlen,
+                           block_table=None if table is None else torch.from_numpy(table).cuda(),
+                           scale=0.01, num_splits=s)
+        torch.cuda.synchronize()
+        assert torch.equal(o8, ob) and torch.equal(l8, lb), f"fp8 != bf16 widening at splits={s}"
+    ro, rl = decode_fp8_ref(q, kc, vc, lens, table, 0.01, 1.0, 1.0)
+    # the bar is set for V of order one; these codes reach 448, so O and the reference are
+    # divided by 128 (exact) first
+    check(f"decode fp8 unit scales paged={paged}", o8.float() / 128, l8, ro / 128, rl)
+
+
+@pytest.mark.parametrize("scale,k_scale,v_scale", [(-0.09, 0.02, 0.5), (0.2, 3.0, 0.001),
+                                                   (0.0884, 2.0 ** -7, 2.0 ** 5)])
+def test_decode_fp8_scale_values(scale, k_scale, v_scale):
+    cfg, q, kc, vc, lens, table, maxlen = make_decode(2, 8, 2, 64, [513, 40], 1900, True,
+                                                      fp8=True)
+    o, lse = run_decode_fp8(q, kc, vc, lens, table, maxlen, scale, k_scale, v_scale)
+    ro, rl = decode_fp8_ref(q, kc, vc, lens, table, scale, k_scale, v_scale)
+    # V = v_scale * codes, where the codes are N(0,1) draws / FP8_V_SCALE: outputs and their
+    # errors scale with v_scale / FP8_V_SCALE, which the bar (set for V of order one) divides out
+    norm = v_scale / ai.FP8_V_SCALE
+    check(f"decode fp8 scale={scale} ks={k_scale} vs={v_scale}", o.float() / norm, lse,
+          ro / norm, rl)
+
+
+def test_decode_fp8_paged_equals_contiguous():
+    lens = [5000, 2048, 333, 4097]
+    cfgc, q, kc, vc, lens_, _, maxlen = make_decode(4, 16, 4, 128, lens, 1950, False, fp8=True)
+    _, q2, kp, vp, _, table, _ = make_decode(4, 16, 4, 128, lens, 1950, True, fp8=True)
+    assert (q == q2).all()
+    ref = decode_fp8_ref(q, kc, vc, lens_, None, cfgc.scale)
+    for s in (0, 5):
+        oc, lc = run_decode_fp8(q, kc, vc, lens_, None, maxlen, cfgc.scale, num_splits=s)
+        op, lp = run_decode_fp8(q, kp, vp, lens_, table, maxlen, cfgc.scale, num_splits=s)
+        assert torch.equal(oc, op) and torch.equal(lc, lp), f"paged != contiguous at splits={s}"
+        check(f"decode fp8 splits={s}", oc, lc, *ref)
+
+
+def test_decode_fp8_paged_config():
+    cfg = ai.CONFIGS["paged_gqa_decode_fp8"]
+    lens = ai.decode_lengths(cfg)
+    lay = ai.paged_layout(lens, cfg.page_size, cfg.seed)
+    q = ai.decode_q(cfg)
+    kp = ai.build_paged_cache(cfg, ai.T_K, lens, lay)
+    vp = ai.build_paged_cache(cfg, ai.T_V, lens, lay)
+    maxlen = int(lens.max())
+    o, lse = run_decode_fp8(q, kp, vp, lens, lay.block_table, maxlen, cfg.scale)
+    ro, rl = decode_fp8_ref(q, kp, vp, lens, lay.block_table, cfg.scale)
+    check("paged_gqa_decode_fp8", o, lse, ro, rl)
 
 
 # ------------------------------------------------------------------ chunked prefill, paged cache
