@@ -49,6 +49,10 @@ def parse():
                    help="skip the other workloads (non-causal, 32K prefill, contiguous decode)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle sample")
+    p.add_argument("--settle-ms", type=float, default=300.0,
+                   help="after the W warmup steps, keep running untimed steps until the warmup "
+                        "has lasted this long: the GPU raises its clocks over tens of ms of "
+                        "load after an idle spell, and the timed steps should see the steady state")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="after the timed region, run one plain device copy of this many MiB "
                         "(a reference dispatch of known traffic for counter calibration)")
@@ -130,11 +134,31 @@ def decode_setup(name):
     return cfg, lens, maxlen, (dq, dkc, dvc, table, seq, o, lse)
 
 
+def settle(fn, t_start: float, settle_ms: float) -> int:
+    """Run fn (untimed) until settle_ms have passed since t_start (the start of the
+    warmup); returns the number of extra calls.  Synchronises every 8 calls so that the
+    time waited is GPU time."""
+    import torch
+    extra = 0
+    torch.cuda.synchronize()
+    while (time.perf_counter() - t_start) * 1e3 < settle_ms:
+        for _ in range(8):
+            fn()
+        extra += 8
+        torch.cuda.synchronize()
+    return extra
+
+
+SETTLE_MS = 300.0
+
+
 def time_kernel(fn, steps, warmup):
     """Average microseconds per call, from HIP events on the current stream."""
     import torch
+    t0 = time.perf_counter()
     for _ in range(warmup):
         fn()
+    settle(fn, t0, SETTLE_MS)
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ev[0].record()
@@ -223,10 +247,19 @@ def main():
         mi.attn_fwd_decode(dq, dkc, dvc, table, seq, do, dlse, maxlen, dcfg.scale, 0, ws,
                            stream=stream)
 
-    # warmup, then K timed steps (prefill + decode), each launch bracketed by events
-    for _ in range(args.warmup):
+    global SETTLE_MS
+    SETTLE_MS = args.settle_ms
+
+    def step_call():
         prefill_call()
         decode_call()
+
+    # warmup (W steps, then untimed steps until the warmup has lasted settle_ms), then K
+    # timed steps (prefill + decode), each launch bracketed by events
+    t_warm = time.perf_counter()
+    for _ in range(args.warmup):
+        step_call()
+    settle_steps = settle(step_call, t_warm, args.settle_ms)
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
     t_wall0 = time.perf_counter()
@@ -255,6 +288,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"ms": args.settle_ms, "extra_untimed_steps": settle_steps},
         "ms_per_step": round(t_wall * 1e3 / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",

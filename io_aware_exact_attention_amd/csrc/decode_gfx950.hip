@@ -52,10 +52,12 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t x) {
   return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
-#ifndef MIATTN_DECODE_SETS_F8
-#define MIATTN_DECODE_SETS_F8 3
-#endif
-constexpr int kDecodeSetsF8 = MIATTN_DECODE_SETS_F8;  // FP8 blocks in flight per wave
+constexpr int kDecodeSetsF8 = 3;  // FP8 blocks in flight per wave
+// Cache policy of the K/V loads: nt (non-temporal), the hint for data read once per step.
+// The KV cache is streamed once per decode step and nothing rereads it; with nt the
+// decode reads 6-8% faster than with the default policy (paged 5.95 vs 5.52 TB/s,
+// contiguous 6.25 vs 5.86 TB/s).
+constexpr int kKvLoadPolicy = 2;
 
 template <int D, bool PAGED, bool F8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -166,8 +168,8 @@ void decode_split_kernel(DecodeParams a) {
       const int nbytes = __builtin_amdgcn_readfirstlane(rows * D * EB);
 #pragma unroll
       for (int i = 0; i < HALF; ++i) {
-        kr[h * HALF + i] = buffer_load16(kg, nbytes, lane * 16 + 1024 * i);
-        vr[h * HALF + i] = buffer_load16(vg, nbytes, lane * 16 + 1024 * i);
+        kr[h * HALF + i] = buffer_load16<kKvLoadPolicy>(kg, nbytes, lane * 16 + 1024 * i);
+        vr[h * HALF + i] = buffer_load16<kKvLoadPolicy>(vg, nbytes, lane * 16 + 1024 * i);
       }
     }
   };

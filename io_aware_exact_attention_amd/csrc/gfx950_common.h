@@ -77,11 +77,12 @@ __device__ __forceinline__ void lds_dma16(const void* base, int nbytes, uint32_t
 }
 
 // 16-byte buffer load into registers: reads base + off (bytes) when off < nbytes, else
-// returns zeros.
+// returns zeros.  CPOL is the instruction's cache-policy field (0: default).
+template <int CPOL = 0>
 __device__ __forceinline__ u32x4 buffer_load16(const void* base, int nbytes, int off) {
   const __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, kBufferFlags);
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL));
 }
 
 __device__ __forceinline__ bf16x8 concat(bf16x4 lo, bf16x4 hi) {
