@@ -11,7 +11,8 @@ full-size workload can be regenerated on its own (the oracle checks sampled
 heads of the large workloads without drawing the whole tensor).
 
 Value recipe (all workloads): i.i.d. float32 N(0, 1) draws, optionally multiplied
-by a constant in float32, rounded to bfloat16 with round-to-nearest-even.  An FP8
+by a constant in float32, rounded to bfloat16 with round-to-nearest-even (to IEEE
+fp16, also nearest-even, for the fp16 variants: the same draws, rounded differently).  An FP8
 KV cache holds the same draws divided (in float32) by a per-tensor scale and rounded
 to OCP FP8 E4M3 codes (round-to-nearest-even, saturating at +-448); the value a code
 stands for is that scale times the code's E4M3 value.
@@ -64,6 +65,22 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return bf16_bits_to_f32(bits).astype(np.float64)
 
 
+def to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE fp16 (numpy's conversion: nearest, ties to even),
+    returned as uint16 bit patterns.  The draws stay far inside the fp16 range."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of fp16 bit patterns to float64."""
+    return np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def bits_to_f64(bits: np.ndarray, f16: bool) -> np.ndarray:
+    """Exact widening of 16-bit patterns of either element type."""
+    return f16_bits_to_f64(bits) if f16 else bf16_bits_to_f64(bits)
+
+
 def to_e4m3_codes(x: np.ndarray) -> np.ndarray:
     """Round float32 values to OCP FP8 E4M3 codes (1 sign, 4 exponent bits with bias 7,
     3 mantissa bits; no infinities), round to nearest with ties to even, magnitudes
@@ -91,12 +108,14 @@ def _stream(seed: int, tensor: int, b: int = 0, h: int = 0) -> np.random.Generat
     return np.random.default_rng(np.random.SeedSequence([seed, tensor, b, h]))
 
 
-def normal_bf16(seed: int, tensor: int, b: int, h: int, shape, mult: float = 1.0) -> np.ndarray:
-    """One head's slice: float32 N(0,1) draws (times ``mult`` in float32), rounded to bf16 bits."""
+def normal_bf16(seed: int, tensor: int, b: int, h: int, shape, mult: float = 1.0,
+                f16: bool = False) -> np.ndarray:
+    """One head's slice: float32 N(0,1) draws (times ``mult`` in float32), rounded to bf16
+    bits (to fp16 bits when ``f16``)."""
     x = _stream(seed, tensor, b, h).standard_normal(shape, dtype=np.float32)
     if mult != 1.0:
         x *= np.float32(mult)
-    return to_bf16_bits(x)
+    return to_f16_bits(x) if f16 else to_bf16_bits(x)
 
 
 def normal_e4m3(seed: int, tensor: int, b: int, h: int, shape, scale: float) -> np.ndarray:
@@ -121,6 +140,7 @@ class PrefillCfg:
     causal: bool
     seed: int
     q_mult: float = 1.0
+    f16: bool = False             # fp16 elements instead of bf16
 
     @property
     def scale(self) -> float:
@@ -142,6 +162,7 @@ class DecodeCfg:
     len_range: tuple = (0, 0)     # inclusive uniform range of lengths (paged workload)
     chunk: int = 0                # chunked prefill: new tokens (queries) per sequence
     kv_fp8: bool = False          # K/V cache as E4M3 codes with FP8_K_SCALE / FP8_V_SCALE
+    f16: bool = False             # fp16 Q and cache instead of bf16 (not with kv_fp8)
 
     @property
     def scale(self) -> float:
@@ -157,6 +178,9 @@ CONFIGS = {
                                     d=128, causal=True, seed=2),
     "llama2_7b_prefill_noncausal": PrefillCfg("llama2_7b_prefill_noncausal", B=4, Hq=32, Hkv=32,
                                               Nq=2048, Nk=2048, d=128, causal=False, seed=2),
+    # The same draws rounded to fp16 (the fp16 entry points).
+    "llama2_7b_prefill_f16": PrefillCfg("llama2_7b_prefill_f16", B=4, Hq=32, Hkv=32, Nq=2048,
+                                        Nk=2048, d=128, causal=True, seed=2, f16=True),
     # Long-context prefill, Q scaled by 3 before rounding so softmax rows are peaky.
     "long_prefill_32k": PrefillCfg("long_prefill_32k", B=1, Hq=32, Hkv=32, Nq=32768, Nk=32768,
                                    d=128, causal=True, seed=3, q_mult=3.0),
@@ -184,8 +208,8 @@ CONFIGS = {
 def prefill_head(cfg: PrefillCfg, tensor: int, b: int, h: int) -> np.ndarray:
     """bf16 bits of one head: Q [Nq, d] for tensor T_Q, K/V [Nk, d] for T_K/T_V."""
     if tensor == T_Q:
-        return normal_bf16(cfg.seed, T_Q, b, h, (cfg.Nq, cfg.d), cfg.q_mult)
-    return normal_bf16(cfg.seed, tensor, b, h, (cfg.Nk, cfg.d))
+        return normal_bf16(cfg.seed, T_Q, b, h, (cfg.Nq, cfg.d), cfg.q_mult, cfg.f16)
+    return normal_bf16(cfg.seed, tensor, b, h, (cfg.Nk, cfg.d), f16=cfg.f16)
 
 
 def prefill_inputs(cfg: PrefillCfg):
@@ -203,9 +227,9 @@ def prefill_inputs(cfg: PrefillCfg):
 
 
 def custom_prefill(seed: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int,
-                   q_mult: float = 1.0):
+                   q_mult: float = 1.0, f16: bool = False):
     """Inputs for an arbitrary prefill shape (edge cases), same recipe."""
-    cfg = PrefillCfg("custom", B, Hq, Hkv, Nq, Nk, d, True, seed, q_mult)
+    cfg = PrefillCfg("custom", B, Hq, Hkv, Nq, Nk, d, True, seed, q_mult, f16)
     return prefill_inputs(cfg)
 
 
@@ -225,7 +249,7 @@ def decode_q(cfg: DecodeCfg) -> np.ndarray:
     q = np.empty((cfg.B, cfg.Hq, cfg.d), np.uint16)
     for b in range(cfg.B):
         for h in range(cfg.Hq):
-            q[b, h] = normal_bf16(cfg.seed, T_Q, b, h, (cfg.d,))
+            q[b, h] = normal_bf16(cfg.seed, T_Q, b, h, (cfg.d,), f16=cfg.f16)
     return q
 
 
@@ -236,9 +260,14 @@ def kv_scale(cfg: DecodeCfg, tensor: int) -> float:
     return FP8_K_SCALE if tensor == T_K else FP8_V_SCALE
 
 
+F16_NAN = np.uint16(0x7E00)
+
+
 def kv_pad(cfg: DecodeCfg):
     """NaN of the cache's element type: fills slots that must never be read."""
-    return E4M3_NAN if cfg.kv_fp8 else BF16_NAN
+    if cfg.kv_fp8:
+        return E4M3_NAN
+    return F16_NAN if cfg.f16 else BF16_NAN
 
 
 def decode_kv_logical(cfg: DecodeCfg, tensor: int, b: int, kvh: int, length: int) -> np.ndarray:
@@ -246,7 +275,7 @@ def decode_kv_logical(cfg: DecodeCfg, tensor: int, b: int, kvh: int, length: int
     bf16 bits, or E4M3 codes for an FP8 cache."""
     if cfg.kv_fp8:
         return normal_e4m3(cfg.seed, tensor, b, kvh, (length, cfg.d), kv_scale(cfg, tensor))
-    return normal_bf16(cfg.seed, tensor, b, kvh, (length, cfg.d))
+    return normal_bf16(cfg.seed, tensor, b, kvh, (length, cfg.d), f16=cfg.f16)
 
 
 @dataclass
@@ -358,7 +387,7 @@ def chunk_q(cfg: DecodeCfg) -> np.ndarray:
     q = np.empty((cfg.B, cfg.Hq, cfg.chunk, cfg.d), np.uint16)
     for b in range(cfg.B):
         for h in range(cfg.Hq):
-            q[b, h] = normal_bf16(cfg.seed, T_Q, b, h, (cfg.chunk, cfg.d))
+            q[b, h] = normal_bf16(cfg.seed, T_Q, b, h, (cfg.chunk, cfg.d), f16=cfg.f16)
     return q
 
 

@@ -46,7 +46,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-extra", action="store_true",
-                   help="skip the other workloads (non-causal, 32K prefill, contiguous decode)")
+                   help="skip the other workloads (non-causal, 32K and fp16 prefill, contiguous and "
+                        "FP8-cache decode, chunked prefill)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle sample")
     p.add_argument("--settle-ms", type=float, default=300.0,
@@ -62,6 +63,12 @@ def parse():
 def to_dev(bits):
     import torch
     t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    return t.cuda()
+
+
+def to_dev16(bits):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.float16)
     return t.cuda()
 
 
@@ -100,7 +107,8 @@ def prefill_setup(name):
     import torch
     cfg = ai.CONFIGS[name]
     q, k, v = ai.prefill_inputs(cfg)
-    dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+    conv = to_dev16 if cfg.f16 else to_dev
+    dq, dk, dv = conv(q), conv(k), conv(v)
     o = torch.empty_like(dq)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
     return cfg, (dq, dk, dv, o, lse)
@@ -326,10 +334,11 @@ def main():
     if not args.no_extra:
         extra = {}
         del q, k, v, o, lse
-        for name in ("llama2_7b_prefill_noncausal", "long_prefill_32k"):
+        for name in ("llama2_7b_prefill_noncausal", "long_prefill_32k", "llama2_7b_prefill_f16"):
             cfg, (eq, ek, ev_, eo, el) = prefill_setup(name)
+            fwd = mi.attn_fwd_prefill_f16 if cfg.f16 else mi.attn_fwd_prefill
             avg, med, mn = time_kernel(
-                lambda: mi.attn_fwd_prefill(eq, ek, ev_, eo, el, cfg.causal, cfg.scale, stream),
+                lambda: fwd(eq, ek, ev_, eo, el, cfg.causal, cfg.scale, stream),
                 max(3, args.steps // 4) if name == "long_prefill_32k" else args.steps,
                 args.warmup)
             tf = ai.prefill_flops(cfg) / (avg * 1e-6) / 1e12

@@ -26,7 +26,9 @@
  *    allocates, frees or synchronises; every call is asynchronous on `stream`
  *    (0 = the null stream) and its outputs are valid once the stream reaches it.
  *  - Tensors are dense, contiguous, row-major, in the layouts stated per argument; no
- *    strides are taken.  bf16 tensors are passed as `const void*` (16-bit patterns).
+ *    strides are taken.  bf16 and fp16 tensors are passed as `const void*` (16-bit
+ *    patterns); the entry points with the _f16 suffix take IEEE fp16 where the others
+ *    take bf16.
  *    Outputs must not alias inputs.
  *  - Every call returns an attn_status_t.  Arguments are validated before any HIP call;
  *    a failed validation launches nothing.  Nothing throws across this interface.
@@ -76,6 +78,14 @@ int attn_fwd_prefill(const void* q, const void* k, const void* v, void* o, float
                      int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                      hipStream_t stream);
 
+/* attn_fwd_prefill with q, k, v and o in IEEE fp16 instead of bf16: the same layouts,
+ * arguments and errors.  The products run on the fp16 MFMA with fp32 accumulation, P is
+ * rounded to fp16 (nearest even) before P*V and o is rounded to fp16 (nearest even).  Each
+ * output row is a convex combination of V rows, so it stays in fp16 range when V does. */
+int attn_fwd_prefill_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                         hipStream_t stream);
+
 /*
  * Chunked (append) prefill against a paged KV cache: the Nq newest tokens of every
  * sequence attend to that sequence's whole cached context, which already holds their
@@ -106,6 +116,13 @@ int attn_fwd_prefill_paged(const void* q, const void* kcache, const void* vcache
                            float* lse, int B, int Hq, int Hkv, int Nq, int d, int max_kv_len,
                            int page_size, int max_blocks_per_seq, int num_pages, int causal,
                            float scale, hipStream_t stream);
+
+/* attn_fwd_prefill_paged with fp16 q, caches and o (as in attn_fwd_prefill_f16). */
+int attn_fwd_prefill_paged_f16(const void* q, const void* kcache, const void* vcache,
+                               const int32_t* block_table, const int32_t* kv_lens, void* o,
+                               float* lse, int B, int Hq, int Hkv, int Nq, int d, int max_kv_len,
+                               int page_size, int max_blocks_per_seq, int num_pages, int causal,
+                               float scale, hipStream_t stream);
 
 /*
  * Decode: one query per sequence against the sequence's KV cache, split along the
@@ -143,6 +160,14 @@ int attn_fwd_decode(const void* q, const void* kcache, const void* vcache,
                     int max_blocks_per_seq, int num_pages, float scale, int num_splits,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* attn_fwd_decode with fp16 q, caches and o (as in attn_fwd_prefill_f16): the same
+ * layouts, chunking, workspace and errors. */
+int attn_fwd_decode_f16(const void* q, const void* kcache, const void* vcache,
+                        const int32_t* block_table, const int32_t* seqlens, void* o, float* lse,
+                        int B, int Hq, int Hkv, int d, int max_seqlen, int page_size,
+                        int max_blocks_per_seq, int num_pages, float scale, int num_splits,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /*
  * Decode over an FP8 KV cache: attn_fwd_decode with K and V stored as OCP FP8 E4M3 codes
  * (1 byte per element: sign, 4 exponent bits with bias 7, 3 mantissa bits, no
@@ -167,7 +192,7 @@ int attn_fwd_decode_fp8(const void* q, const void* kcache, const void* vcache,
                         float k_scale, float v_scale, int num_splits, void* workspace,
                         size_t workspace_bytes, hipStream_t stream);
 
-/* Number of KV chunks attn_fwd_decode (and attn_fwd_decode_fp8) uses for these arguments
+/* Number of KV chunks attn_fwd_decode (and its _f16 and _fp8 variants) uses for these arguments
  * (num_splits 0 = auto).
  * Returns 0 for invalid arguments.  Pure host arithmetic; no HIP call. */
 int attn_decode_num_splits(int B, int Hq, int Hkv, int d, int max_seqlen, int num_splits);

@@ -52,11 +52,17 @@ def load_library():
     lib.attn_fwd_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
                                      vp]
     lib.attn_fwd_prefill.restype = i32
+    lib.attn_fwd_prefill_f16.argtypes = lib.attn_fwd_prefill.argtypes
+    lib.attn_fwd_prefill_f16.restype = i32
     lib.attn_fwd_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp] + [i32] * 10 + [f32, vp]
     lib.attn_fwd_prefill_paged.restype = i32
+    lib.attn_fwd_prefill_paged_f16.argtypes = lib.attn_fwd_prefill_paged.argtypes
+    lib.attn_fwd_prefill_paged_f16.restype = i32
     lib.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                     i32, f32, i32, vp, ctypes.c_size_t, vp]
     lib.attn_fwd_decode.restype = i32
+    lib.attn_fwd_decode_f16.argtypes = lib.attn_fwd_decode.argtypes
+    lib.attn_fwd_decode_f16.restype = i32
     lib.attn_fwd_decode_fp8.argtypes = [vp] * 7 + [i32] * 8 + [f32, f32, f32, i32, vp,
                                                                ctypes.c_size_t, vp]
     lib.attn_fwd_decode_fp8.restype = i32
@@ -101,14 +107,13 @@ def _check(t, name, dtype, ndim, device=None):
 
 
 # -------------------------------------------------------------------------------- prefill
-def attn_fwd_prefill(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
-    """q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d], o [B,Hq,Nq,d] bf16; lse [B,Hq,Nq] fp32 or None."""
+def _prefill_call(fn, dtype, q, k, v, o, lse, causal, scale, stream):
     lib = load_library()
-    _check(q, "q", torch.bfloat16, 4)
+    _check(q, "q", dtype, 4)
     dev = q.device
-    _check(k, "k", torch.bfloat16, 4, dev)
-    _check(v, "v", torch.bfloat16, 4, dev)
-    _check(o, "o", torch.bfloat16, 4, dev)
+    _check(k, "k", dtype, 4, dev)
+    _check(v, "v", dtype, 4, dev)
+    _check(o, "o", dtype, 4, dev)
     B, Hq, Nq, d = q.shape
     Bk, Hkv, Nk, dk = k.shape
     if Bk != B or dk != d or tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape):
@@ -117,34 +122,42 @@ def attn_fwd_prefill(q, k, v, o, lse, causal: bool, scale: float, stream=None) -
         _check(lse, "lse", torch.float32, 3, dev)
         if tuple(lse.shape) != (B, Hq, Nq):
             raise ValueError("lse must be [B, Hq, Nq]")
-    st = lib.attn_fwd_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk,
-                              d, 1 if causal else 0, float(scale), _stream_handle(stream))
+    st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk,
+                          d, 1 if causal else 0, float(scale), _stream_handle(stream))
     if st != ATTN_OK:
-        raise AttnError(st, "attn_fwd_prefill")
+        raise AttnError(st, fn)
+
+
+def attn_fwd_prefill(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
+    """q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d], o [B,Hq,Nq,d] bf16; lse [B,Hq,Nq] fp32 or None."""
+    _prefill_call("attn_fwd_prefill", torch.bfloat16, q, k, v, o, lse, causal, scale, stream)
+
+
+def attn_fwd_prefill_f16(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
+    """attn_fwd_prefill with fp16 q, k, v, o."""
+    _prefill_call("attn_fwd_prefill_f16", torch.float16, q, k, v, o, lse, causal, scale, stream)
 
 
 def prefill(q, k, v, causal: bool = True, scale: float | None = None):
-    """Allocate O and LSE and run attn_fwd_prefill.  scale None means 1/sqrt(d)."""
+    """Allocate O and LSE and run attn_fwd_prefill (attn_fwd_prefill_f16 for fp16 inputs).
+    scale None means 1/sqrt(d)."""
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    attn_fwd_prefill(q, k, v, o, lse, causal, scale)
+    fn = attn_fwd_prefill_f16 if q.dtype == torch.float16 else attn_fwd_prefill
+    fn(q, k, v, o, lse, causal, scale)
     return o, lse
 
 
-def attn_fwd_prefill_paged(q, kcache, vcache, block_table, kv_lens, o, lse, max_kv_len: int,
-                           causal: bool, scale: float, page_size: int = 16,
-                           num_pages: int | None = None, stream=None) -> None:
-    """Chunked prefill against a paged cache.  q/o [B,Hq,Nq,d] bf16; caches
-    [num_pages,Hkv,16,d] bf16; block_table int32 [B, max_blocks] and kv_lens int32 [B]
-    (device), each kv_lens[b] in [Nq, max_kv_len]; lse [B,Hq,Nq] fp32 or None."""
+def _prefill_paged_call(fn, dtype, q, kcache, vcache, block_table, kv_lens, o, lse, max_kv_len,
+                        causal, scale, page_size, num_pages, stream):
     lib = load_library()
-    _check(q, "q", torch.bfloat16, 4)
+    _check(q, "q", dtype, 4)
     dev = q.device
-    _check(kcache, "kcache", torch.bfloat16, 4, dev)
-    _check(vcache, "vcache", torch.bfloat16, 4, dev)
-    _check(o, "o", torch.bfloat16, 4, dev)
+    _check(kcache, "kcache", dtype, 4, dev)
+    _check(vcache, "vcache", dtype, 4, dev)
+    _check(o, "o", dtype, 4, dev)
     _check(block_table, "block_table", torch.int32, 2, dev)
     _check(kv_lens, "kv_lens", torch.int32, 1, dev)
     B, Hq, Nq, d = q.shape
@@ -160,13 +173,32 @@ def attn_fwd_prefill_paged(q, kcache, vcache, block_table, kv_lens, o, lse, max_
             raise ValueError("lse must be [B, Hq, Nq]")
     if num_pages is None:
         num_pages = kcache.shape[0]
-    st = lib.attn_fwd_prefill_paged(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(block_table),
-                                    _ptr(kv_lens), _ptr(o), _ptr(lse), B, Hq, kcache.shape[1], Nq,
-                                    d, int(max_kv_len), int(page_size), int(block_table.shape[1]),
-                                    int(num_pages), 1 if causal else 0, float(scale),
-                                    _stream_handle(stream))
+    st = getattr(lib, fn)(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(block_table),
+                          _ptr(kv_lens), _ptr(o), _ptr(lse), B, Hq, kcache.shape[1], Nq,
+                          d, int(max_kv_len), int(page_size), int(block_table.shape[1]),
+                          int(num_pages), 1 if causal else 0, float(scale),
+                          _stream_handle(stream))
     if st != ATTN_OK:
-        raise AttnError(st, "attn_fwd_prefill_paged")
+        raise AttnError(st, fn)
+
+
+def attn_fwd_prefill_paged(q, kcache, vcache, block_table, kv_lens, o, lse, max_kv_len: int,
+                           causal: bool, scale: float, page_size: int = 16,
+                           num_pages: int | None = None, stream=None) -> None:
+    """Chunked prefill against a paged cache.  q/o [B,Hq,Nq,d] bf16; caches
+    [num_pages,Hkv,16,d] bf16; block_table int32 [B, max_blocks] and kv_lens int32 [B]
+    (device), each kv_lens[b] in [Nq, max_kv_len]; lse [B,Hq,Nq] fp32 or None."""
+    _prefill_paged_call("attn_fwd_prefill_paged", torch.bfloat16, q, kcache, vcache, block_table,
+                        kv_lens, o, lse, max_kv_len, causal, scale, page_size, num_pages, stream)
+
+
+def attn_fwd_prefill_paged_f16(q, kcache, vcache, block_table, kv_lens, o, lse, max_kv_len: int,
+                               causal: bool, scale: float, page_size: int = 16,
+                               num_pages: int | None = None, stream=None) -> None:
+    """attn_fwd_prefill_paged with fp16 q, caches and o."""
+    _prefill_paged_call("attn_fwd_prefill_paged_f16", torch.float16, q, kcache, vcache,
+                        block_table, kv_lens, o, lse, max_kv_len, causal, scale, page_size,
+                        num_pages, stream)
 
 
 def prefill_paged(q, kcache, vcache, block_table, kv_lens, max_kv_len: int, causal: bool = True,
@@ -176,8 +208,8 @@ def prefill_paged(q, kcache, vcache, block_table, kv_lens, max_kv_len: int, caus
         scale = 1.0 / math.sqrt(q.shape[-1])
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    attn_fwd_prefill_paged(q, kcache, vcache, block_table, kv_lens, o, lse, max_kv_len, causal,
-                           scale)
+    fn = attn_fwd_prefill_paged_f16 if q.dtype == torch.float16 else attn_fwd_prefill_paged
+    fn(q, kcache, vcache, block_table, kv_lens, o, lse, max_kv_len, causal, scale)
     return o, lse
 
 
@@ -191,16 +223,16 @@ def attn_decode_num_splits(B, Hq, Hkv, d, max_seqlen, num_splits=0) -> int:
 
 
 def _decode_args(q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen, workspace,
-                 page_size, num_pages, cache_dtypes):
-    """Checks shared by both decode entry points; returns the size arguments."""
-    _check(q, "q", torch.bfloat16, 3)
+                 page_size, num_pages, cache_dtypes, qo_dtype=torch.bfloat16):
+    """Checks shared by the decode entry points; returns the size arguments."""
+    _check(q, "q", qo_dtype, 3)
     dev = q.device
     for name, t in (("kcache", kcache), ("vcache", vcache)):
         if isinstance(t, torch.Tensor) and t.dtype in cache_dtypes:
             _check(t, name, t.dtype, 4, dev)
         else:
             _check(t, name, cache_dtypes[0], 4, dev)
-    _check(o, "o", torch.bfloat16, 3, dev)
+    _check(o, "o", qo_dtype, 3, dev)
     _check(seqlens, "seqlens", torch.int32, 1, dev)
     B, Hq, d = q.shape
     if tuple(vcache.shape) != tuple(kcache.shape) or tuple(o.shape) != tuple(q.shape):
@@ -236,22 +268,36 @@ def _decode_args(q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen, wo
     return B, Hq, Hkv, d, max_blocks, num_pages, ws_bytes
 
 
+def _decode_call(fn, dtype, q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen, scale,
+                 num_splits, workspace, page_size, num_pages, stream):
+    lib = load_library()
+    B, Hq, Hkv, d, max_blocks, num_pages, ws_bytes = _decode_args(
+        q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen, workspace, page_size,
+        num_pages, (dtype,), dtype)
+    st = getattr(lib, fn)(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(block_table),
+                          _ptr(seqlens), _ptr(o), _ptr(lse), B, Hq, Hkv, d, int(max_seqlen),
+                          int(page_size), int(max_blocks), int(num_pages), float(scale),
+                          int(num_splits), _ptr(workspace), ws_bytes, _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, fn)
+
+
 def attn_fwd_decode(q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen: int,
                     scale: float, num_splits: int = 0, workspace=None, page_size: int = 16,
                     num_pages: int | None = None, stream=None) -> None:
     """q/o [B,Hq,d] bf16; lse [B,Hq] fp32 or None; seqlens int32 [B] (device).
     block_table None: caches [B,Hkv,max_seqlen,d]; else caches [num_pages,Hkv,16,d] and
     block_table int32 [B, max_blocks]."""
-    lib = load_library()
-    B, Hq, Hkv, d, max_blocks, num_pages, ws_bytes = _decode_args(
-        q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen, workspace, page_size,
-        num_pages, (torch.bfloat16,))
-    st = lib.attn_fwd_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(block_table),
-                             _ptr(seqlens), _ptr(o), _ptr(lse), B, Hq, Hkv, d, int(max_seqlen),
-                             int(page_size), int(max_blocks), int(num_pages), float(scale),
-                             int(num_splits), _ptr(workspace), ws_bytes, _stream_handle(stream))
-    if st != ATTN_OK:
-        raise AttnError(st, "attn_fwd_decode")
+    _decode_call("attn_fwd_decode", torch.bfloat16, q, kcache, vcache, block_table, seqlens, o,
+                 lse, max_seqlen, scale, num_splits, workspace, page_size, num_pages, stream)
+
+
+def attn_fwd_decode_f16(q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen: int,
+                        scale: float, num_splits: int = 0, workspace=None, page_size: int = 16,
+                        num_pages: int | None = None, stream=None) -> None:
+    """attn_fwd_decode with fp16 q, caches and o."""
+    _decode_call("attn_fwd_decode_f16", torch.float16, q, kcache, vcache, block_table, seqlens, o,
+                 lse, max_seqlen, scale, num_splits, workspace, page_size, num_pages, stream)
 
 
 def attn_fwd_decode_fp8(q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen: int,
@@ -290,8 +336,8 @@ def decode(q, kcache, vcache, seqlens, max_seqlen: int, block_table=None,
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = decode_workspace(B, Hq, kcache.shape[1], d, max_seqlen, num_splits, q.device)
-    attn_fwd_decode(q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen, scale,
-                    num_splits, workspace)
+    fn = attn_fwd_decode_f16 if q.dtype == torch.float16 else attn_fwd_decode
+    fn(q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen, scale, num_splits, workspace)
     return o, lse
 
 
@@ -311,7 +357,8 @@ def decode_fp8(q, kcache, vcache, seqlens, max_seqlen: int, k_scale: float, v_sc
     return o, lse
 
 
-__all__ = ["attn_fwd_prefill", "attn_fwd_decode", "attn_fwd_decode_fp8",
+__all__ = ["attn_fwd_prefill", "attn_fwd_prefill_f16", "attn_fwd_prefill_paged_f16",
+           "attn_fwd_decode", "attn_fwd_decode_f16", "attn_fwd_decode_fp8",
            "attn_decode_workspace_bytes", "decode_fp8",
            "attn_decode_num_splits", "attn_status_string", "prefill", "decode",
            "attn_fwd_prefill_paged", "prefill_paged",

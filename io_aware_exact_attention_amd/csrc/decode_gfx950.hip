@@ -59,7 +59,7 @@ constexpr int kDecodeSetsF8 = 3;  // FP8 blocks in flight per wave
 // contiguous 6.25 vs 5.86 TB/s).
 constexpr int kKvLoadPolicy = 2;
 
-template <int D, bool PAGED, bool F8>
+template <int D, bool PAGED, bool F8, typename E>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_split_kernel(DecodeParams a) {
   using S = DecodeShape<D>;
@@ -232,7 +232,7 @@ void decode_split_kernel(DecodeParams a) {
 #pragma unroll
       for (int st = 0; st < D / 32; ++st) {
         const bf16x8 ka = *(const bf16x8*)(kp_l + h * 16 * S::KSTR + st * 64);
-        s[h] = mfma_16x16x32(ka, qop[st], s[h]);
+        s[h] = E::mfma16(ka, qop[st], s[h]);
       }
     }
     // accumulator r of half h is key tb + 16*h + 4*g4 + r
@@ -272,8 +272,8 @@ void decode_split_kernel(DecodeParams a) {
           p0 = k0 >= t1 ? 0.f : p0;
           p1 = k0 + 1 >= t1 ? 0.f : p1;
         }
-        pk[2 * h + j] = pack_bf16x2(p0, p1);
-        l_run = add_bf16x2(pk[2 * h + j], l_run);
+        pk[2 * h + j] = E::pack2(p0, p1);
+        l_run = E::add2(pk[2 * h + j], l_run);
         l_ex += p0 + p1;
       }
     // P^T operand: k-slots 8*g4 + e <-> keys 4*g4 + e (e < 4), 16 + 4*g4 + e - 4 (e >= 4)
@@ -282,7 +282,7 @@ void decode_split_kernel(DecodeParams a) {
     for (int db = 0; db < D / 16; ++db) {
       const bf16x4 lo = lds_read_tr(vp_l + db * 32);
       const bf16x4 hi = lds_read_tr(vp_l + db * 32 + 16 * S::VSTR);
-      oacc[db] = mfma_16x16x32(concat(lo, hi), pb, oacc[db]);
+      oacc[db] = E::mfma16(concat(lo, hi), pb, oacc[db]);
     }
   };
 
@@ -354,7 +354,7 @@ merge:
     const float lse_nat = (M * c + log2f(Esum)) * kLn2;
     const size_t row = (size_t)b * a.Hq + kvh * a.G + grp * NH + h;
     if (a.num_splits == 1) {
-      a.o[row * D + dv] = __builtin_bit_cast(uint16_t, (__bf16)out);
+      a.o[row * D + dv] = E::bits(out);
       if (dv == 0 && a.lse) a.lse[row] = lse_nat;
     } else {
       a.ws_o[(row * a.num_splits + split) * D + dv] = out;
@@ -369,7 +369,7 @@ merge:
 // and the kMergeSub partial sums are combined in LDS.
 constexpr int kMergeThreads = 512;
 
-template <int D>
+template <int D, typename E>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParams a) {
   constexpr int kMergeSub = kMergeThreads / D;
   __shared__ float s_lse[kDecodeMaxSplits];
@@ -410,28 +410,32 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
       t += s_acc[k][tid];
       wt += s_w[k];
     }
-    orow[tid] = __builtin_bit_cast(uint16_t, (__bf16)(t / wt));
+    orow[tid] = E::bits(t / wt);
     if (tid == 0 && a.lse) a.lse[row] = M + logf(wt);
   }
 }
 
-template <int D, bool F8>
+template <int D, bool F8, typename E>
 static hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid(p.num_splits, p.Hkv * p.ngroups, p.B);
   if (p.block_table)
-    hipLaunchKernelGGL((decode_split_kernel<D, true, F8>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_split_kernel<D, true, F8, E>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_split_kernel<D, false, F8>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_split_kernel<D, false, F8, E>), grid, dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.num_splits == 1) return e;
   const int rows = p.B * p.Hq;
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(rows), dim3(kMergeThreads), 0, stream, p);
+  hipLaunchKernelGGL((decode_merge_kernel<D, E>), dim3(rows), dim3(kMergeThreads), 0, stream, p);
   return hipGetLastError();
 }
 
+// The FP8 cache widens to bf16 and is paired with bf16 Q and O only.
 hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t stream) {
-  if (p.kv_fp8) return d == 64 ? launch_d<64, true>(p, stream) : launch_d<128, true>(p, stream);
-  return d == 64 ? launch_d<64, false>(p, stream) : launch_d<128, false>(p, stream);
+  if (p.kv_fp8)
+    return d == 64 ? launch_d<64, true, ElemBf16>(p, stream) : launch_d<128, true, ElemBf16>(p, stream);
+  if (p.f16)
+    return d == 64 ? launch_d<64, false, ElemF16>(p, stream) : launch_d<128, false, ElemF16>(p, stream);
+  return d == 64 ? launch_d<64, false, ElemBf16>(p, stream) : launch_d<128, false, ElemBf16>(p, stream);
 }
 
 }  // namespace miattn

@@ -28,23 +28,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 // arithmetic the result does not depend on which reference max is used.
 constexpr float kRescaleLog2 = 8.0f;
 // Prefill variant of the same idea: a tile's weights are formed against the current
-// reference max and only redone against a fresh one when their sum exceeds 2^32 (or is
-// not finite).  Weights then stay below 2^32, so O and l cannot overflow for any input
-// that the exact softmax can handle.
-constexpr float kRedoBound = 4294967296.0f;
-
-// D = A(32x16) * B(16x32) + C, bf16 inputs, fp32 accumulate.
-// Lane l holds A[l%32][8*(l/32) .. +7], B[8*(l/32) .. +7][l%32] and
-// C[8*(r/4) + 4*(l/32) + r%4][l%32] in accumulator r.
-__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// D = A(16x32) * B(32x16) + C.  Lane l holds A[l%16][8*(l/16) .. +7],
-// B[8*(l/16) .. +7][l%16] and C[4*(l/16) + r][l%16] in accumulator r.
-__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
+// reference max and only redone against a fresh one when their sum exceeds the element
+// type's kRedoBound (or is not finite).  Weights then stay below that bound, so P, O and
+// l cannot overflow for any input that the exact softmax can handle.
 
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i
 // supplies the address of 4 consecutive bf16 holding row i/4, columns 4*(i%4)..+3 of a
@@ -102,6 +88,64 @@ __device__ __forceinline__ float add_bf16x2(uint32_t x, float acc) {
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), ones, acc, false);
 }
+
+// Element types of Q, K, V and O.  Operand registers and LDS hold raw 16-bit patterns
+// (typed bf16x8 throughout); the type decides the MFMA instruction, how P and O are
+// rounded from fp32 (nearest even either way) and how far a prefill tile's unnormalised
+// weights may grow before the tile is redone against a fresh row max.
+//
+// MFMA lane layouts (the same for both element types):
+//   mfma32: D = A(32x16) * B(16x32) + C.  Lane l holds A[l%32][8*(l/32) .. +7],
+//           B[8*(l/32) .. +7][l%32] and C[8*(r/4) + 4*(l/32) + r%4][l%32] in accumulator r.
+//   mfma16: D = A(16x32) * B(32x16) + C.  Lane l holds A[l%16][8*(l/16) .. +7],
+//           B[8*(l/16) .. +7][l%16] and C[4*(l/16) + r][l%16] in accumulator r.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+struct ElemBf16 {
+  // weights stay below 2^32: far inside the fp32 and bf16 ranges
+  static constexpr float kRedoBound = 4294967296.0f;
+  static __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
+  // acc + both halves of a packed pair
+  static __device__ __forceinline__ float add2(uint32_t x, float acc) { return add_bf16x2(x, acc); }
+  static __device__ __forceinline__ uint16_t bits(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+  }
+};
+
+struct ElemF16 {
+  // fp16 tops out at 65504, so a tile's weights (each at most their sum) stay below 2^15
+  static constexpr float kRedoBound = 32768.0f;
+  static __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  // v_cvt_pk_f16_f32
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    f16x2 v;
+    v[0] = (_Float16)a;
+    v[1] = (_Float16)b;
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  // v_dot2_f32_f16 against (1, 1)
+  static __device__ __forceinline__ float add2(uint32_t x, float acc) {
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), ones, acc, false);
+  }
+  static __device__ __forceinline__ uint16_t bits(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+};
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

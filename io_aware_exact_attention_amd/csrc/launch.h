@@ -24,6 +24,7 @@ struct PrefillParams {
   const int32_t* block_table;
   const int32_t* kv_lens;
   int max_blocks;
+  int f16;  // Q, K, V, O are fp16 (else bf16)
 };
 
 struct DecodeParams {
@@ -44,6 +45,7 @@ struct DecodeParams {
   int negate_q;
   int kv_fp8;     // K/V caches hold E4M3 codes
   float v_scale;  // FP8 cache: multiplies the normalised output
+  int f16;        // Q, O and the cache are fp16 (else bf16; never with kv_fp8)
 };
 
 // Query heads sharing one KV head that a decode workgroup serves at once.

@@ -71,7 +71,7 @@ size_t workspace_for(int B, int Hq, int d, const Plan& pl) {
 int decode_impl(const void* q, const void* kcache, const void* vcache,
                 const int32_t* block_table, const int32_t* seqlens, void* o, float* lse, int B,
                 int Hq, int Hkv, int d, int max_seqlen, int page_size, int max_blocks_per_seq,
-                int num_pages, float scale, bool fp8, float k_scale, float v_scale,
+                int num_pages, float scale, bool fp8, bool f16, float k_scale, float v_scale,
                 int num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!q || !kcache || !vcache || !seqlens || !o) return ATTN_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16) || !aligned(kcache, 16) || !aligned(vcache, 16) || !aligned(o, 16) ||
@@ -118,29 +118,16 @@ int decode_impl(const void* q, const void* kcache, const void* vcache,
   if (!std::isfinite(p.c)) return ATTN_ERR_INVALID_ARGUMENT;
   p.negate_q = scale < 0.f;
   p.kv_fp8 = fp8;
+  p.f16 = f16;
   p.v_scale = v_scale;
   (void)hipGetLastError();
   return miattn::launch_decode(p, d, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* attn_status_string(int status) {
-  switch (status) {
-    case ATTN_OK: return "ok";
-    case ATTN_ERR_INVALID_ARGUMENT: return "invalid argument";
-    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
-    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
-    case ATTN_ERR_HIP: return "HIP launch error";
-    default: return "unknown status";
-  }
-}
-
-int attn_fwd_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                     int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
-                     hipStream_t stream) {
+// The prefill entry points (bf16 or fp16 elements).
+int prefill_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                 int Hkv, int Nq, int Nk, int d, int causal, float scale, bool f16,
+                 hipStream_t stream) {
   if (!q || !k || !v || !o) return ATTN_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
     return ATTN_ERR_INVALID_ARGUMENT;
@@ -165,16 +152,17 @@ int attn_fwd_prefill(const void* q, const void* k, const void* v, void* o, float
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk;
   p.c = std::fabs(scale) * 1.4426950408889634f;
   p.negate_q = scale < 0.f;
+  p.f16 = f16;
   (void)hipGetLastError();  // clear a stale error so the check below is ours
   return miattn::launch_prefill(p, d, causal ? 1 : 0, stream) == hipSuccess ? ATTN_OK
                                                                              : ATTN_ERR_HIP;
 }
 
-int attn_fwd_prefill_paged(const void* q, const void* kcache, const void* vcache,
-                           const int32_t* block_table, const int32_t* kv_lens, void* o,
-                           float* lse, int B, int Hq, int Hkv, int Nq, int d, int max_kv_len,
-                           int page_size, int max_blocks_per_seq, int num_pages, int causal,
-                           float scale, hipStream_t stream) {
+int prefill_paged_impl(const void* q, const void* kcache, const void* vcache,
+                       const int32_t* block_table, const int32_t* kv_lens, void* o, float* lse,
+                       int B, int Hq, int Hkv, int Nq, int d, int max_kv_len, int page_size,
+                       int max_blocks_per_seq, int num_pages, int causal, float scale, bool f16,
+                       hipStream_t stream) {
   if (!q || !kcache || !vcache || !block_table || !kv_lens || !o) return ATTN_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16) || !aligned(kcache, 16) || !aligned(vcache, 16) || !aligned(o, 16) ||
       !aligned(block_table, 4) || !aligned(kv_lens, 4))
@@ -201,9 +189,57 @@ int attn_fwd_prefill_paged(const void* q, const void* kcache, const void* vcache
   p.block_table = block_table;
   p.kv_lens = kv_lens;
   p.max_blocks = max_blocks_per_seq;
+  p.f16 = f16;
   (void)hipGetLastError();
   return miattn::launch_prefill(p, d, causal ? 1 : 0, stream) == hipSuccess ? ATTN_OK
                                                                              : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int attn_fwd_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                     hipStream_t stream) {
+  return prefill_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, false, stream);
+}
+
+int attn_fwd_prefill_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                         hipStream_t stream) {
+  return prefill_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, true, stream);
+}
+
+int attn_fwd_prefill_paged(const void* q, const void* kcache, const void* vcache,
+                           const int32_t* block_table, const int32_t* kv_lens, void* o,
+                           float* lse, int B, int Hq, int Hkv, int Nq, int d, int max_kv_len,
+                           int page_size, int max_blocks_per_seq, int num_pages, int causal,
+                           float scale, hipStream_t stream) {
+  return prefill_paged_impl(q, kcache, vcache, block_table, kv_lens, o, lse, B, Hq, Hkv, Nq, d,
+                            max_kv_len, page_size, max_blocks_per_seq, num_pages, causal, scale,
+                            false, stream);
+}
+
+int attn_fwd_prefill_paged_f16(const void* q, const void* kcache, const void* vcache,
+                               const int32_t* block_table, const int32_t* kv_lens, void* o,
+                               float* lse, int B, int Hq, int Hkv, int Nq, int d, int max_kv_len,
+                               int page_size, int max_blocks_per_seq, int num_pages, int causal,
+                               float scale, hipStream_t stream) {
+  return prefill_paged_impl(q, kcache, vcache, block_table, kv_lens, o, lse, B, Hq, Hkv, Nq, d,
+                            max_kv_len, page_size, max_blocks_per_seq, num_pages, causal, scale,
+                            true, stream);
 }
 
 int attn_decode_num_splits(int B, int Hq, int Hkv, int d, int max_seqlen, int num_splits) {
@@ -223,7 +259,17 @@ int attn_fwd_decode(const void* q, const void* kcache, const void* vcache,
                     int max_blocks_per_seq, int num_pages, float scale, int num_splits,
                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return decode_impl(q, kcache, vcache, block_table, seqlens, o, lse, B, Hq, Hkv, d, max_seqlen,
-                     page_size, max_blocks_per_seq, num_pages, scale, false, 1.f, 1.f,
+                     page_size, max_blocks_per_seq, num_pages, scale, false, false, 1.f, 1.f,
+                     num_splits, workspace, workspace_bytes, stream);
+}
+
+int attn_fwd_decode_f16(const void* q, const void* kcache, const void* vcache,
+                        const int32_t* block_table, const int32_t* seqlens, void* o, float* lse,
+                        int B, int Hq, int Hkv, int d, int max_seqlen, int page_size,
+                        int max_blocks_per_seq, int num_pages, float scale, int num_splits,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl(q, kcache, vcache, block_table, seqlens, o, lse, B, Hq, Hkv, d, max_seqlen,
+                     page_size, max_blocks_per_seq, num_pages, scale, false, true, 1.f, 1.f,
                      num_splits, workspace, workspace_bytes, stream);
 }
 
@@ -237,7 +283,7 @@ int attn_fwd_decode_fp8(const void* q, const void* kcache, const void* vcache,
       !(v_scale > 0.f))
     return ATTN_ERR_INVALID_ARGUMENT;
   return decode_impl(q, kcache, vcache, block_table, seqlens, o, lse, B, Hq, Hkv, d, max_seqlen,
-                     page_size, max_blocks_per_seq, num_pages, scale, true, k_scale, v_scale,
+                     page_size, max_blocks_per_seq, num_pages, scale, true, false, k_scale, v_scale,
                      num_splits, workspace, workspace_bytes, stream);
 }
 

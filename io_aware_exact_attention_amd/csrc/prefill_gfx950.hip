@@ -167,7 +167,7 @@ __device__ __forceinline__ PagedItem paged_work_item(int p, int B, int Hq, int n
   return it;
 }
 
-template <int D, bool CAUSAL, bool PAGED>
+template <int D, bool CAUSAL, bool PAGED, typename E>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillParams a) {
   using S = PrefillShape<D>;
@@ -376,11 +376,11 @@ void prefill_kernel(PrefillParams a) {
         const int t4 = m / (D / 32), db = m % (D / 32);
         const u32x4 pw = {pk[t4 >> 1][4 * (t4 & 1) + 0], pk[t4 >> 1][4 * (t4 & 1) + 1],
                           pk[t4 >> 1][4 * (t4 & 1) + 2], pk[t4 >> 1][4 * (t4 & 1) + 3]};
-        oacc[db] = mfma_32x32x16(ops[m], __builtin_bit_cast(bf16x8, pw), oacc[db]);
+        oacc[db] = E::mfma32(ops[m], __builtin_bit_cast(bf16x8, pw), oacc[db]);
       } else {
         const int q = m - P0;
-        if (q & 1) s1 = mfma_32x32x16(ops[m], qop[q >> 1], s1);
-        else s0 = mfma_32x32x16(ops[m], qop[q >> 1], s0);
+        if (q & 1) s1 = E::mfma32(ops[m], qop[q >> 1], s1);
+        else s0 = E::mfma32(ops[m], qop[q >> 1], s0);
       }
     }
     // issue order: [the first kLead Q.K^T reads when nothing was prefetched], then per MFMA
@@ -427,14 +427,14 @@ void prefill_kernel(PrefillParams a) {
         for (int jj = 0; jj < 8; ++jj) {
           const float p0 = fast_exp2(fmaf(sacc[kb][2 * jj], c, nmc));
           const float p1 = fast_exp2(fmaf(sacc[kb][2 * jj + 1], c, nmc));
-          pk[kb][jj] = pack_bf16x2(p0, p1);
+          pk[kb][jj] = E::pack2(p0, p1);
           ex0 += p0;
           ex1 += p1;
         }
       return ex0 + ex1;
     };
     float ts = weights();
-    if (__builtin_amdgcn_ballot_w64(!(ts <= kRedoBound))) {
+    if (__builtin_amdgcn_ballot_w64(!(ts <= E::kRedoBound))) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -547,8 +547,8 @@ void prefill_kernel(PrefillParams a) {
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         const int dv = 32 * db + 8 * a4 + 4 * g;
-        const u32x2 w = {pack_bf16x2(oacc[db][4 * a4 + 0] * inv, oacc[db][4 * a4 + 1] * inv),
-                         pack_bf16x2(oacc[db][4 * a4 + 2] * inv, oacc[db][4 * a4 + 3] * inv)};
+        const u32x2 w = {E::pack2(oacc[db][4 * a4 + 0] * inv, oacc[db][4 * a4 + 1] * inv),
+                         E::pack2(oacc[db][4 * a4 + 2] * inv, oacc[db][4 * a4 + 3] * inv)};
         *(u32x2*)(orow + dv) = w;
       }
     if (g == 0 && a.lse)
@@ -556,13 +556,22 @@ void prefill_kernel(PrefillParams a) {
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, typename E>
 static hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
   if (p.block_table)
-    hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, true>), dim3(p.total_wg), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, true, E>), dim3(p.total_wg), dim3(512), 0,
+                       stream, p);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, false>), dim3(p.total_wg), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, false, E>), dim3(p.total_wg), dim3(512), 0,
+                       stream, p);
   return hipGetLastError();
+}
+
+template <typename E>
+static hipError_t launch_e(const PrefillParams& p, int d, int causal, hipStream_t stream) {
+  if (d == 64)
+    return causal ? launch_one<64, true, E>(p, stream) : launch_one<64, false, E>(p, stream);
+  return causal ? launch_one<128, true, E>(p, stream) : launch_one<128, false, E>(p, stream);
 }
 
 hipError_t launch_prefill(PrefillParams p, int d, int causal, hipStream_t stream) {
@@ -582,8 +591,7 @@ hipError_t launch_prefill(PrefillParams p, int d, int causal, hipStream_t stream
     int hg = (int)((4.0 * 1024 * 1024) / kv_bytes);
     p.head_group = hg < 1 ? 1 : (hg > nh ? nh : hg);
   }
-  if (d == 64) return causal ? launch_one<64, true>(p, stream) : launch_one<64, false>(p, stream);
-  return causal ? launch_one<128, true>(p, stream) : launch_one<128, false>(p, stream);
+  return p.f16 ? launch_e<ElemF16>(p, d, causal, stream) : launch_e<ElemBf16>(p, d, causal, stream);
 }
 
 }  // namespace miattn

@@ -30,7 +30,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["attn_fwd_prefill", "attn_fwd_prefill_paged",
-                                           "attn_fwd_decode", "attn_fwd_decode_fp8",
+                                           "attn_fwd_prefill_f16", "attn_fwd_prefill_paged_f16",
+                                           "attn_fwd_decode", "attn_fwd_decode_f16",
+                                           "attn_fwd_decode_fp8",
                                            "attn_decode_workspace_bytes",
                                            "attn_decode_num_splits", "attn_status_string"])
 
@@ -140,6 +142,44 @@ def decode_fp8(lib, k_scale=0.02, v_scale=0.03, **kw):
 ])
 def test_decode_fp8_validation(lib, kw, status):
     assert decode_fp8(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(B=0), INVALID), (dict(Hq=3, Hkv=2), INVALID),
+    (dict(Nq=5, Nk=4, causal=1), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(d=96), UNSUPPORTED)])
+def test_f16_entry_points_validate_like_bf16(lib, kw, status):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, Hq=2, Hkv=1, Nq=4, Nk=4, d=64, causal=1,
+             scale=0.125)
+    a.update(kw)
+    assert lib.attn_fwd_prefill_f16(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
+                                    a["Hkv"], a["Nq"], a["Nk"], a["d"], a["causal"],
+                                    ctypes.c_float(a["scale"]), None) == status
+    assert prefill(lib, **kw) == status
+
+
+def test_f16_paged_and_decode_validate_like_bf16(lib):
+    for kw, status in ((dict(table=None), INVALID), (dict(page_size=32), UNSUPPORTED),
+                       (dict(max_blocks=6), INVALID), (dict(d=80), UNSUPPORTED)):
+        a = dict(q=P, kc=P, vc=P, table=P, kv_lens=P, o=P, lse=None, B=2, Hq=8, Hkv=2, Nq=16,
+                 d=128, max_kv=100, page_size=16, max_blocks=7, num_pages=10, causal=1, scale=0.1)
+        a.update(kw)
+        args = [a[n] for n in ("q", "kc", "vc", "table", "kv_lens", "o", "lse", "B", "Hq", "Hkv",
+                               "Nq", "d", "max_kv", "page_size", "max_blocks", "num_pages",
+                               "causal")] + [ctypes.c_float(a["scale"]), None]
+        assert lib.attn_fwd_prefill_paged_f16(*args) == status
+        assert lib.attn_fwd_prefill_paged(*args) == status
+    for kw, status in ((dict(kc=None), INVALID), (dict(d=80), UNSUPPORTED),
+                       (dict(max_seqlen=4096, splits=4), WORKSPACE)):
+        a = dict(q=P, kc=P, vc=P, table=None, seqlens=P, o=P, lse=None, B=2, Hq=8, Hkv=2, d=128,
+                 max_seqlen=100, page_size=16, max_blocks=7, num_pages=10, scale=0.1, splits=1,
+                 ws=None, ws_bytes=0)
+        a.update(kw)
+        args = [a[n] for n in ("q", "kc", "vc", "table", "seqlens", "o", "lse", "B", "Hq", "Hkv",
+                               "d", "max_seqlen", "page_size", "max_blocks", "num_pages")]
+        args += [ctypes.c_float(a["scale"]), a["splits"], a["ws"], a["ws_bytes"], None]
+        assert lib.attn_fwd_decode_f16(*args) == status
+        assert lib.attn_fwd_decode(*args) == status
 
 
 def test_decode_split_plan(lib):

@@ -138,3 +138,37 @@ def test_fp8_cache_quantises_the_bf16_workload_draws():
     lb = ai.decode_lengths(base)
     kv = 2 * int(lb.sum()) * base.Hkv * base.d
     assert ai.decode_bytes(base, lb) - ai.decode_bytes(f8, lb) == kv
+
+
+# ----------------------------------------------------------------------------- fp16 rounding
+def test_f16_rounding_matches_torch():
+    rng = np.random.default_rng(2)
+    x = np.concatenate([rng.standard_normal(100_000).astype(np.float32) * 3,
+                        rng.uniform(-6e4, 6e4, 1000).astype(np.float32),
+                        (rng.standard_normal(1000) * 1e-6).astype(np.float32),  # subnormals
+                        np.array([0.0, -0.0, 1.0, 65504.0, 2.0 ** -24], np.float32)])
+    # exact ties halfway between neighbouring fp16 values, both parities of the kept bit
+    ties = ((np.arange(64, dtype=np.uint32) << 13) | np.uint32(0x3F801000)).view(np.float32)
+    x = np.concatenate([x, ties, -ties])
+    ours = ai.to_f16_bits(x)
+    ref = torch.from_numpy(x).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+    np.testing.assert_array_equal(ai.f16_bits_to_f64(ours),
+                                  torch.from_numpy(x).to(torch.float16).double().numpy())
+
+
+def test_f16_variant_rounds_the_same_draws():
+    a16 = ai.normal_bf16(5, ai.T_K, 1, 2, (8, 4), f16=True)
+    x = np.random.default_rng(np.random.SeedSequence([5, ai.T_K, 1, 2])).standard_normal(
+        (8, 4), dtype=np.float32)
+    np.testing.assert_array_equal(a16, ai.to_f16_bits(x))
+    cfg = ai.CONFIGS["llama2_7b_prefill_f16"]
+    assert cfg.f16 and cfg.seed == ai.CONFIGS["llama2_7b_prefill"].seed
+    q16 = ai.prefill_head(cfg, ai.T_Q, 0, 3)
+    q = ai.prefill_head(ai.CONFIGS["llama2_7b_prefill"], ai.T_Q, 0, 3)
+    # the two roundings of one draw differ by at most half a bf16 ulp plus half an fp16 ulp
+    d = np.abs(ai.f16_bits_to_f64(q16) - ai.bf16_bits_to_f64(q))
+    assert (d <= np.abs(ai.bf16_bits_to_f64(q)) * (2.0 ** -8 + 2.0 ** -11) + 2.0 ** -24).all()
+    dc = ai.DecodeCfg("t", B=1, Hq=2, Hkv=1, d=8, seed=3, paged=False, fixed_len=5, f16=True)
+    assert (ai.build_contig_cache(dc, ai.T_K, np.array([3], np.int32), 5)[0, 0, 3:]
+            == ai.F16_NAN).all()

@@ -502,3 +502,130 @@ def test_chunked_prefill_paged_config():
              mean_abs=float(err.mean()), lse_max_abs=float(lerr.max()), n=int(err.size))
     assert np.isfinite(go).all()
     assert err.max() <= TOL_MAX and err.mean() <= TOL_MEAN and lerr.max() <= TOL_LSE
+
+
+# ------------------------------------------------------------------ fp16 entry points
+def dev16(bits):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.float16)
+    return t.cuda()
+
+
+def h64(bits):
+    return ai.f16_bits_to_f64(bits)
+
+
+def run_prefill16(q, k, v, causal, scale):
+    o, lse = mi.prefill(dev16(q).reshape(q.shape), dev16(k).reshape(k.shape),
+                        dev16(v).reshape(v.shape), causal, scale)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.float16
+    return o, lse
+
+
+@pytest.mark.parametrize("N,Nk,causal,d", [(1, 1, True, 64), (65, 65, False, 128),
+                                           (129, 129, True, 128), (1000, 1000, True, 64),
+                                           (300, 300, False, 64), (100, 700, True, 128),
+                                           (77, 300, False, 128)])
+def test_prefill_f16_shapes(N, Nk, causal, d):
+    q, k, v = ai.custom_prefill(seed=5200 + N + d, B=1, Hq=2, Hkv=2, Nq=N, Nk=Nk, d=d, f16=True)
+    scale = 1 / math.sqrt(d)
+    o, lse = run_prefill16(q, k, v, causal, scale)
+    ro, rl = attention_prefill(h64(q), h64(k), h64(v), scale, causal)
+    check(f"prefill f16 Nq={N} Nk={Nk} causal={causal} d={d}", o, lse, ro, rl)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, 0.6])
+def test_prefill_f16_gqa_and_scale(scale):
+    q, k, v = ai.custom_prefill(seed=5300, B=2, Hq=8, Hkv=2, Nq=190, Nk=190, d=64, f16=True)
+    o, lse = run_prefill16(q, k, v, True, scale)
+    ro, rl = attention_prefill(h64(q), h64(k), h64(v), float(np.float32(scale)), True)
+    check(f"prefill f16 GQA scale={scale}", o, lse, ro, rl)
+
+
+def test_prefill_f16_rising_scores_redo_every_tile():
+    """Scores that rise by ~40 (natural log units) from one 64-key tile to the next: each
+    new tile's weights against the previous tile's max would be ~2^58, far past fp16, so
+    the fp16 kernel must redo every tile against a fresh max (its bound is 2^15)."""
+    d, N = 64, 512
+    rng = np.random.default_rng(11)
+    u = np.zeros(d, np.float32)
+    u[0] = 1.0
+    t = np.arange(N, dtype=np.float32) * np.float32(40.0 / 64.0)   # score of key j
+    k = ai.to_f16_bits(t[:, None] * u[None, :] + rng.standard_normal((N, d)).astype(np.float32)
+                       * np.float32(0.01))
+    q = ai.to_f16_bits(np.tile(u, (N, 1)))
+    v = ai.to_f16_bits(rng.standard_normal((N, d)).astype(np.float32))
+    q, k, v = q[None, None], k[None, None], v[None, None]
+    for causal in (False, True):
+        o, lse = run_prefill16(q, k, v, causal, 1.0)
+        ro, rl = attention_prefill(h64(q), h64(k), h64(v), 1.0, causal)
+        check(f"prefill f16 rising scores causal={causal}", o, lse, ro, rl)
+
+
+def test_prefill_f16_llama2_shape():
+    cfg = ai.CONFIGS["llama2_7b_prefill_f16"]
+    q, k, v = ai.prefill_inputs(cfg)
+    o, lse = run_prefill16(q, k, v, cfg.causal, cfg.scale)
+    go = o.float().cpu().numpy()
+    gl = lse.cpu().numpy()
+    rng = np.random.default_rng(17)
+    errs, lerrs = [], []
+    for (b, h) in [(0, 0), (3, 31), (2, 9)]:
+        rows = np.unique(np.concatenate([[0, cfg.Nq - 1], rng.integers(0, cfg.Nq, 64)]))
+        ro, rl = attention_rows(h64(q[b, h, rows]), h64(k[b, h]), h64(v[b, h]), cfg.scale,
+                                cfg.causal, rows, cfg.Nq)
+        errs.append(np.abs(go[b, h, rows] - ro).ravel())
+        lerrs.append(np.abs(gl[b, h, rows] - rl).ravel())
+    err, lerr = np.concatenate(errs), np.concatenate(lerrs)
+    log_case("llama2_7b_prefill_f16 (sampled)", max_abs=float(err.max()),
+             mean_abs=float(err.mean()), lse_max_abs=float(lerr.max()))
+    assert np.isfinite(go).all()
+    assert err.max() <= TOL_MAX and err.mean() <= TOL_MEAN and lerr.max() <= TOL_LSE
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_paged_f16_chunks(causal):
+    cfg = ai.DecodeCfg("chunk16", B=3, Hq=4, Hkv=2, d=128, seed=5400, paged=True, chunk=77,
+                       f16=True)
+    lens = np.array([77, 200, 1000], np.int32)
+    q = ai.chunk_q(cfg)
+    lay = ai.paged_layout(lens, 16, cfg.seed, extra_pages=3)
+    kc = ai.build_paged_cache(cfg, ai.T_K, lens, lay)
+    vc = ai.build_paged_cache(cfg, ai.T_V, lens, lay)
+    o, lse = mi.prefill_paged(dev16(q).reshape(q.shape), dev16(kc).reshape(kc.shape),
+                              dev16(vc).reshape(vc.shape),
+                              torch.from_numpy(lay.block_table).cuda(),
+                              torch.from_numpy(lens).cuda(), int(lens.max()), causal, 0.088)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.float16
+    ro, rl = attention_prefill_paged(h64(q), h64(kc), h64(vc), lay.block_table, lens, 0.088,
+                                     causal)
+    check(f"prefill_paged f16 causal={causal}", o, lse, ro, rl)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("splits", [1, 0])
+def test_decode_f16(paged, splits):
+    lens = [0, 1, 17, 33, 1000, 4097]
+    cfg = ai.DecodeCfg("dec16", B=6, Hq=16, Hkv=4, d=128, seed=5500, paged=paged, f16=True)
+    lens = np.asarray(lens, np.int32)
+    q = ai.decode_q(cfg)
+    maxlen = int(lens.max())
+    if paged:
+        lay = ai.paged_layout(lens, 16, cfg.seed, extra_pages=3)
+        kc = ai.build_paged_cache(cfg, ai.T_K, lens, lay)
+        vc = ai.build_paged_cache(cfg, ai.T_V, lens, lay)
+        table = lay.block_table
+    else:
+        kc = ai.build_contig_cache(cfg, ai.T_K, lens, maxlen)
+        vc = ai.build_contig_cache(cfg, ai.T_V, lens, maxlen)
+        table = None
+    o, lse = mi.decode(dev16(q).reshape(q.shape), dev16(kc).reshape(kc.shape),
+                       dev16(vc).reshape(vc.shape), torch.from_numpy(lens).cuda(), maxlen,
+                       block_table=None if table is None else torch.from_numpy(table).cuda(),
+                       scale=cfg.scale, num_splits=splits)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.float16
+    ro, rl = attention_decode(h64(q), h64(kc), h64(vc), lens, cfg.scale, table, 16)
+    check(f"decode f16 paged={paged} splits={splits}", o, lse, ro, rl)
+    assert (o[0] == 0).all() and torch.isinf(lse[0]).all()
