@@ -160,6 +160,59 @@ def attention_decode(q: np.ndarray, kcache: np.ndarray, vcache: np.ndarray,
 
 
 # ---------------------------------------------------------------------------
+# Backward: gradients of the definition
+# ---------------------------------------------------------------------------
+def attention_backward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
+                            scale: float, causal: bool):
+    """Gradients of one head of O = softmax(scale * Q K^T [+ mask]) V (the definition of
+    the page "FlashAttention 완전 정리" (cell-devlog), section "Attention이 뭔가") with
+    respect to Q, K and V, for the output gradient dO.  The pages only say that the fused
+    method recomputes the attention matrix in its backward pass instead of storing it
+    (page "메모리 장벽을 넘어" (tiptinker), section "1. FlashAttention": tiling and
+    recomputation); the gradients themselves are plain calculus:
+        P  = softmax rows of S,  S = scale * Q K^T (masked entries -inf)
+        dV = P^T dO
+        dP = dO V^T
+        dS = P * (dP - rowsum(P * dP))      (the softmax Jacobian applied row by row)
+        dQ = scale * dS K,   dK = scale * dS^T Q
+    q, do [Nq, d]; k, v [Nk, d].  Returns dq [Nq, d], dk, dv [Nk, d] (float64)."""
+    rows = np.arange(q.shape[0])
+    p, _, _ = softmax_rows(attention_scores(q, k, scale, causal, rows, q.shape[0]))
+    dv = p.T @ do
+    dp = do @ v.T
+    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv
+
+
+def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
+                       scale: float, causal: bool):
+    """Backward of attention_prefill: q, do [B,Hq,Nq,d]; k, v [B,Hkv,Nk,d].  With grouped
+    query heads, a KV head's dK and dV are the sums over the query heads that read it
+    (head h reads KV head h // (Hq / Hkv)).  Returns dq [B,Hq,Nq,d], dk, dv [B,Hkv,Nk,d]."""
+    B, Hq, Nq, d = q.shape
+    Hkv = k.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if causal and Nq > k.shape[2]:
+        raise ValueError("causal attention needs Nq <= Nk")
+    G = Hq // Hkv
+    dq = np.empty(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for b in range(B):
+        for h in range(Hq):
+            kvh = h // G
+            gq, gk, gv = attention_backward_head(q[b, h], k[b, kvh], v[b, kvh], do[b, h],
+                                                 scale, causal)
+            dq[b, h] = gq
+            dk[b, kvh] += gk
+            dv[b, kvh] += gv
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
 # FP8 (E4M3) KV cache
 # ---------------------------------------------------------------------------
 def e4m3_value(codes: np.ndarray) -> np.ndarray:

@@ -513,3 +513,99 @@ def test_fp8_paged_equals_contiguous():
                                   page_size=4)
     np.testing.assert_array_equal(o1, o0)
     np.testing.assert_array_equal(l1, l0)
+
+
+# ----------------------------------------------------------------------------- backward
+def _bwd_case(seed, B=1, Hq=2, Hkv=1, Nq=5, Nk=7, d=3):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((B, Hq, Nq, d)), rng.standard_normal((B, Hkv, Nk, d)),
+            rng.standard_normal((B, Hkv, Nk, d)), rng.standard_normal((B, Hq, Nq, d)))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Hq,Hkv,Nq,Nk", [(2, 2, 6, 6), (4, 2, 5, 9), (3, 1, 1, 4)])
+def test_backward_matches_torch_autograd(causal, Hq, Hkv, Nq, Nk):
+    """Autograd through torch's own fp64 matmul and softmax on the plain definition."""
+    import torch
+    from oracle import attention_backward
+    q, k, v, do = _bwd_case(80 + Nq, 2, Hq, Hkv, Nq, Nk, 4)
+    scale = 0.7
+    dq, dk, dv = attention_backward(q, k, v, do, scale, causal)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    G = Hq // Hkv
+    kr, vr = tk.repeat_interleave(G, dim=1), tv.repeat_interleave(G, dim=1)
+    s = scale * tq @ kr.transpose(-1, -2)
+    if causal:
+        vis = torch.arange(Nk)[None, :] <= torch.arange(Nq)[:, None] + (Nk - Nq)
+        s = s.masked_fill(~vis, float("-inf"))
+    o = torch.softmax(s, dim=-1) @ vr
+    o.backward(torch.tensor(do))
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_finite_differences(causal):
+    """Central differences of L = sum(dO * O) in every input coordinate."""
+    from oracle import attention_backward
+    q, k, v, do = _bwd_case(91, 1, 2, 1, 4, 5, 3)
+    scale = 0.9
+    loss = lambda q_, k_, v_: float((attention_prefill(q_, k_, v_, scale, causal)[0] * do).sum())
+    grads = attention_backward(q, k, v, do, scale, causal)
+    h = 1e-6
+    for x, g, idx in ((q, grads[0], 0), (k, grads[1], 1), (v, grads[2], 2)):
+        fd = np.zeros_like(x)
+        for pos in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[pos] += h
+            xm[pos] -= h
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[idx], args_m[idx] = xp, xm
+            fd[pos] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-7)
+
+
+def test_backward_single_key_and_zero_scale():
+    from oracle import attention_backward
+    # one key: O = V[0] for every row, so dV[0] = sum of dO rows and dQ = dK = 0
+    q, k, v, do = _bwd_case(92, 1, 2, 2, 4, 1, 3)
+    dq, dk, dv = attention_backward(q, k, v, do, 0.8, False)
+    assert np.abs(dq).max() < 1e-15 and np.abs(dk).max() < 1e-15
+    np.testing.assert_allclose(dv[0, :, 0], do[0].sum(axis=1), atol=1e-14)
+    # scale 0: uniform weights over the visible keys; dQ = dK = 0 and
+    # dV_j = sum over the queries i that see key j of dO_i / (number of keys i sees)
+    q, k, v, do = _bwd_case(93, 1, 1, 1, 5, 7, 3)
+    for causal in (False, True):
+        dq, dk, dv = attention_backward(q, k, v, do, 0.0, causal)
+        assert np.abs(dq).max() == 0 and np.abs(dk).max() == 0
+        n_vis = np.array([7 - 5 + i + 1 if causal else 7 for i in range(5)])
+        want = np.zeros((7, 3))
+        for i in range(5):
+            for j in range(n_vis[i]):
+                want[j] += do[0, 0, i] / n_vis[i]
+        np.testing.assert_allclose(dv[0, 0], want, atol=1e-14)
+
+
+def test_backward_gqa_is_sum_over_repeated_heads():
+    from oracle import attention_backward
+    q, k, v, do = _bwd_case(94, 2, 6, 2, 5, 8, 4)
+    dq, dk, dv = attention_backward(q, k, v, do, 0.5, True)
+    dq2, dk2, dv2 = attention_backward(q, np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1), do,
+                                       0.5, True)
+    np.testing.assert_allclose(dq, dq2, atol=1e-14)
+    np.testing.assert_allclose(dk, dk2.reshape(2, 2, 3, 8, 4).sum(axis=2), atol=1e-13)
+    np.testing.assert_allclose(dv, dv2.reshape(2, 2, 3, 8, 4).sum(axis=2), atol=1e-13)
+
+
+def test_backward_row_term_equals_do_dot_o():
+    """rowsum(P * dP) = rowsum(dO * O): the row term a kernel can take from O instead of P."""
+    from oracle.attention import attention_scores
+    q, k, v, do = _bwd_case(95, 1, 1, 1, 6, 9, 4)
+    for causal in (False, True):
+        p, _, _ = softmax_rows(attention_scores(q[0, 0], k[0, 0], 0.6, causal, np.arange(6), 6))
+        o = p @ v[0, 0]
+        dp = do[0, 0] @ v[0, 0].T
+        np.testing.assert_allclose((p * dp).sum(axis=1), (do[0, 0] * o).sum(axis=1),
+                                   atol=1e-13)
