@@ -25,7 +25,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 # Stream identifiers inside one workload seed.
-T_Q, T_K, T_V, T_LEN, T_PERM = 0, 1, 2, 3, 4
+T_Q, T_K, T_V, T_LEN, T_PERM, T_DO = 0, 1, 2, 3, 4, 5
 
 BF16_NAN = np.uint16(0x7FC0)
 E4M3_NAN = np.uint8(0x7F)
@@ -226,6 +226,16 @@ def prefill_inputs(cfg: PrefillCfg):
     return q, k, v
 
 
+def prefill_dout(cfg: PrefillCfg) -> np.ndarray:
+    """Output gradient dO [B, Hq, Nq, d] for the backward: bf16 bits (fp16 when cfg.f16)
+    of N(0,1) draws from its own stream."""
+    do = np.empty((cfg.B, cfg.Hq, cfg.Nq, cfg.d), np.uint16)
+    for b in range(cfg.B):
+        for h in range(cfg.Hq):
+            do[b, h] = normal_bf16(cfg.seed, T_DO, b, h, (cfg.Nq, cfg.d), f16=cfg.f16)
+    return do
+
+
 def custom_prefill(seed: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int,
                    q_mult: float = 1.0, f16: bool = False):
     """Inputs for an arbitrary prefill shape (edge cases), same recipe."""
@@ -355,6 +365,14 @@ def visible_pairs(Nq: int, Nk: int, causal: bool) -> int:
 def prefill_flops(cfg: PrefillCfg) -> int:
     """Algorithmic FLOPs: 2*d for Q.K^T plus 2*d for P.V per visible pair."""
     return 4 * cfg.d * cfg.B * cfg.Hq * visible_pairs(cfg.Nq, cfg.Nk, cfg.causal)
+
+
+def backward_flops(cfg: PrefillCfg) -> int:
+    """Algorithmic FLOPs of the backward: five products of 2*d per visible pair each
+    (dV = P^T dO, dP = dO V^T, dQ = dS K, dK = dS^T Q, and S = Q K^T recomputed), i.e.
+    2.5x the forward's count; the second recomputation of S and dP that a two-pass
+    kernel does is not counted."""
+    return 10 * cfg.d * cfg.B * cfg.Hq * visible_pairs(cfg.Nq, cfg.Nk, cfg.causal)
 
 
 def prefill_bytes(cfg: PrefillCfg) -> int:

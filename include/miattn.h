@@ -203,6 +203,38 @@ int attn_decode_num_splits(int B, int Hq, int Hkv, int d, int max_seqlen, int nu
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seqlen,
                                    int num_splits);
 
+/*
+ * Backward of attn_fwd_prefill (bf16): the gradients dq, dk, dv of the attention output
+ * for the output gradient dout, recomputing the attention weights tile by tile from the
+ * forward's LSE instead of storing them (tiling and recomputation: page "메모리 장벽을
+ * 넘어: LLM 연산자 가속 라이브러리 심층 분석" (tiptinker), section "1. FlashAttention").
+ * The gradients are those of O = softmax(scale * Q K^T [+ causal mask]) V:
+ *   dV = P^T dO,  dS = P * (dO V^T - rowsum(dO * O)),  dQ = scale * dS K,  dK = scale * dS^T Q,
+ * with dK, dV of a KV head summed over the query heads that read it.
+ *
+ *   q, o, dout, dq  [B, Hq, Nq, d] bf16      k, v, dk, dv  [B, Hkv, Nk, d] bf16
+ *   lse             [B, Hq, Nq] fp32: the LSE attn_fwd_prefill wrote for
+ *                   the same q, k, v, causal and scale (o likewise its output).
+ *   workspace       at least attn_bwd_workspace_bytes(B, Hq, Nq) bytes of device memory,
+ *                   16-byte aligned; its contents on entry do not matter.  Calls sharing it
+ *                   must be ordered on one stream.
+ *   dq, dk, dv are written in full (no accumulation into existing contents).  Results are
+ *   deterministic: no atomics are used.
+ *
+ * Errors: INVALID_ARGUMENT for a null or misaligned pointer, any size < 1, Hq % Hkv != 0,
+ * causal with Nq > Nk, a non-finite scale; UNSUPPORTED for d not in {64,128}, a grid
+ * beyond 2^31-1 workgroups, or one head's rows beyond 2^31-1 bytes; WORKSPACE when the
+ * workspace is missing or too small; HIP if a launch fails.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
+             int Nk, int d, int causal, float scale, void* workspace, size_t workspace_bytes,
+             hipStream_t stream);
+
+/* Workspace bytes attn_bwd needs: B*Hq*Nq*4 (the fp32 row terms rowsum(dO * O)) rounded
+ * up to 256.  Returns 0 for invalid arguments.  Pure host arithmetic; no HIP call. */
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* attn_status_string(int status);
 

@@ -70,6 +70,10 @@ def load_library():
     lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_decode_num_splits.argtypes = [i32] * 6
     lib.attn_decode_num_splits.restype = i32
+    lib.attn_bwd.argtypes = [vp] * 9 + [i32] * 7 + [f32, vp, ctypes.c_size_t, vp]
+    lib.attn_bwd.restype = i32
+    lib.attn_bwd_workspace_bytes.argtypes = [i32] * 3
+    lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_status_string.argtypes = [i32]
     lib.attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -357,7 +361,54 @@ def decode_fp8(q, kcache, vcache, seqlens, max_seqlen: int, k_scale: float, v_sc
     return o, lse
 
 
-__all__ = ["attn_fwd_prefill", "attn_fwd_prefill_f16", "attn_fwd_prefill_paged_f16",
+# -------------------------------------------------------------------------------- backward
+def attn_bwd_workspace_bytes(B, Hq, Nq) -> int:
+    return int(load_library().attn_bwd_workspace_bytes(B, Hq, Nq))
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal: bool, scale: float, workspace=None,
+             stream=None) -> None:
+    """Gradients of attn_fwd_prefill.  q, o, dout, dq [B,Hq,Nq,d] bf16; k, v, dk, dv
+    [B,Hkv,Nk,d] bf16; lse [B,Hq,Nq] fp32 (the forward's); workspace of at least
+    attn_bwd_workspace_bytes(B, Hq, Nq) bytes (allocated here when None)."""
+    lib = load_library()
+    _check(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk),
+                    ("dv", dv)):
+        _check(t, name, torch.bfloat16, 4, dev)
+    _check(lse, "lse", torch.float32, 3, dev)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if (tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape)
+            or tuple(dq.shape) != tuple(q.shape) or tuple(v.shape) != tuple(k.shape)
+            or tuple(dk.shape) != tuple(k.shape) or tuple(dv.shape) != tuple(k.shape)
+            or k.shape[0] != B or k.shape[3] != d or tuple(lse.shape) != (B, Hq, Nq)):
+        raise ValueError("shape mismatch between the backward's tensors")
+    if workspace is None:
+        workspace = torch.empty(attn_bwd_workspace_bytes(B, Hq, Nq), dtype=torch.uint8,
+                                device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                      _ptr(dk), _ptr(dv), B, Hq, Hkv, Nq, Nk, d, 1 if causal else 0,
+                      float(scale), _ptr(workspace), ws_bytes, _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd")
+
+
+def backward(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = None):
+    """Allocate dq, dk, dv and run attn_bwd.  scale None means 1/sqrt(d)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal, scale)
+    return dq, dk, dv
+
+
+__all__ = ["attn_bwd", "attn_bwd_workspace_bytes", "backward",
+           "attn_fwd_prefill", "attn_fwd_prefill_f16", "attn_fwd_prefill_paged_f16",
            "attn_fwd_decode", "attn_fwd_decode_f16", "attn_fwd_decode_fp8",
            "attn_decode_workspace_bytes", "decode_fp8",
            "attn_decode_num_splits", "attn_status_string", "prefill", "decode",

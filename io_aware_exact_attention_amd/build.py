@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libmiattn.so")
 SOURCES = [
     "csrc/prefill_gfx950.hip",
     "csrc/decode_gfx950.hip",
+    "csrc/backward_gfx950.hip",
     "csrc/miattn_api.cpp",
 ]
 FLAGS = [

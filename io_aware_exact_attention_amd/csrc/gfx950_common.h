@@ -62,6 +62,15 @@ __device__ __forceinline__ void lds_dma16(const void* base, int nbytes, uint32_t
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
 }
 
+// The same with 4 bytes per lane (buffer_load_dword ... lds): the wave's 256 bytes land
+// contiguously at dst, lane l at dst + 4*l.
+__device__ __forceinline__ void lds_dma4(const void* base, int nbytes, uint32_t voff,
+                                         lds_void* dst) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, kBufferFlags);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, voff, 0, 0, 0);
+}
+
 // 16-byte buffer load into registers: reads base + off (bytes) when off < nbytes, else
 // returns zeros.  CPOL is the instruction's cache-policy field (0: default).
 template <int CPOL = 0>
@@ -146,6 +155,33 @@ struct ElemF16 {
     return __builtin_bit_cast(uint16_t, (_Float16)x);
   }
 };
+
+// LDS tiles of D-wide bf16/fp16 rows (ROWB = 2*D bytes, unpadded) used by the prefill and
+// backward kernels.
+// XOR applied to the 16-byte chunk index of row R.  Chosen so that both LDS read
+// patterns are free of bank conflicts: the K operand read (16 lanes, 16 different rows,
+// same chunk) and the transposing V read (4 consecutive rows x 4 consecutive chunks).
+template <int D>
+__device__ __forceinline__ int chunk_swizzle(int R) {
+  if constexpr (D == 128) return ((R & 3) << 2) | ((R >> 2) & 3);
+  else return (((R >> 1) & 1) << 2) | ((R >> 2) & 3);
+}
+
+// Row index within a 32-key block that the MFMA A operand of lane l loads, chosen so
+// that accumulator r of lane group g holds key 16*(r/8) + 8*g + r%8: with that order
+// the 8 accumulators a lane contributes to one 16-key PV step are 8 consecutive keys.
+__device__ __forceinline__ int swap_bits_2_3(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

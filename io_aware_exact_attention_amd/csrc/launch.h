@@ -55,7 +55,27 @@ constexpr int kDecodeBlock = 32;
 constexpr int kDecodeWaves = 4;
 constexpr int kDecodeMaxSplits = 1024;  // chunks per sequence, at most
 
+// Backward (bf16): gradients of the prefill attention.  Layouts as for prefill; dvec is
+// the [B, Hq, Nq] fp32 workspace for D = rowsum(dO * O), written by the first kernel and
+// read by the second.
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;  // [B, Hq, Nq] natural-log log-sum-exp of the forward
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dvec;
+  int B, Hq, Hkv, Nq, Nk;
+  float scale;  // signed softmax scale
+  float c;      // scale * log2(e), signed
+};
+
 hipError_t launch_prefill(PrefillParams p, int d, int causal, hipStream_t stream);
+hipError_t launch_backward(const BwdParams& p, int d, int causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t stream);
 
 }  // namespace miattn

@@ -287,4 +287,49 @@ int attn_fwd_decode_fp8(const void* q, const void* kcache, const void* vcache,
                      num_splits, workspace, workspace_bytes, stream);
 }
 
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq) {
+  if (B < 1 || Hq < 1 || Nq < 1) return 0;
+  const size_t bytes = (size_t)B * Hq * Nq * 4;
+  return (bytes + 255) / 256 * 256;
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
+             int Nk, int d, int causal, float scale, void* workspace, size_t workspace_bytes,
+             hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return ATTN_ERR_INVALID_ARGUMENT;
+  if (Hq % Hkv || (causal && Nq > Nk) || !std::isfinite(scale)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  const long qtiles = (Nq + 127) / 128, ktiles = (Nk + 127) / 128;
+  if (qtiles * (long)Hq * B > 0x7fffffffL || ktiles * (long)Hkv * B > 0x7fffffffL)
+    return ATTN_ERR_UNSUPPORTED;
+  // one head's K (or Q) rows must fit a buffer descriptor's 32-bit byte range
+  if ((long)Nk * d * 2 > 0x7fffffffL || (long)Nq * d * 2 > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
+  const size_t need = attn_bwd_workspace_bytes(B, Hq, Nq);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return ATTN_ERR_WORKSPACE;
+
+  miattn::BwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<const uint16_t*>(o);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.dvec = static_cast<float*>(workspace);
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk;
+  p.scale = scale;
+  p.c = scale * 1.4426950408889634f;
+  (void)hipGetLastError();
+  return miattn::launch_backward(p, d, causal ? 1 : 0, stream) == hipSuccess ? ATTN_OK
+                                                                               : ATTN_ERR_HIP;
+}
+
 }  // extern "C"

@@ -55,31 +55,6 @@ struct PrefillShape {
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-// XOR applied to the 16-byte chunk index of row R.  Chosen so that both LDS read
-// patterns are free of bank conflicts: the K operand read (16 lanes, 16 different rows,
-// same chunk) and the transposing V read (4 consecutive rows x 4 consecutive chunks).
-template <int D>
-__device__ __forceinline__ int chunk_swizzle(int R) {
-  if constexpr (D == 128) return ((R & 3) << 2) | ((R >> 2) & 3);
-  else return (((R >> 1) & 1) << 2) | ((R >> 2) & 3);
-}
-
-// Row index within a 32-key block that the MFMA A operand of lane l loads, chosen so
-// that accumulator r of lane group g holds key 16*(r/8) + 8*g + r%8: with that order
-// the 8 accumulators a lane contributes to one 16-key PV step are 8 consecutive keys.
-__device__ __forceinline__ int swap_bits_2_3(int r) {
-  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 // Workgroup barrier that is also a hard scheduling boundary: no instruction (memory or
 // ALU) is moved across it, so the MFMA and softmax phases of the two wave groups stay
 // where the schedule puts them.  The LDS DMA writes are ordered by explicit vmcnt waits

@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["attn_fwd_prefill", "attn_fwd_prefill_paged",
                                            "attn_fwd_prefill_f16", "attn_fwd_prefill_paged_f16",
                                            "attn_fwd_decode", "attn_fwd_decode_f16",
-                                           "attn_fwd_decode_fp8",
+                                           "attn_fwd_decode_fp8", "attn_bwd",
+                                           "attn_bwd_workspace_bytes",
                                            "attn_decode_workspace_bytes",
                                            "attn_decode_num_splits", "attn_status_string"])
 
@@ -180,6 +181,32 @@ def test_f16_paged_and_decode_validate_like_bf16(lib):
         args += [ctypes.c_float(a["scale"]), a["splits"], a["ws"], a["ws_bytes"], None]
         assert lib.attn_fwd_decode_f16(*args) == status
         assert lib.attn_fwd_decode(*args) == status
+
+
+def bwd(lib, ws_bytes=1 << 20, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, B=1, Hq=2, Hkv=1, Nq=4, Nk=4,
+             d=64, causal=1, scale=0.125, ws=P)
+    a.update(kw)
+    return lib.attn_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"], a["dk"],
+                        a["dv"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["causal"],
+                        ctypes.c_float(a["scale"]), a["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(lse=None), INVALID), (dict(dout=None), INVALID),
+    (dict(dq=None), INVALID), (dict(dk=MIS), INVALID), (dict(lse=ctypes.c_void_p(4096 + 2)), INVALID),
+    (dict(B=0), INVALID), (dict(Nk=0), INVALID), (dict(Hq=3, Hkv=2), INVALID),
+    (dict(Nq=5, Nk=4, causal=1), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(Nq=16, Nk=(1 << 23) + 1, d=128), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE),
+])
+def test_backward_validation(lib, kw, status):
+    assert bwd(lib, **kw) == status
+
+
+def test_backward_workspace_arithmetic(lib):
+    assert mi.attn_bwd_workspace_bytes(2, 8, 100) == (2 * 8 * 100 * 4 + 255) // 256 * 256
+    assert mi.attn_bwd_workspace_bytes(0, 8, 100) == 0
 
 
 def test_decode_split_plan(lib):

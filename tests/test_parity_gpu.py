@@ -16,8 +16,8 @@ import torch
 
 import attn_inputs as ai
 import io_aware_exact_attention_amd as mi
-from oracle import (attention_decode, attention_decode_fp8, attention_prefill,
-                    attention_prefill_paged, attention_rows, gather_paged)
+from oracle import (attention_backward, attention_decode, attention_decode_fp8,
+                    attention_prefill, attention_prefill_paged, attention_rows, gather_paged)
 
 pytestmark = pytest.mark.gpu
 
@@ -629,3 +629,91 @@ def test_decode_f16(paged, splits):
     ro, rl = attention_decode(h64(q), h64(kc), h64(vc), lens, cfg.scale, table, 16)
     check(f"decode f16 paged={paged} splits={splits}", o, lse, ro, rl)
     assert (o[0] == 0).all() and torch.isinf(lse[0]).all()
+
+
+# ------------------------------------------------------------------ backward
+# Bar for gradients (the forward bar is for outputs of order one; gradients have no fixed
+# scale, so errors are measured relative to the reference gradient's size): per tensor,
+# max|err| <= 2e-2 * max(max|ref|, 1e-2) and mean|err| <= 1e-2 * max(mean|ref|, 1e-2).
+# Derivation: P and dS are rounded to bf16 before their products (relative 2^-9 each) and
+# the outputs are bf16 (relative 2^-9), so the expected relative error is a few times
+# 2^-9 ~ 0.2-0.6%.  The 1e-2 floor covers gradients that vanish exactly (one visible key,
+# scale 0): there the kernel's dS is the difference of rowsum(dO*O), with O the forward's
+# bf16 output, and rowsum(P*dP), which differ by ~2^-9 of dO*V, not by zero.
+BWD_REL_MAX, BWD_REL_MEAN, BWD_FLOOR = 2e-2, 1e-2, 1e-2
+
+
+def check_grads(label, got, ref):
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        x = g.float().cpu().numpy().astype(np.float64)
+        assert x.shape == r.shape, (name, x.shape, r.shape)
+        assert np.isfinite(x).all(), f"{label} {name}: non-finite"
+        err = np.abs(x - r)
+        scale_max = max(np.abs(r).max(), BWD_FLOOR)
+        scale_mean = max(np.abs(r).mean(), BWD_FLOOR)
+        log_case(f"{label} {name}", rel_max=float(err.max() / scale_max),
+                 rel_mean=float(err.mean() / scale_mean), ref_max=float(scale_max))
+        assert err.max() <= BWD_REL_MAX * scale_max, f"{label} {name}: max {err.max():.3e}"
+        assert err.mean() <= BWD_REL_MEAN * scale_mean, f"{label} {name}: mean {err.mean():.3e}"
+
+
+def run_bwd(q, k, v, do, causal, scale):
+    dq_, dk_, dv_ = (dev(x).reshape(x.shape) for x in (q, k, v))
+    o, lse = mi.prefill(dq_, dk_, dv_, causal, scale)
+    gdo = dev(do).reshape(do.shape)
+    grads = mi.backward(dq_, dk_, dv_, o, lse, gdo, causal, scale)
+    torch.cuda.synchronize()
+    return grads
+
+
+def bwd_inputs(seed, B, Hq, Hkv, Nq, Nk, d):
+    q, k, v = ai.custom_prefill(seed=seed, B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nk=Nk, d=d)
+    do = ai.prefill_dout(ai.PrefillCfg("bwd", B, Hq, Hkv, Nq, Nk, d, True, seed))
+    return q, k, v, do
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("Nq,Nk", [(1, 1), (17, 17), (65, 65), (130, 130), (300, 300),
+                                   (64, 200), (100, 333)])
+def test_backward_shapes(Nq, Nk, causal, d):
+    q, k, v, do = bwd_inputs(7000 + Nq + Nk + d, 1, 2, 2, Nq, Nk, d)
+    scale = 1 / math.sqrt(d)
+    got = run_bwd(q, k, v, do, causal, scale)
+    ref = attention_backward(f64(q), f64(k), f64(v), f64(do), scale, causal)
+    check_grads(f"bwd Nq={Nq} Nk={Nk} causal={causal} d={d}", got, ref)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.2, 0.6])
+def test_backward_gqa_and_scale(scale):
+    q, k, v, do = bwd_inputs(7100, 2, 8, 2, 150, 150, 64)
+    got = run_bwd(q, k, v, do, True, scale)
+    ref = attention_backward(f64(q), f64(k), f64(v), f64(do), float(np.float32(scale)), True)
+    if scale == 0.0:
+        assert (got[0] == 0).all() and (got[1] == 0).all()   # dQ = dK = 0 exactly
+        ref = (ref[0], ref[1], ref[2])
+        check_grads("bwd GQA scale=0 (dv)", got[2:], ref[2:])
+        return
+    check_grads(f"bwd GQA scale={scale}", got, ref)
+
+
+def test_backward_is_deterministic():
+    q, k, v, do = bwd_inputs(7200, 1, 4, 2, 700, 700, 128)
+    g1 = run_bwd(q, k, v, do, True, 0.09)
+    g2 = run_bwd(q, k, v, do, True, 0.09)
+    for a_, b_ in zip(g1, g2):
+        assert torch.equal(a_, b_)
+
+
+def test_backward_llama2_shape():
+    cfg = ai.CONFIGS["llama2_7b_prefill"]
+    q, k, v = ai.prefill_inputs(cfg)
+    do = ai.prefill_dout(cfg)
+    dq, dk, dv = run_bwd(q, k, v, do, cfg.causal, cfg.scale)
+    got = [x.float().cpu().numpy() for x in (dq, dk, dv)]
+    for (b, h) in [(0, 0), (3, 31), (2, 9)]:
+        ref = attention_backward(f64(q[b:b + 1, h:h + 1]), f64(k[b:b + 1, h:h + 1]),
+                                 f64(v[b:b + 1, h:h + 1]), f64(do[b:b + 1, h:h + 1]),
+                                 cfg.scale, cfg.causal)
+        check_grads(f"bwd llama2 head ({b},{h})",
+                    [torch.from_numpy(x[b:b + 1, h:h + 1]) for x in got], ref)
