@@ -47,7 +47,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-extra", action="store_true",
                    help="skip the other workloads (non-causal, 32K and fp16 prefill, contiguous and "
-                        "FP8-cache decode, chunked prefill)")
+                        "FP8-cache decode, backward, chunked prefill)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle sample")
     p.add_argument("--settle-ms", type=float, default=300.0,
@@ -371,6 +371,23 @@ def main():
                                          "frac": round(gbs / PEAK_HBM_GBS, 4),
                                          "speedup_vs_bf16_cache": round(d_avg / avg, 3)}
         del fq, fkc, fvc, ftab, fseq, fo, fl, fws
+        torch.cuda.empty_cache()
+        # backward of the causal Llama-2-shaped prefill (dQ, dK, dV from the stored LSE)
+        cfg, (bq, bk, bv, bo, bl) = prefill_setup("llama2_7b_prefill")
+        bdo = to_dev(ai.prefill_dout(cfg))
+        mi.attn_fwd_prefill(bq, bk, bv, bo, bl, cfg.causal, cfg.scale, stream)
+        gq, gk, gv = torch.empty_like(bq), torch.empty_like(bk), torch.empty_like(bv)
+        bws = torch.empty(mi.attn_bwd_workspace_bytes(cfg.B, cfg.Hq, cfg.Nq), dtype=torch.uint8,
+                          device="cuda")
+        avg, med, mn = time_kernel(
+            lambda: mi.attn_bwd(bq, bk, bv, bo, bl, bdo, gq, gk, gv, cfg.causal, cfg.scale, bws,
+                                stream), args.steps, args.warmup)
+        tf = ai.backward_flops(cfg) / (avg * 1e-6) / 1e12
+        extra["llama2_7b_backward"] = {"us": round(avg, 2), "us_min": round(mn, 2),
+                                       "TFLOP/s": round(tf, 2),
+                                       "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                                       "flops": ai.backward_flops(cfg)}
+        del bq, bk, bv, bo, bl, bdo, gq, gk, gv, bws
         torch.cuda.empty_cache()
         # chunked prefill against a paged cache (512 new tokens per sequence)
         cfg = ai.CONFIGS["chunked_prefill_paged"]
