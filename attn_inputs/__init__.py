@@ -194,6 +194,11 @@ CONFIGS = {
     "paged_gqa_decode_fp8": DecodeCfg("paged_gqa_decode_fp8", B=8, Hq=32, Hkv=8, d=128,
                                       seed=5, paged=True, page_size=16,
                                       len_range=(1024, 131072), kv_fp8=True),
+    # Ragged batch of prompts (self-attention, causal) packed along tokens: 16 sequences
+    # of 256..4096 tokens, Llama-2-style GQA heads.  B, Hq, Hkv, d as listed; the lengths
+    # come from varlen_lengths(seed, B, *len_range).
+    "varlen_prefill": DecodeCfg("varlen_prefill", B=16, Hq=32, Hkv=8, d=128, seed=8,
+                                paged=False, len_range=(256, 4096)),
     # Chunked prefill against a paged cache: 512 new tokens per sequence appended to
     # contexts (which already hold them) of 2048..16384 tokens, Llama-2-style GQA heads.
     "chunked_prefill_paged": DecodeCfg("chunked_prefill_paged", B=8, Hq=32, Hkv=8, d=128,
@@ -241,6 +246,35 @@ def custom_prefill(seed: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: in
     """Inputs for an arbitrary prefill shape (edge cases), same recipe."""
     cfg = PrefillCfg("custom", B, Hq, Hkv, Nq, Nk, d, True, seed, q_mult, f16)
     return prefill_inputs(cfg)
+
+
+# ----------------------------------------------------------------------------
+# Variable-length (ragged) prefill inputs
+# ----------------------------------------------------------------------------
+def varlen_inputs(seed: int, lens_q, lens_k, Hq: int, Hkv: int, d: int):
+    """Packed ragged batch: q [total_q, Hq, d], k, v [total_k, Hkv, d] bf16 bits and the
+    cumulative lengths cu_q, cu_k (int32 [B+1]).  Sequence b, head h draws its rows from
+    the same per-(b, h) streams as the dense layout does, so each sequence equals a dense
+    prefill input of its own length."""
+    lens_q = np.asarray(lens_q, np.int64)
+    lens_k = np.asarray(lens_k, np.int64)
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    q = np.empty((int(cu_q[-1]), Hq, d), np.uint16)
+    k = np.empty((int(cu_k[-1]), Hkv, d), np.uint16)
+    v = np.empty_like(k)
+    for b in range(len(lens_q)):
+        for h in range(Hq):
+            q[cu_q[b]:cu_q[b + 1], h] = normal_bf16(seed, T_Q, b, h, (int(lens_q[b]), d))
+        for h in range(Hkv):
+            k[cu_k[b]:cu_k[b + 1], h] = normal_bf16(seed, T_K, b, h, (int(lens_k[b]), d))
+            v[cu_k[b]:cu_k[b + 1], h] = normal_bf16(seed, T_V, b, h, (int(lens_k[b]), d))
+    return q, k, v, cu_q, cu_k
+
+
+def varlen_lengths(seed: int, B: int, lo: int, hi: int) -> np.ndarray:
+    """B sequence lengths uniform in [lo, hi] from the lengths stream."""
+    return _stream(seed, T_LEN).integers(lo, hi, size=B, endpoint=True).astype(np.int32)
 
 
 # ----------------------------------------------------------------------------
@@ -398,6 +432,12 @@ def decode_bytes(cfg: DecodeCfg, lengths: np.ndarray) -> int:
 
 def decode_flops(cfg: DecodeCfg, lengths: np.ndarray) -> int:
     return 4 * cfg.d * cfg.Hq * int(np.sum(lengths, dtype=np.int64))
+
+
+def varlen_flops(lens_q, lens_k, Hq: int, d: int, causal: bool) -> int:
+    """Algorithmic FLOPs of a ragged batch: 4*d per visible pair of each sequence."""
+    return 4 * d * Hq * sum(visible_pairs(int(a), int(b), causal) for a, b in zip(lens_q, lens_k)
+                            if a > 0)
 
 
 def chunk_q(cfg: DecodeCfg) -> np.ndarray:

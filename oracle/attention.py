@@ -160,6 +160,38 @@ def attention_decode(q: np.ndarray, kcache: np.ndarray, vcache: np.ndarray,
 
 
 # ---------------------------------------------------------------------------
+# Variable-length (ragged) batch packed along tokens
+# ---------------------------------------------------------------------------
+def attention_prefill_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q: np.ndarray,
+                             cu_k: np.ndarray, scale: float, causal: bool):
+    """A ragged batch (the continuous-batching shape of the page "Transformers optimization
+    overview", section on continuous batching) packed along tokens: q [total_q, Hq, d],
+    k, v [total_k, Hkv, d]; sequence b owns query rows cu_q[b]:cu_q[b+1] and key rows
+    cu_k[b]:cu_k[b+1], and its queries attend only to its own keys (bottom-right causal per
+    sequence).  A sequence without keys gets O = 0, LSE = -inf.  Returns O [total_q, Hq, d]
+    and LSE [Hq, total_q] (float64)."""
+    total_q, Hq, d = q.shape
+    Hkv = k.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    o = np.zeros((total_q, Hq, d))
+    lse = np.full((Hq, total_q), -np.inf)
+    for b in range(len(cu_q) - 1):
+        qs, qe, ks, ke = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        nq, nk = qe - qs, ke - ks
+        if nq == 0 or nk == 0:
+            continue
+        if causal and nq > nk:
+            raise ValueError("causal attention needs Nq <= Nk in every sequence")
+        rows = np.arange(nq)
+        for h in range(Hq):
+            o[qs:qe, h], lse[h, qs:qe] = attention_rows(q[qs:qe, h], k[ks:ke, h // G],
+                                                        v[ks:ke, h // G], scale, causal, rows, nq)
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
 # Backward: gradients of the definition
 # ---------------------------------------------------------------------------
 def attention_backward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,

@@ -172,3 +172,14 @@ def test_f16_variant_rounds_the_same_draws():
     dc = ai.DecodeCfg("t", B=1, Hq=2, Hkv=1, d=8, seed=3, paged=False, fixed_len=5, f16=True)
     assert (ai.build_contig_cache(dc, ai.T_K, np.array([3], np.int32), 5)[0, 0, 3:]
             == ai.F16_NAN).all()
+
+
+def test_varlen_inputs_pack_the_dense_streams():
+    q, k, v, cu_q, cu_k = ai.varlen_inputs(9, [3, 0, 5], [4, 2, 6], 4, 2, 8)
+    assert q.shape == (8, 4, 8) and k.shape == (12, 2, 8)
+    assert cu_q.tolist() == [0, 3, 3, 8] and cu_k.tolist() == [0, 4, 6, 12]
+    np.testing.assert_array_equal(q[3:8, 1], ai.normal_bf16(9, ai.T_Q, 2, 1, (5, 8)))
+    np.testing.assert_array_equal(v[4:6, 0], ai.normal_bf16(9, ai.T_V, 1, 0, (2, 8)))
+    lens = ai.varlen_lengths(8, 16, 256, 4096)
+    assert lens.shape == (16,) and lens.min() >= 256 and lens.max() <= 4096
+    assert ai.varlen_flops([2, 3], [2, 5], 1, 1, True) == 4 * (3 + 3 + 4 + 5)

@@ -609,3 +609,49 @@ def test_backward_row_term_equals_do_dot_o():
         dp = do[0, 0] @ v[0, 0].T
         np.testing.assert_allclose((p * dp).sum(axis=1), (do[0, 0] * o).sum(axis=1),
                                    atol=1e-13)
+
+
+# ----------------------------------------------------------------------------- varlen
+def _varlen_case(seed, lens_q, lens_k, Hq=2, Hkv=1, d=3):
+    rng = np.random.default_rng(seed)
+    tq, tk = sum(lens_q), sum(lens_k)
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    return (rng.standard_normal((tq, Hq, d)), rng.standard_normal((tk, Hkv, d)),
+            rng.standard_normal((tk, Hkv, d)), cu_q, cu_k)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_matches_brute_force_per_sequence(causal):
+    from oracle import attention_prefill_varlen
+    lens_q, lens_k = [3, 1, 4, 2], [5, 1, 4, 6]
+    q, k, v, cu_q, cu_k = _varlen_case(101, lens_q, lens_k, Hq=4, Hkv=2)
+    o, lse = attention_prefill_varlen(q, k, v, cu_q, cu_k, 0.8, causal)
+    for b in range(4):
+        for h in range(4):
+            qs, qe, ks, ke = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+            bo, bl = brute_force_attention(q[qs:qe, h].tolist(), k[ks:ke, h // 2].tolist(),
+                                           v[ks:ke, h // 2].tolist(), 0.8, causal)
+            np.testing.assert_allclose(o[qs:qe, h], np.array(bo), atol=1e-12)
+            np.testing.assert_allclose(lse[h, qs:qe], np.array(bl), atol=1e-12)
+
+
+def test_varlen_sequence_order_and_empty_sequences():
+    from oracle import attention_prefill_varlen
+    lens_q, lens_k = [3, 0, 5, 2], [4, 2, 5, 0]
+    q, k, v, cu_q, cu_k = _varlen_case(102, lens_q, lens_k)
+    o, lse = attention_prefill_varlen(q, k, v, cu_q, cu_k, 0.5, False)
+    # the empty-query sequence writes nothing; the key-less one gives O = 0, LSE = -inf
+    assert (o[cu_q[3]:cu_q[4]] == 0).all() and (lse[:, cu_q[3]:cu_q[4]] == -np.inf).all()
+    # reversing the sequence order reverses the outputs' blocks
+    order = [3, 2, 1, 0]
+    qb = [q[cu_q[b]:cu_q[b + 1]] for b in order]
+    kb = [k[cu_k[b]:cu_k[b + 1]] for b in order]
+    vb = [v[cu_k[b]:cu_k[b + 1]] for b in order]
+    cq = np.concatenate([[0], np.cumsum([lens_q[b] for b in order])]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum([lens_k[b] for b in order])]).astype(np.int32)
+    o2, l2 = attention_prefill_varlen(np.concatenate(qb), np.concatenate(kb), np.concatenate(vb),
+                                      cq, ck, 0.5, False)
+    for i, b in enumerate(order):
+        np.testing.assert_array_equal(o2[cq[i]:cq[i + 1]], o[cu_q[b]:cu_q[b + 1]])
+        np.testing.assert_array_equal(l2[:, cq[i]:cq[i + 1]], lse[:, cu_q[b]:cu_q[b + 1]])
