@@ -47,7 +47,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-extra", action="store_true",
                    help="skip the other workloads (non-causal, 32K and fp16 prefill, contiguous and "
-                        "FP8-cache decode, backward, chunked prefill)")
+                        "FP8-cache decode, varlen prefill, backward, chunked prefill)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle sample")
     p.add_argument("--settle-ms", type=float, default=300.0,
@@ -371,6 +371,26 @@ def main():
                                          "frac": round(gbs / PEAK_HBM_GBS, 4),
                                          "speedup_vs_bf16_cache": round(d_avg / avg, 3)}
         del fq, fkc, fvc, ftab, fseq, fo, fl, fws
+        torch.cuda.empty_cache()
+        # ragged batch of 16 prompts (256..4096 tokens) packed along tokens, causal
+        cfg = ai.CONFIGS["varlen_prefill"]
+        vl = ai.varlen_lengths(cfg.seed, cfg.B, *cfg.len_range)
+        vq, vk, vv, vcq, vck = ai.varlen_inputs(cfg.seed, vl, vl, cfg.Hq, cfg.Hkv, cfg.d)
+        vq, vk, vv = to_dev(vq).reshape(vq.shape), to_dev(vk).reshape(vk.shape), \
+            to_dev(vv).reshape(vv.shape)
+        vcq, vck = torch.from_numpy(vcq).cuda(), torch.from_numpy(vck).cuda()
+        vo = torch.empty_like(vq)
+        vlse = torch.empty((cfg.Hq, vq.shape[0]), dtype=torch.float32, device="cuda")
+        mx = int(vl.max())
+        avg, med, mn = time_kernel(
+            lambda: mi.attn_fwd_prefill_varlen(vq, vk, vv, vo, vlse, vcq, vck, mx, mx, True,
+                                               cfg.scale, stream), args.steps, args.warmup)
+        fl = ai.varlen_flops(vl, vl, cfg.Hq, cfg.d, True)
+        tf = fl / (avg * 1e-6) / 1e12
+        extra["varlen_prefill"] = {"us": round(avg, 2), "us_min": round(mn, 2),
+                                   "TFLOP/s": round(tf, 2), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                                   "lengths": [int(x) for x in vl]}
+        del vq, vk, vv, vcq, vck, vo, vlse
         torch.cuda.empty_cache()
         # backward of the causal Llama-2-shaped prefill (dQ, dK, dV from the stored LSE)
         cfg, (bq, bk, bv, bo, bl) = prefill_setup("llama2_7b_prefill")

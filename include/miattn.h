@@ -125,6 +125,32 @@ int attn_fwd_prefill_paged_f16(const void* q, const void* kcache, const void* vc
                                float scale, hipStream_t stream);
 
 /*
+ * Variable-length (ragged) batched prefill: B sequences of different lengths packed along
+ * the token axis, the batch shape of continuous batching (page "Transformers optimization
+ * overview", section on continuous batching).  Sequence b owns query rows
+ * [cu_seqlens_q[b], cu_seqlens_q[b+1]) and key rows [cu_seqlens_k[b], cu_seqlens_k[b+1]);
+ * its queries attend only to its own keys (bottom-right aligned when causal, per sequence).
+ *
+ *   q, o   [total_q, Hq, d] bf16 (token-major)      k, v  [total_k, Hkv, d] bf16
+ *   lse    [Hq, total_q] fp32 (written) or NULL
+ *   cu_seqlens_q, cu_seqlens_k  [B + 1] int32, DEVICE memory (not read on the host):
+ *          cu[0] = 0, non-decreasing, cu[B] = total.  Sequence lengths must not exceed
+ *          max_seqlen_q / max_seqlen_k.  A sequence with queries needs at least one key
+ *          (and, when causal, at least as many keys as queries); one with no queries is
+ *          skipped.  Values are clamped to [0, total] on the device, so no value reads
+ *          outside the tensors; a sequence with no keys gets o = 0 and lse = -inf.
+ *
+ * Errors: INVALID_ARGUMENT for a null required pointer, misalignment, any size < 1,
+ * Hq % Hkv != 0, a max length above its total, a non-finite scale; UNSUPPORTED for d not
+ * in {64,128} or a grid beyond 2^31-1 workgroups; HIP if the launch fails.
+ */
+int attn_fwd_prefill_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
+                            int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                            int max_seqlen_k, int d, int causal, float scale,
+                            hipStream_t stream);
+
+/*
  * Decode: one query per sequence against the sequence's KV cache, split along the
  * KV length into chunks whose partial results are merged by log-sum-exp.
  *

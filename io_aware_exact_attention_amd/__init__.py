@@ -70,6 +70,8 @@ def load_library():
     lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_decode_num_splits.argtypes = [i32] * 6
     lib.attn_decode_num_splits.restype = i32
+    lib.attn_fwd_prefill_varlen.argtypes = [vp] * 7 + [i32] * 9 + [f32, vp]
+    lib.attn_fwd_prefill_varlen.restype = i32
     lib.attn_bwd.argtypes = [vp] * 9 + [i32] * 7 + [f32, vp, ctypes.c_size_t, vp]
     lib.attn_bwd.restype = i32
     lib.attn_bwd_workspace_bytes.argtypes = [i32] * 3
@@ -214,6 +216,48 @@ def prefill_paged(q, kcache, vcache, block_table, kv_lens, max_kv_len: int, caus
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     fn = attn_fwd_prefill_paged_f16 if q.dtype == torch.float16 else attn_fwd_prefill_paged
     fn(q, kcache, vcache, block_table, kv_lens, o, lse, max_kv_len, causal, scale)
+    return o, lse
+
+
+def attn_fwd_prefill_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+                            max_seqlen_k: int, causal: bool, scale: float, stream=None) -> None:
+    """Ragged batch packed along tokens: q/o [total_q,Hq,d], k/v [total_k,Hkv,d] bf16;
+    cu_seqlens_q/k int32 [B+1] (device); lse [Hq,total_q] fp32 or None."""
+    lib = load_library()
+    _check(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _check(k, "k", torch.bfloat16, 3, dev)
+    _check(v, "v", torch.bfloat16, 3, dev)
+    _check(o, "o", torch.bfloat16, 3, dev)
+    _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1, dev)
+    _check(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1, dev)
+    total_q, Hq, d = q.shape
+    total_k, Hkv, dk = k.shape
+    B = cu_seqlens_q.shape[0] - 1
+    if (dk != d or tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape)
+            or cu_seqlens_k.shape[0] != B + 1):
+        raise ValueError("shape mismatch between q, k, v, o or the cumulative lengths")
+    if lse is not None:
+        _check(lse, "lse", torch.float32, 2, dev)
+        if tuple(lse.shape) != (Hq, total_q):
+            raise ValueError("lse must be [Hq, total_q]")
+    st = lib.attn_fwd_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                     _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, Hq, Hkv, total_q,
+                                     total_k, int(max_seqlen_q), int(max_seqlen_k), d,
+                                     1 if causal else 0, float(scale), _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_prefill_varlen")
+
+
+def prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                   causal: bool = True, scale: float | None = None):
+    """Allocate O and LSE and run attn_fwd_prefill_varlen.  scale None means 1/sqrt(d)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    o = torch.empty_like(q)
+    lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    attn_fwd_prefill_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                            max_seqlen_k, causal, scale)
     return o, lse
 
 
@@ -407,7 +451,8 @@ def backward(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = N
     return dq, dk, dv
 
 
-__all__ = ["attn_bwd", "attn_bwd_workspace_bytes", "backward",
+__all__ = ["attn_bwd", "attn_bwd_workspace_bytes", "backward", "attn_fwd_prefill_varlen",
+           "prefill_varlen",
            "attn_fwd_prefill", "attn_fwd_prefill_f16", "attn_fwd_prefill_paged_f16",
            "attn_fwd_decode", "attn_fwd_decode_f16", "attn_fwd_decode_fp8",
            "attn_decode_workspace_bytes", "decode_fp8",

@@ -25,6 +25,12 @@ struct PrefillParams {
   const int32_t* kv_lens;
   int max_blocks;
   int f16;  // Q, K, V, O are fp16 (else bf16)
+  // Varlen (cu_q non-null): q, o are [total_q, Hq, D] and k, v [total_k, Hkv, D], sequence
+  // b owning rows [cu_q[b], cu_q[b+1]) and [cu_k[b], cu_k[b+1]); lse is [Hq, total_q].
+  // Nq and Nk are then the longest sequence's lengths.
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int total_q, total_k;
 };
 
 struct DecodeParams {

@@ -242,6 +242,45 @@ int attn_fwd_prefill_paged_f16(const void* q, const void* kcache, const void* vc
                             true, stream);
 }
 
+int attn_fwd_prefill_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
+                            int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                            int max_seqlen_k, int d, int causal, float scale,
+                            hipStream_t stream) {
+  if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (lse && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (B < 1 || Hq < 1 || Hkv < 1 || total_q < 1 || total_k < 1 || max_seqlen_q < 1 ||
+      max_seqlen_k < 1 || d < 1)
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (Hq % Hkv || max_seqlen_q > total_q || max_seqlen_k > total_k || !std::isfinite(scale))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  const long qtiles = (max_seqlen_q + 255) / 256;
+  if (qtiles * (long)Hq * B > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
+  // 64 key rows of the packed K (row stride Hkv*d*2 bytes) must fit a buffer descriptor
+  if (64L * Hkv * d * 2 > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
+
+  miattn::PrefillParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = max_seqlen_q; p.Nk = max_seqlen_k;
+  p.c = std::fabs(scale) * 1.4426950408889634f;
+  p.negate_q = scale < 0.f;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.total_q = total_q;
+  p.total_k = total_k;
+  (void)hipGetLastError();
+  return miattn::launch_prefill(p, d, causal ? 1 : 0, stream) == hipSuccess ? ATTN_OK
+                                                                             : ATTN_ERR_HIP;
+}
+
 int attn_decode_num_splits(int B, int Hq, int Hkv, int d, int max_seqlen, int num_splits) {
   if (!decode_sizes_ok(B, Hq, Hkv, d, max_seqlen) || num_splits < 0) return 0;
   return plan_decode(B, Hq, Hkv, max_seqlen, num_splits).splits;

@@ -107,9 +107,9 @@ struct PagedItem {
   int b, hq, qrank;
 };
 
-__device__ __forceinline__ int sequence_of_rank(int r, int B, const int32_t* kv_lens, int lane) {
+// `mine` is lane l's sequence length (for l < B).
+__device__ __forceinline__ int sequence_of_rank(int r, int B, int mine, int lane) {
   if (B > 64) return r;
-  const int mine = lane < B ? kv_lens[lane] : -1;
   int rank = 0;
   for (int j = 0; j < B; ++j) {
     const int o = __builtin_amdgcn_readlane(mine, j);
@@ -119,8 +119,8 @@ __device__ __forceinline__ int sequence_of_rank(int r, int B, const int32_t* kv_
   return (int)__builtin_ctzll(hit);
 }
 
-__device__ __forceinline__ PagedItem paged_work_item(int p, int B, int Hq, int nq,
-                                                     const int32_t* kv_lens, int lane) {
+__device__ __forceinline__ PagedItem paged_work_item(int p, int B, int Hq, int nq, int mine,
+                                                     int lane) {
   int r, hq, qr;
   if ((Hq & 7) == 0) {
     const int hpx = Hq >> 3;
@@ -136,13 +136,16 @@ __device__ __forceinline__ PagedItem paged_work_item(int p, int B, int Hq, int n
     qr = rem % nq;
   }
   PagedItem it;
-  it.b = sequence_of_rank(r, B, kv_lens, lane);
+  it.b = sequence_of_rank(r, B, mine, lane);
   it.hq = hq;
   it.qrank = qr;
   return it;
 }
 
-template <int D, bool CAUSAL, bool PAGED, typename E>
+// Layouts: dense [B, H, N, D] (PAGED and VARLEN false); PAGED: K/V in the paged cache,
+// kv_lens per sequence; VARLEN: sequences packed along the token axis, [total, H, D], with
+// cumulative lengths cu_q, cu_k.
+template <int D, bool CAUSAL, bool PAGED, bool VARLEN, typename E>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillParams a) {
   using S = PrefillShape<D>;
@@ -156,8 +159,11 @@ void prefill_kernel(PrefillParams a) {
 
   // --- workgroup -> (query tile, head, batch)
   int hq, b, qrank;
-  if (PAGED) {
-    const PagedItem pi = paged_work_item(blockIdx.x, a.B, a.Hq, a.num_qtiles, a.kv_lens, lane);
+  if (PAGED || VARLEN) {
+    int mine = -1;  // lane l: length of sequence l, the key count that ranks sequences
+    if (lane < a.B)
+      mine = PAGED ? a.kv_lens[lane] : a.cu_k[lane + 1] - a.cu_k[lane];
+    const PagedItem pi = paged_work_item(blockIdx.x, a.B, a.Hq, a.num_qtiles, mine, lane);
     hq = pi.hq;
     b = pi.b;
     qrank = pi.qrank;
@@ -167,22 +173,57 @@ void prefill_kernel(PrefillParams a) {
     b = wi.bh / a.Hq;
     qrank = wi.qrank;
   }
-  const int qtile = CAUSAL ? (a.num_qtiles - 1 - qrank) : qrank;
+  // Queries and keys of this sequence.  Dense: Nq and Nk.  Paged: Nq and the sequence's
+  // context length (which includes the Nq new queries as its last tokens).  Varlen: the
+  // sequence's rows [cu[b], cu[b+1]) of the packed tensors, clamped to the totals so that
+  // no cumulative-length value can send a read outside them.
+  int nq = a.Nq, nk = PAGED ? a.kv_lens[b] : a.Nk;
+  int q_start = 0, k_start = 0;
+  if (VARLEN) {
+    q_start = min(max(a.cu_q[b], 0), a.total_q);
+    nq = min(max(a.cu_q[b + 1], q_start), a.total_q) - q_start;
+    k_start = min(max(a.cu_k[b], 0), a.total_k);
+    nk = min(max(a.cu_k[b + 1], k_start), a.total_k) - k_start;
+  }
+  // Varlen query tiles are counted per sequence (the grid covers the longest); the causal
+  // order is reversed per sequence so that each one's heaviest tile goes first.
+  const int nqt = VARLEN ? (nq + S::BM - 1) / S::BM : a.num_qtiles;
+  if (VARLEN && qrank >= nqt) return;
+  const int qtile = CAUSAL ? (nqt - 1 - qrank) : qrank;
   const int kvh = hq / (a.Hq / a.Hkv);
   const int m0 = qtile * S::BM;
-  // Keys of this sequence: Nk, or (paged cache) its own context length, which includes
-  // the Nq new queries as its last tokens.
-  const int nk = PAGED ? a.kv_lens[b] : a.Nk;
-  const int off = nk - a.Nq;  // bottom-right causal alignment
+  const int off = nk - nq;  // bottom-right causal alignment
 
-  const uint16_t* __restrict__ Qh = a.q + (size_t)(b * a.Hq + hq) * a.Nq * D;
-  const uint16_t* __restrict__ Kh = PAGED ? a.k : a.k + (size_t)(b * a.Hkv + kvh) * a.Nk * D;
-  const uint16_t* __restrict__ Vh = PAGED ? a.v : a.v + (size_t)(b * a.Hkv + kvh) * a.Nk * D;
+  // Row strides in elements: one head's consecutive query (key) rows.
+  const size_t qstride = VARLEN ? (size_t)a.Hq * D : D;
+  const size_t kstride = VARLEN ? (size_t)a.Hkv * D : D;
+  const uint16_t* __restrict__ Qh =
+      VARLEN ? a.q + ((size_t)q_start * a.Hq + hq) * D : a.q + (size_t)(b * a.Hq + hq) * a.Nq * D;
+  const uint16_t* __restrict__ Kh =
+      PAGED ? a.k
+            : (VARLEN ? a.k + ((size_t)k_start * a.Hkv + kvh) * D
+                      : a.k + (size_t)(b * a.Hkv + kvh) * a.Nk * D);
+  const uint16_t* __restrict__ Vh =
+      PAGED ? a.v
+            : (VARLEN ? a.v + ((size_t)k_start * a.Hkv + kvh) * D
+                      : a.v + (size_t)(b * a.Hkv + kvh) * a.Nk * D);
 
   // keys the workgroup needs: everything, or up to the diagonal of its last query
   int kend = nk;
-  if (CAUSAL) kend = min(nk, min(m0 + S::BM, a.Nq) - 1 + off + 1);
+  if (CAUSAL) kend = min(nk, min(m0 + S::BM, nq) - 1 + off + 1);
   const int ntiles = (kend + S::BN - 1) / S::BN;
+  if (VARLEN && ntiles <= 0) {
+    // no visible key (a sequence without keys): O = 0, LSE = -inf
+    for (int idx = tid; idx < S::BM * (D / 8); idx += 64 * S::kWaves) {
+      const int row = m0 + idx / (D / 8);
+      if (row < nq)
+        *(u32x4*)(a.o + ((size_t)(q_start + row) * a.Hq + hq) * D + (idx % (D / 8)) * 8) =
+            u32x4{0, 0, 0, 0};
+    }
+    if (a.lse && tid < S::BM && m0 + tid < nq)
+      a.lse[(size_t)hq * a.total_q + q_start + m0 + tid] = -INFINITY;
+    return;
+  }
 
   // This wave's 32 query rows.  The two groups interleave 32-row blocks so that both
   // reach the causal diagonal at about the same tile.
@@ -193,12 +234,14 @@ void prefill_kernel(PrefillParams a) {
   // that KB.  The buffer descriptor of tile j starts at its first key row and covers the
   // rows left, so rows past Nk read as zeros (their scores are masked).  The per-lane
   // offsets are the same for every tile; all per-tile address work is scalar.
+  // (Varlen rows are kstride apart in memory; the LDS layout is the same.)
+  const int krow_bytes = VARLEN ? (int)kstride * 2 : S::ROWB;
   uint32_t dma_off[S::DMA];
 #pragma unroll
   for (int i = 0; i < S::DMA; ++i) {
     const int p = (i * S::kWaves + wave) * 64 + lane;
     const int R = p / S::CPR;
-    dma_off[i] = R * S::ROWB + (((p % S::CPR) ^ chunk_swizzle<D>(R)) << 4);
+    dma_off[i] = R * krow_bytes + (((p % S::CPR) ^ chunk_swizzle<D>(R)) << 4);
   }
   // Paged cache [pages, Hkv, 16, D]: each 1 KB DMA block (RPB rows) lies inside one
   // 16-token page and gets its own descriptor.  The page ids of a tile's blocks are read
@@ -236,6 +279,19 @@ void prefill_kernel(PrefillParams a) {
         lds_dma16(Kh + off, nbytes, lo, (lds_void*)(st + blk * 1024));
         lds_dma16(Vh + off, nbytes, lo, (lds_void*)(st + S::TILE + blk * 1024));
       }
+    } else if (VARLEN) {
+      // the range ends with the sequence's last key row inside this tile, so rows past it
+      // (the next sequence's) read as zeros
+      const int rows = min(nk - n0, S::BN);
+      const int nbytes = __builtin_amdgcn_readfirstlane((rows - 1) * krow_bytes + S::ROWB);
+      const uint16_t* kt = Kh + (size_t)n0 * kstride;
+      const uint16_t* vt = Vh + (size_t)n0 * kstride;
+#pragma unroll
+      for (int i = 0; i < S::DMA; ++i) {
+        const int blk = i * S::kWaves + wave;
+        lds_dma16(kt, nbytes, dma_off[i], (lds_void*)(st + blk * 1024));
+        lds_dma16(vt, nbytes, dma_off[i], (lds_void*)(st + S::TILE + blk * 1024));
+      }
     } else {
       const int nbytes = (nk - n0) * (D * 2);
       const uint16_t* kt = Kh + (size_t)n0 * D;
@@ -254,11 +310,11 @@ void prefill_kernel(PrefillParams a) {
   bf16x8 qop[D / 16];
   {
     const uint32_t flip = a.negate_q ? 0x80008000u : 0u;
-    const u32x4* src = (const u32x4*)(Qh + (size_t)min(qrow, a.Nq - 1) * D);
+    const u32x4* src = (const u32x4*)(Qh + (size_t)min(qrow, nq - 1) * qstride);
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       u32x4 w = src[2 * s + g];
-      if (qrow >= a.Nq) w = u32x4{0, 0, 0, 0};
+      if (qrow >= nq) w = u32x4{0, 0, 0, 0};
       w ^= flip;
       qop[s] = __builtin_bit_cast(bf16x8, w);
     }
@@ -514,9 +570,10 @@ void prefill_kernel(PrefillParams a) {
 
   // --- epilogue: O = acc / l -> bf16; LSE = m*scale + ln l
   const float l_tot = l_ex + wave_xor(l_ex, 32);
-  if (qrow < a.Nq) {
+  if (qrow < nq) {
     const float inv = 1.f / l_tot;
-    uint16_t* orow = a.o + ((size_t)(b * a.Hq + hq) * a.Nq + qrow) * D;
+    uint16_t* orow = VARLEN ? a.o + ((size_t)(q_start + qrow) * a.Hq + hq) * D
+                            : a.o + ((size_t)(b * a.Hq + hq) * a.Nq + qrow) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -527,18 +584,22 @@ void prefill_kernel(PrefillParams a) {
         *(u32x2*)(orow + dv) = w;
       }
     if (g == 0 && a.lse)
-      a.lse[(size_t)(b * a.Hq + hq) * a.Nq + qrow] = (m_run * c + log2f(l_tot)) * kLn2;
+      a.lse[VARLEN ? (size_t)hq * a.total_q + q_start + qrow
+                   : (size_t)(b * a.Hq + hq) * a.Nq + qrow] = (m_run * c + log2f(l_tot)) * kLn2;
   }
 }
 
 template <int D, bool CAUSAL, typename E>
 static hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
   if (p.block_table)
-    hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, true, E>), dim3(p.total_wg), dim3(512), 0,
-                       stream, p);
+    hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, true, false, E>), dim3(p.total_wg), dim3(512),
+                       0, stream, p);
+  else if (p.cu_q)
+    hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, false, true, E>), dim3(p.total_wg), dim3(512),
+                       0, stream, p);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, false, E>), dim3(p.total_wg), dim3(512), 0,
-                       stream, p);
+    hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, false, false, E>), dim3(p.total_wg), dim3(512),
+                       0, stream, p);
   return hipGetLastError();
 }
 

@@ -33,6 +33,7 @@ def test_header_declares_the_entry_points():
                                            "attn_fwd_prefill_f16", "attn_fwd_prefill_paged_f16",
                                            "attn_fwd_decode", "attn_fwd_decode_f16",
                                            "attn_fwd_decode_fp8", "attn_bwd",
+                                           "attn_fwd_prefill_varlen",
                                            "attn_bwd_workspace_bytes",
                                            "attn_decode_workspace_bytes",
                                            "attn_decode_num_splits", "attn_status_string"])
@@ -207,6 +208,28 @@ def test_backward_validation(lib, kw, status):
 def test_backward_workspace_arithmetic(lib):
     assert mi.attn_bwd_workspace_bytes(2, 8, 100) == (2 * 8 * 100 * 4 + 255) // 256 * 256
     assert mi.attn_bwd_workspace_bytes(0, 8, 100) == 0
+
+
+def varlen(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, cu_q=P, cu_k=P, B=2, Hq=4, Hkv=2, total_q=100,
+             total_k=120, max_q=60, max_k=70, d=128, causal=1, scale=0.1)
+    a.update(kw)
+    return lib.attn_fwd_prefill_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu_q"],
+                                       a["cu_k"], a["B"], a["Hq"], a["Hkv"], a["total_q"],
+                                       a["total_k"], a["max_q"], a["max_k"], a["d"], a["causal"],
+                                       ctypes.c_float(a["scale"]), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(cu_q=None), INVALID), (dict(cu_k=None), INVALID),
+    (dict(k=MIS), INVALID), (dict(cu_k=ctypes.c_void_p(4098)), INVALID),
+    (dict(lse=ctypes.c_void_p(4098)), INVALID), (dict(B=0), INVALID), (dict(total_q=0), INVALID),
+    (dict(max_k=0), INVALID), (dict(Hq=3, Hkv=2), INVALID), (dict(max_q=101), INVALID),
+    (dict(max_k=121), INVALID), (dict(scale=float("nan")), INVALID), (dict(d=96), UNSUPPORTED),
+    (dict(B=65536, Hq=65536, Hkv=1, total_q=1 << 20, max_q=1 << 20), UNSUPPORTED),
+])
+def test_varlen_validation(lib, kw, status):
+    assert varlen(lib, **kw) == status
 
 
 def test_decode_split_plan(lib):

@@ -17,7 +17,8 @@ import torch
 import attn_inputs as ai
 import io_aware_exact_attention_amd as mi
 from oracle import (attention_backward, attention_decode, attention_decode_fp8,
-                    attention_prefill, attention_prefill_paged, attention_rows, gather_paged)
+                    attention_prefill, attention_prefill_paged, attention_prefill_varlen,
+                    attention_rows, gather_paged)
 
 pytestmark = pytest.mark.gpu
 
@@ -717,3 +718,77 @@ def test_backward_llama2_shape():
                                  cfg.scale, cfg.causal)
         check_grads(f"bwd llama2 head ({b},{h})",
                     [torch.from_numpy(x[b:b + 1, h:h + 1]) for x in got], ref)
+
+
+# ------------------------------------------------------------------ varlen (ragged) prefill
+def run_varlen(q, k, v, cu_q, cu_k, causal, scale):
+    mq = int(np.diff(cu_q).max())
+    mk = int(np.diff(cu_k).max())
+    o, lse = mi.prefill_varlen(dev(q).reshape(q.shape), dev(k).reshape(k.shape),
+                               dev(v).reshape(v.shape), torch.from_numpy(cu_q).cuda(),
+                               torch.from_numpy(cu_k).cuda(), max(mq, 1), max(mk, 1), causal,
+                               scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("lens_q,lens_k", [
+    ([1, 255, 256, 257, 700], [1, 255, 256, 257, 700]),        # self-attention, tile edges
+    ([5, 0, 300, 64], [40, 17, 300, 1000]),                      # Nq < Nk, an empty chunk
+    ([513], [513]),
+])
+def test_prefill_varlen(d, causal, lens_q, lens_k):
+    q, k, v, cu_q, cu_k = ai.varlen_inputs(7500 + d + len(lens_q), lens_q, lens_k, 4, 2, d)
+    scale = 1 / math.sqrt(d)
+    o, lse = run_varlen(q, k, v, cu_q, cu_k, causal, scale)
+    ro, rl = attention_prefill_varlen(f64(q), f64(k), f64(v), cu_q, cu_k, scale, causal)
+    check(f"varlen d={d} causal={causal} lens_q={lens_q} lens_k={lens_k}", o, lse, ro, rl)
+
+
+def test_prefill_varlen_sequence_without_keys():
+    q, k, v, cu_q, cu_k = ai.varlen_inputs(7600, [10, 20], [30, 0], 2, 2, 64)
+    o, lse = run_varlen(q, k, v, cu_q, cu_k, False, 0.125)
+    assert (o[10:] == 0).all() and torch.isinf(lse[:, 10:]).all()
+    ro, rl = attention_prefill_varlen(f64(q), f64(k), f64(v), cu_q, cu_k, 0.125, False)
+    check("varlen sequence without keys", o, lse, ro, rl)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_varlen_single_sequence_equals_dense(causal):
+    """One sequence packed along tokens is the dense prefill with the layout transposed:
+    the same tiles in the same order, so the same bits."""
+    n, Hq, Hkv, d = 777, 8, 2, 128
+    q, k, v, cu_q, cu_k = ai.varlen_inputs(7700, [n], [n], Hq, Hkv, d)
+    o, lse = run_varlen(q, k, v, cu_q, cu_k, causal, 0.09)
+    qd = np.ascontiguousarray(q.transpose(1, 0, 2))[None]
+    kd = np.ascontiguousarray(k.transpose(1, 0, 2))[None]
+    vd = np.ascontiguousarray(v.transpose(1, 0, 2))[None]
+    od, ld = run_prefill(qd, kd, vd, causal, 0.09)
+    assert torch.equal(o, od[0].transpose(0, 1)) and torch.equal(lse, ld[0])
+
+
+def test_prefill_varlen_config_sampled():
+    cfg = ai.CONFIGS["varlen_prefill"]
+    lens = ai.varlen_lengths(cfg.seed, cfg.B, *cfg.len_range)
+    q, k, v, cu_q, cu_k = ai.varlen_inputs(cfg.seed, lens, lens, cfg.Hq, cfg.Hkv, cfg.d)
+    o, lse = run_varlen(q, k, v, cu_q, cu_k, True, cfg.scale)
+    go, gl = o.float().cpu().numpy(), lse.cpu().numpy()
+    rng = np.random.default_rng(19)
+    errs, lerrs = [], []
+    G = cfg.Hq // cfg.Hkv
+    for b in rng.choice(cfg.B, 4, replace=False):
+        qs, qe = int(cu_q[b]), int(cu_q[b + 1])
+        n = qe - qs
+        for h in rng.choice(cfg.Hq, 2, replace=False):
+            rows = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, 32)]))
+            ro, rl = attention_rows(f64(q[qs + rows, h]), f64(k[qs:qe, h // G]),
+                                    f64(v[qs:qe, h // G]), cfg.scale, True, rows, n)
+            errs.append(np.abs(go[qs + rows, h] - ro).ravel())
+            lerrs.append(np.abs(gl[h, qs + rows] - rl).ravel())
+    err, lerr = np.concatenate(errs), np.concatenate(lerrs)
+    log_case("varlen_prefill (sampled)", max_abs=float(err.max()), mean_abs=float(err.mean()),
+             lse_max_abs=float(lerr.max()))
+    assert np.isfinite(go).all()
+    assert err.max() <= TOL_MAX and err.mean() <= TOL_MEAN and lerr.max() <= TOL_LSE
