@@ -99,7 +99,9 @@ int attn_fwd_prefill_f16(const void* q, const void* k, const void* v, void* o, f
  *   kcache, vcache [num_pages, Hkv, page_size, d] bf16, 16-byte aligned, page_size == 16
  *   block_table [B, max_blocks_per_seq] int32, DEVICE memory: token t of sequence b is
  *          slot t % 16 of page block_table[b, t / 16].  Entries for tokens < kv_lens[b]
- *          must lie in [0, num_pages); other entries are never read.
+ *          must lie in [0, num_pages); other entries are never read.  Entries outside
+ *          that range are clamped into it on the device: the result is then unspecified,
+ *          but no read leaves the cache.
  *   kv_lens [B] int32, DEVICE memory, each in [Nq, max_kv_len] (not read on the host)
  *   o      [B, Hq, Nq, d] bf16 (written), 16-byte aligned
  *   lse    [B, Hq, Nq] fp32 (written) or NULL
@@ -167,6 +169,8 @@ int attn_fwd_prefill_varlen(const void* q, const void* k, const void* v, void* o
  *     block_table [B, max_blocks_per_seq] int32, DEVICE memory; token t of sequence b
  *     is slot t % page_size of page block_table[b, t / page_size].  Entries for
  *     tokens < seqlens[b] must lie in [0, num_pages); other entries are never read.
+ *     Entries outside that range are clamped into it on the device: the result is then
+ *     unspecified, but no read leaves the cache.
  *     Needs max_blocks_per_seq >= ceil(max_seqlen / page_size).
  *   Cache rows at or past seqlens[b] are never read (they may hold anything).
  *   num_splits: number of KV chunks per sequence; 0 picks one automatically.  The

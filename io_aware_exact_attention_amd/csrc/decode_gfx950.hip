@@ -137,8 +137,10 @@ void decode_split_kernel(DecodeParams a) {
         const int tg = tbk(wave + W * (32 * pg_win + (lane >> 1))) + 16 * (lane & 1);
         pg_lane = tg < t1 ? table[tg >> 4] : 0;
       }
-      p0 = __builtin_amdgcn_readlane(pg_lane, 2 * (j & 31));
-      p1 = __builtin_amdgcn_readlane(pg_lane, 2 * (j & 31) + 1);
+      // page ids are clamped into the pool: a bad table entry reads a wrong page, never
+      // memory outside the cache
+      p0 = (int)min((uint32_t)__builtin_amdgcn_readlane(pg_lane, 2 * (j & 31)), a.page_max);
+      p1 = (int)min((uint32_t)__builtin_amdgcn_readlane(pg_lane, 2 * (j & 31) + 1), a.page_max);
     }
   };
   // One 32-key block = two 16-token groups (a page of the paged cache, 16 consecutive

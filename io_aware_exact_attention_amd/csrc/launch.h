@@ -24,6 +24,7 @@ struct PrefillParams {
   const int32_t* block_table;
   const int32_t* kv_lens;
   int max_blocks;
+  uint32_t page_max;  // num_pages - 1: page ids are clamped to it
   int f16;  // Q, K, V, O are fp16 (else bf16)
   // Varlen (cu_q non-null): q, o are [total_q, Hq, D] and k, v [total_k, Hkv, D], sequence
   // b owning rows [cu_q[b], cu_q[b+1]) and [cu_k[b], cu_k[b+1]); lse is [Hq, total_q].
@@ -46,6 +47,7 @@ struct DecodeParams {
   int B, Hq, Hkv, G, ngroups;
   int max_seqlen;  // row count of the contiguous cache
   int max_blocks;  // block-table row length (paged)
+  uint32_t page_max;  // num_pages - 1 (paged): page ids are clamped to it
   int num_splits, chunk;
   float c;        // |scale| * log2(e), times the K scale of an FP8 cache
   int negate_q;

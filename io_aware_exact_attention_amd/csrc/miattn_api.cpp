@@ -111,6 +111,7 @@ int decode_impl(const void* q, const void* kcache, const void* vcache,
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = G; p.ngroups = ngroups;
   p.max_seqlen = max_seqlen;
   p.max_blocks = block_table ? max_blocks_per_seq : 0;
+  p.page_max = block_table ? (uint32_t)(num_pages - 1) : 0u;
   p.num_splits = pl.splits;
   p.chunk = pl.chunk;
   p.c = std::fabs(scale) * 1.4426950408889634f;
@@ -189,6 +190,7 @@ int prefill_paged_impl(const void* q, const void* kcache, const void* vcache,
   p.block_table = block_table;
   p.kv_lens = kv_lens;
   p.max_blocks = max_blocks_per_seq;
+  p.page_max = (uint32_t)(num_pages - 1);
   p.f16 = f16;
   (void)hipGetLastError();
   return miattn::launch_prefill(p, d, causal ? 1 : 0, stream) == hipSuccess ? ATTN_OK

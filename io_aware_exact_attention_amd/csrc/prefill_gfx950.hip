@@ -256,7 +256,8 @@ void prefill_kernel(PrefillParams a) {
 #pragma unroll
     for (int i = 0; i < S::DMA; ++i) {
       const int tok0 = j * S::BN + (i * S::kWaves + wave) * RPB;
-      pg_next[i] = tok0 < nk ? tbl[tok0 >> 4] : 0;
+      // clamped into the pool: a bad table entry reads a wrong page, never memory outside
+      pg_next[i] = tok0 < nk ? (int)min((uint32_t)tbl[tok0 >> 4], a.page_max) : 0;
     }
   };
   if (PAGED) fetch_pages(0);

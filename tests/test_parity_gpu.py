@@ -792,3 +792,44 @@ def test_prefill_varlen_config_sampled():
              lse_max_abs=float(lerr.max()))
     assert np.isfinite(go).all()
     assert err.max() <= TOL_MAX and err.mean() <= TOL_MEAN and lerr.max() <= TOL_LSE
+
+
+# ------------------------------------------------------------------ bad page-table entries
+def test_out_of_range_page_ids_are_clamped_into_the_pool():
+    """Table entries outside [0, num_pages) are clamped to the nearest end on the device
+    (negative ids, read as unsigned, to num_pages - 1): the result equals, bit for bit, a
+    run whose table holds num_pages - 1 there, and every other sequence's result is the
+    same as with a valid table.  (Caches padded with zeros so that all results are
+    finite.)"""
+    zero = np.uint16(0)
+    lens = np.array([300, 77, 500], np.int32)
+    cfg = ai.DecodeCfg("clamp", B=3, Hq=8, Hkv=2, d=128, seed=1990, paged=True)
+    lay = ai.paged_layout(lens, 16, cfg.seed, extra_pages=3)
+    q = ai.decode_q(cfg)
+    kc = ai.build_paged_cache(cfg, ai.T_K, lens, lay, pad_bits=zero)
+    vc = ai.build_paged_cache(cfg, ai.T_V, lens, lay, pad_bits=zero)
+    last = kc.shape[0] - 1
+    bad, clamped = lay.block_table.copy(), lay.block_table.copy()
+    bad[0, 1], bad[0, 3] = -1, kc.shape[0] + 5
+    clamped[0, 1], clamped[0, 3] = last, last
+    maxlen = int(lens.max())
+    o_ok, l_ok = run_decode(q, kc, vc, lens, lay.block_table, maxlen, cfg.scale, 2)
+    o_bad, l_bad = run_decode(q, kc, vc, lens, bad, maxlen, cfg.scale, 2)
+    o_cl, l_cl = run_decode(q, kc, vc, lens, clamped, maxlen, cfg.scale, 2)
+    assert torch.equal(o_bad, o_cl) and torch.equal(l_bad, l_cl)
+    assert torch.equal(o_ok[1:], o_bad[1:]) and torch.equal(l_ok[1:], l_bad[1:])
+    # the same for chunked prefill against the paged cache
+    ccfg = ai.DecodeCfg("clamp_chunk", B=3, Hq=4, Hkv=2, d=128, seed=1991, paged=True, chunk=77)
+    clay = ai.paged_layout(lens, 16, ccfg.seed, extra_pages=3)
+    cq = ai.chunk_q(ccfg)
+    ckc = ai.build_paged_cache(ccfg, ai.T_K, lens, clay, pad_bits=zero)
+    cvc = ai.build_paged_cache(ccfg, ai.T_V, lens, clay, pad_bits=zero)
+    clast = ckc.shape[0] - 1
+    cbad, ccl = clay.block_table.copy(), clay.block_table.copy()
+    cbad[0, 2], cbad[2, 5] = -7, ckc.shape[0] + 100
+    ccl[0, 2], ccl[2, 5] = clast, clast
+    ok = run_chunk(cq, ckc, cvc, lens, clay.block_table, True, 0.09)
+    bd = run_chunk(cq, ckc, cvc, lens, cbad, True, 0.09)
+    cl = run_chunk(cq, ckc, cvc, lens, ccl, True, 0.09)
+    assert torch.equal(bd[0], cl[0]) and torch.equal(bd[1], cl[1])
+    assert torch.equal(ok[0][1], bd[0][1]) and torch.equal(ok[1][1], bd[1][1])
