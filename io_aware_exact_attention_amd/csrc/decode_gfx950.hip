@@ -3,9 +3,10 @@
 // The KV length of every sequence is cut into chunks of `chunk` tokens.  One workgroup
 // (4 waves) handles one (chunk, KV head, batch) and serves all query heads that share
 // that KV head (up to 16 per workgroup), so every cached K/V byte is read from HBM once.
-// Each wave takes every 4th 32-key block of the chunk: the block is loaded with
-// coalesced 16-byte loads (16 lanes per 256-byte row, one block ahead in registers),
-// staged in the wave's own LDS slice, and consumed by 16x16x32 bf16 MFMAs:
+// Each wave takes every 4th 32-key block of the chunk: the block is loaded with coalesced
+// 16-byte buffer loads (16 lanes per 256-byte row; two blocks ahead in registers, three for
+// an FP8 cache), staged in the wave's own LDS slice, and consumed by 16x16x32 MFMAs (bf16,
+// or fp16 for fp16 inputs):
 //   S^T = K_blk Q^T  (queries on lanes, keys in accumulators), online softmax,
 //   O^T += V_blk^T P^T (V^T through the transposing LDS read).
 // The four waves' states are merged in LDS.  With one chunk the workgroup writes O and

@@ -37,7 +37,7 @@ constexpr float kRescaleLog2 = 8.0f;
 // 4x16 block; lane i receives column i of that block (rows 0..3).
 //
 // The restrict-qualified pointer gives each such read an alias scope of its own.  The
-// compiler then does not make the read wait for every LDS DMA (global_load_lds) still in
+// compiler then does not make the read wait for every LDS DMA (buffer_load ... lds) still in
 // flight; kernels that fill LDS by DMA order those writes and the reads themselves, with
 // explicit vmcnt waits followed by a workgroup barrier.
 __device__ __forceinline__ bf16x4 lds_read_tr(const char* __restrict__ p) {

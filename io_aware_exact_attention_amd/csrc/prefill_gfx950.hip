@@ -2,9 +2,10 @@
 //
 // One workgroup (8 waves, one workgroup per CU) owns BM = 256 queries of one
 // (batch, head); each wave owns 32 of them.  Key/value tiles of BN = 64 rows stream from
-// HBM straight into a 4-stage LDS ring (global_load_lds_dwordx4, issued two tiles ahead,
+// HBM straight into a 4-stage LDS ring (buffer_load_dwordx4 ... lds, issued two tiles ahead,
 // no register staging).  Per tile and wave:
-//   S^T = K_t Q^T       32x32x16 bf16 MFMA; K rows from LDS, Q^T held in registers.
+//   S^T = K_t Q^T       32x32x16 MFMA (bf16, or fp16 for fp16 inputs); K rows from LDS,
+//                       Q^T held in registers.
 //                       Keys land in accumulator registers, queries on lanes, so the
 //                       row max / row sum of a query are in-lane plus one exchange.
 //   online softmax      running max m and sum l per query; P = exp2(S*c - m*c)
@@ -434,10 +435,11 @@ void prefill_kernel(PrefillParams a) {
   // Online softmax of tile j held in sacc; MASK applies the causal diagonal and the ragged
   // key tail.  The weights are formed against the current reference max m_run first.  The
   // max is only recomputed, the two lanes of a query exchange theirs and O and l are
-  // rescaled, when some weight of the tile exceeds 2^kRedoLog2 (the reference has fallen
+  // rescaled, when the tile's weight sum exceeds E::kRedoBound (the reference has fallen
   // far behind the scores) or could not be formed at all.  On the first tile m_run is -inf,
   // so every weight is +inf or NaN and that path runs.  Otherwise the weights stay at most
-  // 2^kRedoLog2, far inside the fp32 and bf16 range, and the result is the same softmax.
+  // E::kRedoBound, inside the range of fp32 and of the element type, and the result is the
+  // same softmax.
   const int lim = CAUSAL ? min(nk - 1, qrow + off) : nk - 1;  // last visible key
   auto softmax = [&](int j, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
