@@ -251,11 +251,11 @@ def custom_prefill(seed: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: in
 # ----------------------------------------------------------------------------
 # Variable-length (ragged) prefill inputs
 # ----------------------------------------------------------------------------
-def varlen_inputs(seed: int, lens_q, lens_k, Hq: int, Hkv: int, d: int):
-    """Packed ragged batch: q [total_q, Hq, d], k, v [total_k, Hkv, d] bf16 bits and the
-    cumulative lengths cu_q, cu_k (int32 [B+1]).  Sequence b, head h draws its rows from
-    the same per-(b, h) streams as the dense layout does, so each sequence equals a dense
-    prefill input of its own length."""
+def varlen_inputs(seed: int, lens_q, lens_k, Hq: int, Hkv: int, d: int, f16: bool = False):
+    """Packed ragged batch: q [total_q, Hq, d], k, v [total_k, Hkv, d] bf16 bits (fp16 when
+    f16) and the cumulative lengths cu_q, cu_k (int32 [B+1]).  Sequence b, head h draws its
+    rows from the same per-(b, h) streams as the dense layout does, so each sequence equals
+    a dense prefill input of its own length."""
     lens_q = np.asarray(lens_q, np.int64)
     lens_k = np.asarray(lens_k, np.int64)
     cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
@@ -265,10 +265,10 @@ def varlen_inputs(seed: int, lens_q, lens_k, Hq: int, Hkv: int, d: int):
     v = np.empty_like(k)
     for b in range(len(lens_q)):
         for h in range(Hq):
-            q[cu_q[b]:cu_q[b + 1], h] = normal_bf16(seed, T_Q, b, h, (int(lens_q[b]), d))
+            q[cu_q[b]:cu_q[b + 1], h] = normal_bf16(seed, T_Q, b, h, (int(lens_q[b]), d), f16=f16)
         for h in range(Hkv):
-            k[cu_k[b]:cu_k[b + 1], h] = normal_bf16(seed, T_K, b, h, (int(lens_k[b]), d))
-            v[cu_k[b]:cu_k[b + 1], h] = normal_bf16(seed, T_V, b, h, (int(lens_k[b]), d))
+            k[cu_k[b]:cu_k[b + 1], h] = normal_bf16(seed, T_K, b, h, (int(lens_k[b]), d), f16=f16)
+            v[cu_k[b]:cu_k[b + 1], h] = normal_bf16(seed, T_V, b, h, (int(lens_k[b]), d), f16=f16)
     return q, k, v, cu_q, cu_k
 
 

@@ -152,6 +152,13 @@ int attn_fwd_prefill_varlen(const void* q, const void* k, const void* v, void* o
                             int max_seqlen_k, int d, int causal, float scale,
                             hipStream_t stream);
 
+/* attn_fwd_prefill_varlen with fp16 q, k, v and o (as in attn_fwd_prefill_f16). */
+int attn_fwd_prefill_varlen_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
+                                int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                                int max_seqlen_k, int d, int causal, float scale,
+                                hipStream_t stream);
+
 /*
  * Decode: one query per sequence against the sequence's KV cache, split along the
  * KV length into chunks whose partial results are merged by log-sum-exp.
@@ -261,7 +268,14 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              int Nk, int d, int causal, float scale, void* workspace, size_t workspace_bytes,
              hipStream_t stream);
 
-/* Workspace bytes attn_bwd needs: B*Hq*Nq*4 (the fp32 row terms rowsum(dO * O)) rounded
+/* attn_bwd with fp16 q, k, v, o, dout, dq, dk and dv (the backward of attn_fwd_prefill_f16);
+ * products take fp16 operands, accumulation and the softmax terms stay fp32. */
+int attn_bwd_f16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
+                 int Nk, int d, int causal, float scale, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
+/* Workspace bytes attn_bwd (and attn_bwd_f16) needs: B*Hq*Nq*4 (the fp32 row terms rowsum(dO * O)) rounded
  * up to 256.  Returns 0 for invalid arguments.  Pure host arithmetic; no HIP call. */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq);
 

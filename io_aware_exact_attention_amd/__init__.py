@@ -72,8 +72,12 @@ def load_library():
     lib.attn_decode_num_splits.restype = i32
     lib.attn_fwd_prefill_varlen.argtypes = [vp] * 7 + [i32] * 9 + [f32, vp]
     lib.attn_fwd_prefill_varlen.restype = i32
+    lib.attn_fwd_prefill_varlen_f16.argtypes = lib.attn_fwd_prefill_varlen.argtypes
+    lib.attn_fwd_prefill_varlen_f16.restype = i32
     lib.attn_bwd.argtypes = [vp] * 9 + [i32] * 7 + [f32, vp, ctypes.c_size_t, vp]
     lib.attn_bwd.restype = i32
+    lib.attn_bwd_f16.argtypes = lib.attn_bwd.argtypes
+    lib.attn_bwd_f16.restype = i32
     lib.attn_bwd_workspace_bytes.argtypes = [i32] * 3
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_status_string.argtypes = [i32]
@@ -219,16 +223,14 @@ def prefill_paged(q, kcache, vcache, block_table, kv_lens, max_kv_len: int, caus
     return o, lse
 
 
-def attn_fwd_prefill_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
-                            max_seqlen_k: int, causal: bool, scale: float, stream=None) -> None:
-    """Ragged batch packed along tokens: q/o [total_q,Hq,d], k/v [total_k,Hkv,d] bf16;
-    cu_seqlens_q/k int32 [B+1] (device); lse [Hq,total_q] fp32 or None."""
+def _varlen_call(fn, dtype, q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                 max_seqlen_k, causal, scale, stream):
     lib = load_library()
-    _check(q, "q", torch.bfloat16, 3)
+    _check(q, "q", dtype, 3)
     dev = q.device
-    _check(k, "k", torch.bfloat16, 3, dev)
-    _check(v, "v", torch.bfloat16, 3, dev)
-    _check(o, "o", torch.bfloat16, 3, dev)
+    _check(k, "k", dtype, 3, dev)
+    _check(v, "v", dtype, 3, dev)
+    _check(o, "o", dtype, 3, dev)
     _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1, dev)
     _check(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1, dev)
     total_q, Hq, d = q.shape
@@ -241,12 +243,28 @@ def attn_fwd_prefill_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seq
         _check(lse, "lse", torch.float32, 2, dev)
         if tuple(lse.shape) != (Hq, total_q):
             raise ValueError("lse must be [Hq, total_q]")
-    st = lib.attn_fwd_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                     _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, Hq, Hkv, total_q,
-                                     total_k, int(max_seqlen_q), int(max_seqlen_k), d,
-                                     1 if causal else 0, float(scale), _stream_handle(stream))
+    st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q),
+                          _ptr(cu_seqlens_k), B, Hq, Hkv, total_q, total_k, int(max_seqlen_q),
+                          int(max_seqlen_k), d, 1 if causal else 0, float(scale),
+                          _stream_handle(stream))
     if st != ATTN_OK:
-        raise AttnError(st, "attn_fwd_prefill_varlen")
+        raise AttnError(st, fn)
+
+
+def attn_fwd_prefill_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+                            max_seqlen_k: int, causal: bool, scale: float, stream=None) -> None:
+    """Ragged batch packed along tokens: q/o [total_q,Hq,d], k/v [total_k,Hkv,d] bf16;
+    cu_seqlens_q/k int32 [B+1] (device); lse [Hq,total_q] fp32 or None."""
+    _varlen_call("attn_fwd_prefill_varlen", torch.bfloat16, q, k, v, o, lse, cu_seqlens_q,
+                 cu_seqlens_k, max_seqlen_q, max_seqlen_k, causal, scale, stream)
+
+
+def attn_fwd_prefill_varlen_f16(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+                                max_seqlen_k: int, causal: bool, scale: float,
+                                stream=None) -> None:
+    """attn_fwd_prefill_varlen with fp16 q, k, v, o."""
+    _varlen_call("attn_fwd_prefill_varlen_f16", torch.float16, q, k, v, o, lse, cu_seqlens_q,
+                 cu_seqlens_k, max_seqlen_q, max_seqlen_k, causal, scale, stream)
 
 
 def prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
@@ -256,8 +274,8 @@ def prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_s
         scale = 1.0 / math.sqrt(q.shape[-1])
     o = torch.empty_like(q)
     lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
-    attn_fwd_prefill_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-                            max_seqlen_k, causal, scale)
+    fn = attn_fwd_prefill_varlen_f16 if q.dtype == torch.float16 else attn_fwd_prefill_varlen
+    fn(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, causal, scale)
     return o, lse
 
 
@@ -410,17 +428,13 @@ def attn_bwd_workspace_bytes(B, Hq, Nq) -> int:
     return int(load_library().attn_bwd_workspace_bytes(B, Hq, Nq))
 
 
-def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal: bool, scale: float, workspace=None,
-             stream=None) -> None:
-    """Gradients of attn_fwd_prefill.  q, o, dout, dq [B,Hq,Nq,d] bf16; k, v, dk, dv
-    [B,Hkv,Nk,d] bf16; lse [B,Hq,Nq] fp32 (the forward's); workspace of at least
-    attn_bwd_workspace_bytes(B, Hq, Nq) bytes (allocated here when None)."""
+def _bwd_call(fn, dtype, q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream):
     lib = load_library()
-    _check(q, "q", torch.bfloat16, 4)
+    _check(q, "q", dtype, 4)
     dev = q.device
     for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk),
                     ("dv", dv)):
-        _check(t, name, torch.bfloat16, 4, dev)
+        _check(t, name, dtype, 4, dev)
     _check(lse, "lse", torch.float32, 3, dev)
     B, Hq, Nq, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
@@ -435,23 +449,42 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal: bool, scale: float, work
     if workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on q's device")
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
-                      _ptr(dk), _ptr(dv), B, Hq, Hkv, Nq, Nk, d, 1 if causal else 0,
-                      float(scale), _ptr(workspace), ws_bytes, _stream_handle(stream))
+    st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                          _ptr(dk), _ptr(dv), B, Hq, Hkv, Nq, Nk, d, 1 if causal else 0,
+                          float(scale), _ptr(workspace), ws_bytes, _stream_handle(stream))
     if st != ATTN_OK:
-        raise AttnError(st, "attn_bwd")
+        raise AttnError(st, fn)
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal: bool, scale: float, workspace=None,
+             stream=None) -> None:
+    """Gradients of attn_fwd_prefill.  q, o, dout, dq [B,Hq,Nq,d] bf16; k, v, dk, dv
+    [B,Hkv,Nk,d] bf16; lse [B,Hq,Nq] fp32 (the forward's); workspace of at least
+    attn_bwd_workspace_bytes(B, Hq, Nq) bytes (allocated here when None)."""
+    _bwd_call("attn_bwd", torch.bfloat16, q, k, v, o, lse, dout, dq, dk, dv, causal, scale,
+              workspace, stream)
+
+
+def attn_bwd_f16(q, k, v, o, lse, dout, dq, dk, dv, causal: bool, scale: float, workspace=None,
+                 stream=None) -> None:
+    """attn_bwd with fp16 q, k, v, o, dout, dq, dk, dv."""
+    _bwd_call("attn_bwd_f16", torch.float16, q, k, v, o, lse, dout, dq, dk, dv, causal, scale,
+              workspace, stream)
 
 
 def backward(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = None):
-    """Allocate dq, dk, dv and run attn_bwd.  scale None means 1/sqrt(d)."""
+    """Allocate dq, dk, dv and run attn_bwd (attn_bwd_f16 for fp16 tensors).  scale None
+    means 1/sqrt(d)."""
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal, scale)
+    fn = attn_bwd_f16 if q.dtype == torch.float16 else attn_bwd
+    fn(q, k, v, o, lse, dout, dq, dk, dv, causal, scale)
     return dq, dk, dv
 
 
-__all__ = ["attn_bwd", "attn_bwd_workspace_bytes", "backward", "attn_fwd_prefill_varlen",
+__all__ = ["attn_bwd", "attn_bwd_f16", "attn_bwd_workspace_bytes", "backward", "attn_fwd_prefill_varlen",
+           "attn_fwd_prefill_varlen_f16",
            "prefill_varlen",
            "attn_fwd_prefill", "attn_fwd_prefill_f16", "attn_fwd_prefill_paged_f16",
            "attn_fwd_decode", "attn_fwd_decode_f16", "attn_fwd_decode_fp8",

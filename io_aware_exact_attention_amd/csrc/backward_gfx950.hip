@@ -94,33 +94,31 @@ __device__ __forceinline__ u32x4 load_row_chunk(const uint16_t* row, int s, int 
   return *(const u32x4*)(row + 16 * s + 8 * g);
 }
 
-__device__ __forceinline__ float dot_bf16x8(u32x4 x, u32x4 y, float acc) {
+// acc + the dot product of two rows' 8 elements
+template <typename E>
+__device__ __forceinline__ float dot8(u32x4 x, u32x4 y, float acc) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    acc = fmaf(__builtin_bit_cast(float, x[e] << 16), __builtin_bit_cast(float, y[e] << 16), acc);
-    acc = fmaf(__builtin_bit_cast(float, x[e] & 0xffff0000u),
-               __builtin_bit_cast(float, y[e] & 0xffff0000u), acc);
-  }
+  for (int e = 0; e < 4; ++e) acc = E::dot2(x[e], y[e], acc);
   return acc;
 }
 
 // Stores a lane's 32 x D accumulator block (rows on lanes, columns 32*db + 8*(r/4) +
-// 4*g + r%4 in accumulator r of block db), times mul, as bf16 into row `out`.
-template <int D>
+// 4*g + r%4 in accumulator r of block db), times mul, in the element type into row `out`.
+template <int D, typename E>
 __device__ __forceinline__ void store_row(uint16_t* out, const f32x16 (&acc)[D / 32], float mul,
                                           int g) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
-      const u32x2 w = {pack_bf16x2(acc[db][4 * a4 + 0] * mul, acc[db][4 * a4 + 1] * mul),
-                       pack_bf16x2(acc[db][4 * a4 + 2] * mul, acc[db][4 * a4 + 3] * mul)};
+      const u32x2 w = {E::pack2(acc[db][4 * a4 + 0] * mul, acc[db][4 * a4 + 1] * mul),
+                       E::pack2(acc[db][4 * a4 + 2] * mul, acc[db][4 * a4 + 3] * mul)};
       *(u32x2*)(out + 32 * db + 8 * a4 + 4 * g) = w;
     }
 }
 
 // ------------------------------------------------------------------------------ dQ
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, typename E>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdParams a) {
   using S = BwdShape<D>;
@@ -159,7 +157,7 @@ void bwd_dq_kernel(BwdParams a) {
       u32x4 wq = load_row_chunk(qr, s, g), wd = load_row_chunk(dr, s, g);
       const u32x4 wo = load_row_chunk(orw, s, g);
       if (!qvalid) wq = wd = u32x4{0, 0, 0, 0};
-      dpart = dot_bf16x8(wd, wo, dpart);
+      dpart = dot8<E>(wd, wo, dpart);
       qop[s] = __builtin_bit_cast(bf16x8, wq);
       doop[s] = __builtin_bit_cast(bf16x8, wd);
     }
@@ -211,8 +209,8 @@ void bwd_dq_kernel(BwdParams a) {
       for (int t = 0; t < D / 16; ++t) {
         const bf16x8 ka = lds_read_b128(st + to.row[t] + kb * 32 * S::ROWB);
         const bf16x8 va = lds_read_b128(st + S::TILE + to.row[t] + kb * 32 * S::ROWB);
-        s[kb] = ElemBf16::mfma32(ka, qop[t], s[kb]);
-        dp[kb] = ElemBf16::mfma32(va, doop[t], dp[kb]);
+        s[kb] = E::mfma32(ka, qop[t], s[kb]);
+        dp[kb] = E::mfma32(va, doop[t], dp[kb]);
       }
     }
     // dS^T = P^T * (dP^T - D), P^T = exp(S - LSE); accumulator r of half kb is key
@@ -229,7 +227,7 @@ void bwd_dq_kernel(BwdParams a) {
         float p1 = fast_exp2(fmaf(s[kb][r + 1], a.c, -lse2));
         p0 = key <= lim ? p0 : 0.f;
         p1 = key + 1 <= lim ? p1 : 0.f;
-        pk[kb][jj] = pack_bf16x2(p0 * (dp[kb][r] - Dq), p1 * (dp[kb][r + 1] - Dq));
+        pk[kb][jj] = E::pack2(p0 * (dp[kb][r] - Dq), p1 * (dp[kb][r + 1] - Dq));
       }
     // dQ^T += K^T dS^T in 16-key steps
 #pragma unroll
@@ -238,16 +236,16 @@ void bwd_dq_kernel(BwdParams a) {
                         pk[t4 >> 1][4 * (t4 & 1) + 2], pk[t4 >> 1][4 * (t4 & 1) + 3]};
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
-        acc[db] = ElemBf16::mfma32(to.trans(st, db, t4), __builtin_bit_cast(bf16x8, pw), acc[db]);
+        acc[db] = E::mfma32(to.trans(st, db, t4), __builtin_bit_cast(bf16x8, pw), acc[db]);
     }
     __syncthreads();  // every wave is done with this stage before it is refilled
   }
 
-  if (qvalid) store_row<D>(a.dq + ((size_t)bh * a.Nq + qrow) * D, acc, a.scale, g);
+  if (qvalid) store_row<D, E>(a.dq + ((size_t)bh * a.Nq + qrow) * D, acc, a.scale, g);
 }
 
 // ------------------------------------------------------------------------------ dK, dV
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, typename E>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdParams a) {
   using S = BwdShape<D>;
@@ -333,8 +331,8 @@ void bwd_dkdv_kernel(BwdParams a) {
       for (int t = 0; t < D / 16; ++t) {
         const bf16x8 qa = lds_read_b128(st + to.row[t] + qh * 32 * S::ROWB);
         const bf16x8 da = lds_read_b128(st + S::TILE + to.row[t] + qh * 32 * S::ROWB);
-        s = ElemBf16::mfma32(qa, kop[t], s);
-        dp = ElemBf16::mfma32(da, vop[t], dp);
+        s = E::mfma32(qa, kop[t], s);
+        dp = E::mfma32(da, vop[t], dp);
       }
       const int qb = 32 * qh + 8 * g;
       const f32x4 L[4] = {*(const f32x4*)(lse_t + qb), *(const f32x4*)(lse_t + qb + 4),
@@ -354,8 +352,8 @@ void bwd_dkdv_kernel(BwdParams a) {
           pv[e] = vis ? p : 0.f;
           dsv[e] = pv[e] * (dp[r] - Dv[r >> 2][r & 3]);
         }
-        ppk[jj] = pack_bf16x2(pv[0], pv[1]);
-        dpk[jj] = pack_bf16x2(dsv[0], dsv[1]);
+        ppk[jj] = E::pack2(pv[0], pv[1]);
+        dpk[jj] = E::pack2(dsv[0], dsv[1]);
       }
       // dV^T += dO^T P and dK^T += Q^T dS in 16-query steps
 #pragma unroll
@@ -364,10 +362,10 @@ void bwd_dkdv_kernel(BwdParams a) {
         const u32x4 dw = {dpk[4 * t], dpk[4 * t + 1], dpk[4 * t + 2], dpk[4 * t + 3]};
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          dv[db] = ElemBf16::mfma32(to.trans(st + S::TILE, db, 2 * qh + t),
-                                    __builtin_bit_cast(bf16x8, pw), dv[db]);
-          dk[db] = ElemBf16::mfma32(to.trans(st, db, 2 * qh + t),
-                                    __builtin_bit_cast(bf16x8, dw), dk[db]);
+          dv[db] = E::mfma32(to.trans(st + S::TILE, db, 2 * qh + t),
+                             __builtin_bit_cast(bf16x8, pw), dv[db]);
+          dk[db] = E::mfma32(to.trans(st, db, 2 * qh + t), __builtin_bit_cast(bf16x8, dw),
+                             dk[db]);
         }
       }
     }
@@ -376,27 +374,35 @@ void bwd_dkdv_kernel(BwdParams a) {
 
   if (kvalid) {
     const size_t out = ((size_t)bh * a.Nk + key) * D;
-    store_row<D>(a.dk + out, dk, a.scale, g);
-    store_row<D>(a.dv + out, dv, 1.f, g);
+    store_row<D, E>(a.dk + out, dk, a.scale, g);
+    store_row<D, E>(a.dv + out, dv, 1.f, g);
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, typename E>
 static hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
   using S = BwdShape<D>;
   const int nqt = (p.Nq + S::ROWS_WG - 1) / S::ROWS_WG;
   const int nkt = (p.Nk + S::ROWS_WG - 1) / S::ROWS_WG;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(nqt * p.B * p.Hq), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, E>), dim3(nqt * p.B * p.Hq), dim3(256), 0, stream,
+                     p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(nkt * p.B * p.Hkv), dim3(256), 0, stream,
-                     p);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, E>), dim3(nkt * p.B * p.Hkv), dim3(256), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
+template <typename E>
+static hipError_t launch_bwd_e(const BwdParams& p, int d, int causal, hipStream_t stream) {
+  if (d == 64)
+    return causal ? launch_bwd_d<64, true, E>(p, stream) : launch_bwd_d<64, false, E>(p, stream);
+  return causal ? launch_bwd_d<128, true, E>(p, stream) : launch_bwd_d<128, false, E>(p, stream);
+}
+
 hipError_t launch_backward(const BwdParams& p, int d, int causal, hipStream_t stream) {
-  if (d == 64) return causal ? launch_bwd_d<64, true>(p, stream) : launch_bwd_d<64, false>(p, stream);
-  return causal ? launch_bwd_d<128, true>(p, stream) : launch_bwd_d<128, false>(p, stream);
+  return p.f16 ? launch_bwd_e<ElemF16>(p, d, causal, stream)
+               : launch_bwd_e<ElemBf16>(p, d, causal, stream);
 }
 
 }  // namespace miattn

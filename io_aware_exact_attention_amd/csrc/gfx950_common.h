@@ -123,6 +123,12 @@ struct ElemBf16 {
   static __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
   // acc + both halves of a packed pair
   static __device__ __forceinline__ float add2(uint32_t x, float acc) { return add_bf16x2(x, acc); }
+  // acc + x.lo*y.lo + x.hi*y.hi, both elements widened exactly to fp32
+  static __device__ __forceinline__ float dot2(uint32_t x, uint32_t y, float acc) {
+    acc = fmaf(__builtin_bit_cast(float, x << 16), __builtin_bit_cast(float, y << 16), acc);
+    return fmaf(__builtin_bit_cast(float, x & 0xffff0000u),
+                __builtin_bit_cast(float, y & 0xffff0000u), acc);
+  }
   static __device__ __forceinline__ uint16_t bits(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
   }
@@ -150,6 +156,11 @@ struct ElemF16 {
   static __device__ __forceinline__ float add2(uint32_t x, float acc) {
     const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), ones, acc, false);
+  }
+  // acc + x.lo*y.lo + x.hi*y.hi (v_dot2_f32_f16: the fp16 products are exact in fp32)
+  static __device__ __forceinline__ float dot2(uint32_t x, uint32_t y, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), __builtin_bit_cast(f16x2, y), acc,
+                                  false);
   }
   static __device__ __forceinline__ uint16_t bits(float x) {
     return __builtin_bit_cast(uint16_t, (_Float16)x);

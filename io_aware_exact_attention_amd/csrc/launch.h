@@ -63,7 +63,7 @@ constexpr int kDecodeBlock = 32;
 constexpr int kDecodeWaves = 4;
 constexpr int kDecodeMaxSplits = 1024;  // chunks per sequence, at most
 
-// Backward (bf16): gradients of the prefill attention.  Layouts as for prefill; dvec is
+// Backward (bf16 or fp16): gradients of the prefill attention.  Layouts as for prefill; dvec is
 // the [B, Hq, Nq] fp32 workspace for D = rowsum(dO * O), written by the first kernel and
 // read by the second.
 struct BwdParams {
@@ -80,6 +80,7 @@ struct BwdParams {
   int B, Hq, Hkv, Nq, Nk;
   float scale;  // signed softmax scale
   float c;      // scale * log2(e), signed
+  int f16;      // fp16 tensors (else bf16)
 };
 
 hipError_t launch_prefill(PrefillParams p, int d, int causal, hipStream_t stream);

@@ -197,6 +197,87 @@ int prefill_paged_impl(const void* q, const void* kcache, const void* vcache,
                                                                              : ATTN_ERR_HIP;
 }
 
+// The varlen entry points (bf16 or fp16 elements).
+int prefill_varlen_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int Hq,
+                        int Hkv, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                        int d, int causal, float scale, bool f16, hipStream_t stream) {
+  if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (lse && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (B < 1 || Hq < 1 || Hkv < 1 || total_q < 1 || total_k < 1 || max_seqlen_q < 1 ||
+      max_seqlen_k < 1 || d < 1)
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (Hq % Hkv || max_seqlen_q > total_q || max_seqlen_k > total_k || !std::isfinite(scale))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  const long qtiles = (max_seqlen_q + 255) / 256;
+  if (qtiles * (long)Hq * B > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
+  // 64 key rows of the packed K (row stride Hkv*d*2 bytes) must fit a buffer descriptor
+  if (64L * Hkv * d * 2 > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
+
+  miattn::PrefillParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = max_seqlen_q; p.Nk = max_seqlen_k;
+  p.c = std::fabs(scale) * 1.4426950408889634f;
+  p.negate_q = scale < 0.f;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.total_q = total_q;
+  p.total_k = total_k;
+  p.f16 = f16;
+  (void)hipGetLastError();
+  return miattn::launch_prefill(p, d, causal ? 1 : 0, stream) == hipSuccess ? ATTN_OK
+                                                                             : ATTN_ERR_HIP;
+}
+
+// The backward entry points (bf16 or fp16 tensors).
+int bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
+             int Nk, int d, int causal, float scale, void* workspace, size_t workspace_bytes,
+             bool f16, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return ATTN_ERR_INVALID_ARGUMENT;
+  if (Hq % Hkv || (causal && Nq > Nk) || !std::isfinite(scale)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  const long qtiles = (Nq + 127) / 128, ktiles = (Nk + 127) / 128;
+  if (qtiles * (long)Hq * B > 0x7fffffffL || ktiles * (long)Hkv * B > 0x7fffffffL)
+    return ATTN_ERR_UNSUPPORTED;
+  // one head's K (or Q) rows must fit a buffer descriptor's 32-bit byte range
+  if ((long)Nk * d * 2 > 0x7fffffffL || (long)Nq * d * 2 > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
+  const size_t need = attn_bwd_workspace_bytes(B, Hq, Nq);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return ATTN_ERR_WORKSPACE;
+
+  miattn::BwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<const uint16_t*>(o);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.dvec = static_cast<float*>(workspace);
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk;
+  p.scale = scale;
+  p.c = scale * 1.4426950408889634f;
+  p.f16 = f16;
+  (void)hipGetLastError();
+  return miattn::launch_backward(p, d, causal ? 1 : 0, stream) == hipSuccess ? ATTN_OK
+                                                                               : ATTN_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -249,38 +330,17 @@ int attn_fwd_prefill_varlen(const void* q, const void* k, const void* v, void* o
                             int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
                             int max_seqlen_k, int d, int causal, float scale,
                             hipStream_t stream) {
-  if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_INVALID_ARGUMENT;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-      !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
-    return ATTN_ERR_INVALID_ARGUMENT;
-  if (lse && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARGUMENT;
-  if (B < 1 || Hq < 1 || Hkv < 1 || total_q < 1 || total_k < 1 || max_seqlen_q < 1 ||
-      max_seqlen_k < 1 || d < 1)
-    return ATTN_ERR_INVALID_ARGUMENT;
-  if (Hq % Hkv || max_seqlen_q > total_q || max_seqlen_k > total_k || !std::isfinite(scale))
-    return ATTN_ERR_INVALID_ARGUMENT;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  const long qtiles = (max_seqlen_q + 255) / 256;
-  if (qtiles * (long)Hq * B > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
-  // 64 key rows of the packed K (row stride Hkv*d*2 bytes) must fit a buffer descriptor
-  if (64L * Hkv * d * 2 > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
+  return prefill_varlen_impl(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q,
+                             total_k, max_seqlen_q, max_seqlen_k, d, causal, scale, false, stream);
+}
 
-  miattn::PrefillParams p{};
-  p.q = static_cast<const uint16_t*>(q);
-  p.k = static_cast<const uint16_t*>(k);
-  p.v = static_cast<const uint16_t*>(v);
-  p.o = static_cast<uint16_t*>(o);
-  p.lse = lse;
-  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = max_seqlen_q; p.Nk = max_seqlen_k;
-  p.c = std::fabs(scale) * 1.4426950408889634f;
-  p.negate_q = scale < 0.f;
-  p.cu_q = cu_seqlens_q;
-  p.cu_k = cu_seqlens_k;
-  p.total_q = total_q;
-  p.total_k = total_k;
-  (void)hipGetLastError();
-  return miattn::launch_prefill(p, d, causal ? 1 : 0, stream) == hipSuccess ? ATTN_OK
-                                                                             : ATTN_ERR_HIP;
+int attn_fwd_prefill_varlen_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
+                                int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                                int max_seqlen_k, int d, int causal, float scale,
+                                hipStream_t stream) {
+  return prefill_varlen_impl(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q,
+                             total_k, max_seqlen_q, max_seqlen_k, d, causal, scale, true, stream);
 }
 
 int attn_decode_num_splits(int B, int Hq, int Hkv, int d, int max_seqlen, int num_splits) {
@@ -338,39 +398,16 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
              int Nk, int d, int causal, float scale, void* workspace, size_t workspace_bytes,
              hipStream_t stream) {
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_INVALID_ARGUMENT;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
-      !aligned(lse, 4))
-    return ATTN_ERR_INVALID_ARGUMENT;
-  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return ATTN_ERR_INVALID_ARGUMENT;
-  if (Hq % Hkv || (causal && Nq > Nk) || !std::isfinite(scale)) return ATTN_ERR_INVALID_ARGUMENT;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  const long qtiles = (Nq + 127) / 128, ktiles = (Nk + 127) / 128;
-  if (qtiles * (long)Hq * B > 0x7fffffffL || ktiles * (long)Hkv * B > 0x7fffffffL)
-    return ATTN_ERR_UNSUPPORTED;
-  // one head's K (or Q) rows must fit a buffer descriptor's 32-bit byte range
-  if ((long)Nk * d * 2 > 0x7fffffffL || (long)Nq * d * 2 > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
-  const size_t need = attn_bwd_workspace_bytes(B, Hq, Nq);
-  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return ATTN_ERR_WORKSPACE;
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, causal, scale,
+                  workspace, workspace_bytes, false, stream);
+}
 
-  miattn::BwdParams p{};
-  p.q = static_cast<const uint16_t*>(q);
-  p.k = static_cast<const uint16_t*>(k);
-  p.v = static_cast<const uint16_t*>(v);
-  p.o = static_cast<const uint16_t*>(o);
-  p.dout = static_cast<const uint16_t*>(dout);
-  p.lse = lse;
-  p.dq = static_cast<uint16_t*>(dq);
-  p.dk = static_cast<uint16_t*>(dk);
-  p.dv = static_cast<uint16_t*>(dv);
-  p.dvec = static_cast<float*>(workspace);
-  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk;
-  p.scale = scale;
-  p.c = scale * 1.4426950408889634f;
-  (void)hipGetLastError();
-  return miattn::launch_backward(p, d, causal ? 1 : 0, stream) == hipSuccess ? ATTN_OK
-                                                                               : ATTN_ERR_HIP;
+int attn_bwd_f16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
+                 int Nk, int d, int causal, float scale, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, causal, scale,
+                  workspace, workspace_bytes, true, stream);
 }
 
 }  // extern "C"

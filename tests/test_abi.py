@@ -32,8 +32,9 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["attn_fwd_prefill", "attn_fwd_prefill_paged",
                                            "attn_fwd_prefill_f16", "attn_fwd_prefill_paged_f16",
                                            "attn_fwd_decode", "attn_fwd_decode_f16",
-                                           "attn_fwd_decode_fp8", "attn_bwd",
+                                           "attn_fwd_decode_fp8", "attn_bwd", "attn_bwd_f16",
                                            "attn_fwd_prefill_varlen",
+                                           "attn_fwd_prefill_varlen_f16",
                                            "attn_bwd_workspace_bytes",
                                            "attn_decode_workspace_bytes",
                                            "attn_decode_num_splits", "attn_status_string"])
@@ -188,9 +189,12 @@ def bwd(lib, ws_bytes=1 << 20, **kw):
     a = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, B=1, Hq=2, Hkv=1, Nq=4, Nk=4,
              d=64, causal=1, scale=0.125, ws=P)
     a.update(kw)
-    return lib.attn_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"], a["dk"],
-                        a["dv"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["causal"],
-                        ctypes.c_float(a["scale"]), a["ws"], ws_bytes, None)
+    args = [a[n] for n in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "B", "Hq", "Hkv",
+                           "Nq", "Nk", "d", "causal")]
+    args += [ctypes.c_float(a["scale"]), a["ws"], ws_bytes, None]
+    st = lib.attn_bwd(*args)
+    assert lib.attn_bwd_f16(*args) == st
+    return st
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -180,6 +180,9 @@ def test_varlen_inputs_pack_the_dense_streams():
     assert cu_q.tolist() == [0, 3, 3, 8] and cu_k.tolist() == [0, 4, 6, 12]
     np.testing.assert_array_equal(q[3:8, 1], ai.normal_bf16(9, ai.T_Q, 2, 1, (5, 8)))
     np.testing.assert_array_equal(v[4:6, 0], ai.normal_bf16(9, ai.T_V, 1, 0, (2, 8)))
+    q16, k16, _, _, _ = ai.varlen_inputs(9, [3, 0, 5], [4, 2, 6], 4, 2, 8, f16=True)
+    np.testing.assert_array_equal(k16[6:12, 1], ai.normal_bf16(9, ai.T_K, 2, 1, (6, 8), f16=True))
+    assert not np.array_equal(q16, q)
     lens = ai.varlen_lengths(8, 16, 256, 4096)
     assert lens.shape == (16,) and lens.min() >= 256 and lens.max() <= 4096
     assert ai.varlen_flops([2, 3], [2, 5], 1, 1, True) == 4 * (3 + 3 + 4 + 5)

@@ -658,18 +658,20 @@ def check_grads(label, got, ref):
         assert err.mean() <= BWD_REL_MEAN * scale_mean, f"{label} {name}: mean {err.mean():.3e}"
 
 
-def run_bwd(q, k, v, do, causal, scale):
-    dq_, dk_, dv_ = (dev(x).reshape(x.shape) for x in (q, k, v))
+def run_bwd(q, k, v, do, causal, scale, f16=False):
+    to = dev16 if f16 else dev
+    dq_, dk_, dv_ = (to(x).reshape(x.shape) for x in (q, k, v))
     o, lse = mi.prefill(dq_, dk_, dv_, causal, scale)
-    gdo = dev(do).reshape(do.shape)
+    gdo = to(do).reshape(do.shape)
     grads = mi.backward(dq_, dk_, dv_, o, lse, gdo, causal, scale)
     torch.cuda.synchronize()
+    assert all(g.dtype == dq_.dtype for g in grads)
     return grads
 
 
-def bwd_inputs(seed, B, Hq, Hkv, Nq, Nk, d):
-    q, k, v = ai.custom_prefill(seed=seed, B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nk=Nk, d=d)
-    do = ai.prefill_dout(ai.PrefillCfg("bwd", B, Hq, Hkv, Nq, Nk, d, True, seed))
+def bwd_inputs(seed, B, Hq, Hkv, Nq, Nk, d, f16=False):
+    q, k, v = ai.custom_prefill(seed=seed, B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nk=Nk, d=d, f16=f16)
+    do = ai.prefill_dout(ai.PrefillCfg("bwd", B, Hq, Hkv, Nq, Nk, d, True, seed, 1.0, f16))
     return q, k, v, do
 
 
@@ -698,6 +700,24 @@ def test_backward_gqa_and_scale(scale):
     check_grads(f"bwd GQA scale={scale}", got, ref)
 
 
+@pytest.mark.parametrize("Nq,Nk,causal,d", [(1, 1, True, 64), (130, 130, True, 128),
+                                            (300, 300, False, 64), (100, 333, True, 128),
+                                            (65, 200, False, 128)])
+def test_backward_f16_shapes(Nq, Nk, causal, d):
+    q, k, v, do = bwd_inputs(7300 + Nq + Nk + d, 1, 2, 2, Nq, Nk, d, f16=True)
+    scale = 1 / math.sqrt(d)
+    got = run_bwd(q, k, v, do, causal, scale, f16=True)
+    ref = attention_backward(h64(q), h64(k), h64(v), h64(do), scale, causal)
+    check_grads(f"bwd f16 Nq={Nq} Nk={Nk} causal={causal} d={d}", got, ref)
+
+
+def test_backward_f16_gqa():
+    q, k, v, do = bwd_inputs(7400, 2, 8, 2, 150, 150, 64, f16=True)
+    got = run_bwd(q, k, v, do, True, -0.2, f16=True)
+    ref = attention_backward(h64(q), h64(k), h64(v), h64(do), float(np.float32(-0.2)), True)
+    check_grads("bwd f16 GQA scale=-0.2", got, ref)
+
+
 def test_backward_is_deterministic():
     q, k, v, do = bwd_inputs(7200, 1, 4, 2, 700, 700, 128)
     g1 = run_bwd(q, k, v, do, True, 0.09)
@@ -721,11 +741,12 @@ def test_backward_llama2_shape():
 
 
 # ------------------------------------------------------------------ varlen (ragged) prefill
-def run_varlen(q, k, v, cu_q, cu_k, causal, scale):
+def run_varlen(q, k, v, cu_q, cu_k, causal, scale, f16=False):
     mq = int(np.diff(cu_q).max())
     mk = int(np.diff(cu_k).max())
-    o, lse = mi.prefill_varlen(dev(q).reshape(q.shape), dev(k).reshape(k.shape),
-                               dev(v).reshape(v.shape), torch.from_numpy(cu_q).cuda(),
+    to = dev16 if f16 else dev
+    o, lse = mi.prefill_varlen(to(q).reshape(q.shape), to(k).reshape(k.shape),
+                               to(v).reshape(v.shape), torch.from_numpy(cu_q).cuda(),
                                torch.from_numpy(cu_k).cuda(), max(mq, 1), max(mk, 1), causal,
                                scale)
     torch.cuda.synchronize()
@@ -745,6 +766,18 @@ def test_prefill_varlen(d, causal, lens_q, lens_k):
     o, lse = run_varlen(q, k, v, cu_q, cu_k, causal, scale)
     ro, rl = attention_prefill_varlen(f64(q), f64(k), f64(v), cu_q, cu_k, scale, causal)
     check(f"varlen d={d} causal={causal} lens_q={lens_q} lens_k={lens_k}", o, lse, ro, rl)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_varlen_f16(causal, d):
+    lens_q, lens_k = [3, 0, 300, 129], [40, 17, 300, 600]
+    q, k, v, cu_q, cu_k = ai.varlen_inputs(7550 + d, lens_q, lens_k, 4, 2, d, f16=True)
+    scale = 1 / math.sqrt(d)
+    o, lse = run_varlen(q, k, v, cu_q, cu_k, causal, scale, f16=True)
+    assert o.dtype == torch.float16
+    ro, rl = attention_prefill_varlen(h64(q), h64(k), h64(v), cu_q, cu_k, scale, causal)
+    check(f"varlen f16 d={d} causal={causal}", o, lse, ro, rl)
 
 
 def test_prefill_varlen_sequence_without_keys():
