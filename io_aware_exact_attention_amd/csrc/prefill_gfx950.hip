@@ -444,12 +444,14 @@ void prefill_kernel(PrefillParams a) {
   auto softmax = [&](int j, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     if (MASK) {
-      const int kbase = j * S::BN + 8 * g;
+      // key kbase + o is visible when o <= lim - kbase; o is a small constant per register,
+      // so each score costs one compare with an inline constant and one select
+      const int vis = lim - (j * S::BN + 8 * g);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          sacc[kb][r] = (kbase + kb * 32 + 16 * (r >> 3) + (r & 7) > lim) ? -INFINITY : sacc[kb][r];
+          sacc[kb][r] = (kb * 32 + 16 * (r >> 3) + (r & 7) > vis) ? -INFINITY : sacc[kb][r];
     }
     // P = exp2(S*c - m*c) -> bf16 pairs, and the tile's sum of the unrounded weights
     auto weights = [&]() {
