@@ -275,8 +275,9 @@ int attn_bwd_f16(const void* q, const void* k, const void* v, const void* o, con
                  int Nk, int d, int causal, float scale, void* workspace, size_t workspace_bytes,
                  hipStream_t stream);
 
-/* Workspace bytes attn_bwd (and attn_bwd_f16) needs: B*Hq*Nq*4 (the fp32 row terms rowsum(dO * O)) rounded
- * up to 256.  Returns 0 for invalid arguments.  Pure host arithmetic; no HIP call. */
+/* Workspace bytes attn_bwd (and attn_bwd_f16) needs: B*Hq*Nq*8 (two fp32 row terms per
+ * query, rowsum(dO * O) and -LSE*log2(e)) rounded up to 256.  Returns 0 for invalid
+ * arguments.  Pure host arithmetic; no HIP call. */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq);
 
 /* Static, human-readable text for a status code (never NULL). */

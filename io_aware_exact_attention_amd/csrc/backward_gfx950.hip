@@ -29,6 +29,8 @@
 // the gradients are those of the definition on the page "FlashAttention 완전 정리"
 // (cell-devlog), section "Attention이 뭔가".
 
+#include <type_traits>
+
 #include "gfx950_common.h"
 #include "launch.h"
 
@@ -163,7 +165,10 @@ void bwd_dq_kernel(BwdParams a) {
     }
   }
   const float Dq = dpart + wave_xor(dpart, 32);
-  if (g == 0 && qvalid) a.dvec[rowi] = Dq;
+  if (g == 0 && qvalid) {
+    a.dvec[rowi] = Dq;
+    a.nlse[rowi] = -a.lse[rowi] * kLog2e;  // the exponent offset the dK/dV pass adds
+  }
   const float lse2 = qvalid ? a.lse[rowi] * kLog2e : INFINITY;
 
   const int kend = CAUSAL ? min(a.Nk, min(m0 + S::ROWS_WG, a.Nq) + off) : a.Nk;
@@ -299,10 +304,10 @@ void bwd_dkdv_kernel(BwdParams a) {
       lds_dma16(a.q + r0 * D, nbytes, to.dma[i], (lds_void*)(st + blk * 1024));
       lds_dma16(a.dout + r0 * D, nbytes, to.dma[i], (lds_void*)(st + S::TILE + blk * 1024));
     }
-    // LSE and D of the tile's 64 rows: one 4-byte-per-lane DMA each (rows past Nq read as
-    // zeros)
+    // -LSE*log2(e) and D of the tile's 64 rows: one 4-byte-per-lane DMA each (rows past Nq
+    // read as zeros)
     const int fbytes = __builtin_amdgcn_readfirstlane((a.Nq - q0) * 4);
-    if (wave == 0) lds_dma4(a.lse + r0, fbytes, lane * 4, (lds_void*)(st + 2 * S::TILE));
+    if (wave == 0) lds_dma4(a.nlse + r0, fbytes, lane * 4, (lds_void*)(st + 2 * S::TILE));
     if (wave == 1) lds_dma4(a.dvec + r0, fbytes, lane * 4, (lds_void*)(st + 2 * S::TILE + 256));
   };
 
@@ -320,7 +325,7 @@ void bwd_dkdv_kernel(BwdParams a) {
     }
     __syncthreads();
     const char* st = smem + (it & 1) * STAGE;
-    const float* lse_t = (const float*)(st + 2 * S::TILE);
+    const float* nl_t = (const float*)(st + 2 * S::TILE);
     const float* d_t = (const float*)(st + 2 * S::TILE + 256);
     const int q0 = (qt0 + it % per_head) * S::TROWS;
 #pragma unroll
@@ -335,26 +340,44 @@ void bwd_dkdv_kernel(BwdParams a) {
         dp = E::mfma32(da, vop[t], dp);
       }
       const int qb = 32 * qh + 8 * g;
-      const f32x4 L[4] = {*(const f32x4*)(lse_t + qb), *(const f32x4*)(lse_t + qb + 4),
-                          *(const f32x4*)(lse_t + qb + 16), *(const f32x4*)(lse_t + qb + 20)};
+      const f32x4 NL[4] = {*(const f32x4*)(nl_t + qb), *(const f32x4*)(nl_t + qb + 4),
+                           *(const f32x4*)(nl_t + qb + 16), *(const f32x4*)(nl_t + qb + 20)};
       const f32x4 Dv[4] = {*(const f32x4*)(d_t + qb), *(const f32x4*)(d_t + qb + 4),
                            *(const f32x4*)(d_t + qb + 16), *(const f32x4*)(d_t + qb + 20)};
       uint32_t ppk[8], dpk[8];
+      // P = exp2(S*c - LSE*log2(e)) and dS = P * (dP - D); MASK zeroes the pairs that are
+      // outside the causal triangle or past Nq, Nk
+      auto weights = [&](auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        float pv[2], dsv[2];
+        for (int jj = 0; jj < 8; ++jj) {
+          float pv[2], dsv[2];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int r = 2 * jj + e;
-          const int qi = q0 + qb + 16 * (r >> 3) + (r & 7);
-          const bool vis = kvalid && qi < a.Nq && (!CAUSAL || key <= qi + off);
-          const float p = fast_exp2(fmaf(s[r], a.c, -L[r >> 2][r & 3] * kLog2e));
-          pv[e] = vis ? p : 0.f;
-          dsv[e] = pv[e] * (dp[r] - Dv[r >> 2][r & 3]);
+          for (int e = 0; e < 2; ++e) {
+            const int r = 2 * jj + e;
+            const float p = fast_exp2(fmaf(s[r], a.c, NL[r >> 2][r & 3]));
+            if (MASK) {
+              const int qi = q0 + qb + 16 * (r >> 3) + (r & 7);
+              const bool vis = kvalid && qi < a.Nq && (!CAUSAL || key <= qi + off);
+              pv[e] = vis ? p : 0.f;
+            } else {
+              pv[e] = p;
+            }
+            dsv[e] = pv[e] * (dp[r] - Dv[r >> 2][r & 3]);
+          }
+          ppk[jj] = E::pack2(pv[0], pv[1]);
+          dpk[jj] = E::pack2(dsv[0], dsv[1]);
         }
-        ppk[jj] = E::pack2(pv[0], pv[1]);
-        dpk[jj] = E::pack2(dsv[0], dsv[1]);
-      }
+      };
+      // every pair of this wave's 32 keys and the half's 32 queries is visible when the
+      // half's rows are all below Nq, the wave's keys all below Nk and, under causal
+      // masking, the half's first query sees the wave's last key (wave-uniform)
+      const int kmax = k0 + 32 * wave + 31;
+      const int qfirst = q0 + 32 * qh;
+      const bool all_visible =
+          qfirst + 31 < a.Nq && kmax < a.Nk && (!CAUSAL || kmax <= qfirst + off);
+      if (all_visible) weights(std::integral_constant<bool, false>{});
+      else weights(std::integral_constant<bool, true>{});
       // dV^T += dO^T P and dK^T += Q^T dS in 16-query steps
 #pragma unroll
       for (int t = 0; t < 2; ++t) {

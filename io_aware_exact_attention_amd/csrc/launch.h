@@ -63,9 +63,9 @@ constexpr int kDecodeBlock = 32;
 constexpr int kDecodeWaves = 4;
 constexpr int kDecodeMaxSplits = 1024;  // chunks per sequence, at most
 
-// Backward (bf16 or fp16): gradients of the prefill attention.  Layouts as for prefill; dvec is
-// the [B, Hq, Nq] fp32 workspace for D = rowsum(dO * O), written by the first kernel and
-// read by the second.
+// Backward (bf16 or fp16): gradients of the prefill attention.  Layouts as for prefill; dvec and
+// nlse are [B, Hq, Nq] fp32 workspace arrays for D = rowsum(dO * O) and -LSE * log2(e),
+// written by the first kernel and read by the second.
 struct BwdParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -77,6 +77,7 @@ struct BwdParams {
   uint16_t* dk;
   uint16_t* dv;
   float* dvec;
+  float* nlse;
   int B, Hq, Hkv, Nq, Nk;
   float scale;  // signed softmax scale
   float c;      // scale * log2(e), signed

@@ -269,6 +269,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dv);
   p.dvec = static_cast<float*>(workspace);
+  p.nlse = p.dvec + (size_t)B * Hq * Nq;
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk;
   p.scale = scale;
   p.c = scale * 1.4426950408889634f;
@@ -390,7 +391,7 @@ int attn_fwd_decode_fp8(const void* q, const void* kcache, const void* vcache,
 
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq) {
   if (B < 1 || Hq < 1 || Nq < 1) return 0;
-  const size_t bytes = (size_t)B * Hq * Nq * 4;
+  const size_t bytes = (size_t)B * Hq * Nq * 8;
   return (bytes + 255) / 256 * 256;
 }
 

@@ -210,7 +210,7 @@ def test_backward_validation(lib, kw, status):
 
 
 def test_backward_workspace_arithmetic(lib):
-    assert mi.attn_bwd_workspace_bytes(2, 8, 100) == (2 * 8 * 100 * 4 + 255) // 256 * 256
+    assert mi.attn_bwd_workspace_bytes(2, 8, 100) == (2 * 8 * 100 * 8 + 255) // 256 * 256
     assert mi.attn_bwd_workspace_bytes(0, 8, 100) == 0
 
 
