@@ -137,10 +137,12 @@ int attn_fwd_prefill_paged_f16(const void* q, const void* kcache, const void* vc
  *   lse    [Hq, total_q] fp32 (written) or NULL
  *   cu_seqlens_q, cu_seqlens_k  [B + 1] int32, DEVICE memory (not read on the host):
  *          cu[0] = 0, non-decreasing, cu[B] = total.  Sequence lengths must not exceed
- *          max_seqlen_q / max_seqlen_k.  A sequence with queries needs at least one key
- *          (and, when causal, at least as many keys as queries); one with no queries is
- *          skipped.  Values are clamped to [0, total] on the device, so no value reads
- *          outside the tensors; a sequence with no keys gets o = 0 and lse = -inf.
+ *          max_seqlen_q / max_seqlen_k (the grid covers max_seqlen_q queries per
+ *          sequence: rows past it are not written).  A sequence with queries needs at
+ *          least one key (and, when causal, at least as many keys as queries: a causal
+ *          row that sees no key gets undefined values); one with no queries is skipped.
+ *          Values are clamped to [0, total] on the device, so no value reads outside the
+ *          tensors; a sequence with no keys gets o = 0 and lse = -inf.
  *
  * Errors: INVALID_ARGUMENT for a null required pointer, misalignment, any size < 1,
  * Hq % Hkv != 0, a max length above its total, a non-finite scale; UNSUPPORTED for d not
