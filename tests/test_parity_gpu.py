@@ -718,6 +718,15 @@ def test_backward_f16_gqa():
     check_grads("bwd f16 GQA scale=-0.2", got, ref)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_odd_group_size(causal):
+    """Three query heads per KV head: dK and dV sum over the group."""
+    q, k, v, do = bwd_inputs(7450, 2, 6, 2, 200, 233 if not causal else 200, 128)
+    got = run_bwd(q, k, v, do, causal, 0.07)
+    ref = attention_backward(f64(q), f64(k), f64(v), f64(do), float(np.float32(0.07)), causal)
+    check_grads(f"bwd Hq=6 Hkv=2 causal={causal}", got, ref)
+
+
 def test_backward_is_deterministic():
     q, k, v, do = bwd_inputs(7200, 1, 4, 2, 700, 700, 128)
     g1 = run_bwd(q, k, v, do, True, 0.09)
@@ -778,6 +787,15 @@ def test_prefill_varlen_f16(causal, d):
     assert o.dtype == torch.float16
     ro, rl = attention_prefill_varlen(h64(q), h64(k), h64(v), cu_q, cu_k, scale, causal)
     check(f"varlen f16 d={d} causal={causal}", o, lse, ro, rl)
+
+
+def test_prefill_varlen_odd_group_size():
+    lens_q, lens_k = [70, 300, 1], [70, 450, 20]
+    q, k, v, cu_q, cu_k = ai.varlen_inputs(7580, lens_q, lens_k, 6, 2, 128)
+    o, lse = run_varlen(q, k, v, cu_q, cu_k, True, 0.1)
+    ro, rl = attention_prefill_varlen(f64(q), f64(k), f64(v), cu_q, cu_k, float(np.float32(0.1)),
+                                      True)
+    check("varlen Hq=6 Hkv=2", o, lse, ro, rl)
 
 
 def test_prefill_varlen_sequence_without_keys():
