@@ -884,3 +884,68 @@ def test_out_of_range_page_ids_are_clamped_into_the_pool():
     cl = run_chunk(cq, ckc, cvc, lens, ccl, True, 0.09)
     assert torch.equal(bd[0], cl[0]) and torch.equal(bd[1], cl[1])
     assert torch.equal(ok[0][1], bd[0][1]) and torch.equal(ok[1][1], bd[1][1])
+
+
+# ------------------------------------------------------------------ seeded random shapes
+# Shapes drawn from fixed seeds (so every run tests the same cases): batch, heads, group
+# size, lengths, head dimension, masking and scale all vary together, at sizes the oracle
+# finishes in well under a second each.
+def _random_shape(seed):
+    rng = np.random.default_rng(seed)
+    G = int(rng.choice([1, 2, 3, 4, 8]))
+    Hkv = int(rng.integers(1, 4))
+    d = int(rng.choice([64, 128]))
+    causal = bool(rng.integers(0, 2))
+    Nk = int(rng.integers(1, 700))
+    Nq = int(rng.integers(1, Nk + 1)) if causal else int(rng.integers(1, 700))
+    scale = float(np.float32(rng.choice([1 / math.sqrt(d), 0.3, -0.15])))
+    return dict(B=int(rng.integers(1, 4)), Hq=G * Hkv, Hkv=Hkv, Nq=Nq, Nk=Nk, d=d,
+                causal=causal, scale=scale)
+
+
+@pytest.mark.parametrize("seed", list(range(9100, 9116)))
+def test_prefill_random_shapes(seed):
+    s = _random_shape(seed)
+    q, k, v = ai.custom_prefill(seed=seed, B=s["B"], Hq=s["Hq"], Hkv=s["Hkv"], Nq=s["Nq"],
+                                Nk=s["Nk"], d=s["d"])
+    o, lse = run_prefill(q, k, v, s["causal"], s["scale"])
+    ro, rl = attention_prefill(f64(q), f64(k), f64(v), s["scale"], s["causal"])
+    check(f"prefill random seed={seed} {s}", o, lse, ro, rl)
+
+
+@pytest.mark.parametrize("seed", list(range(9200, 9212)))
+def test_decode_random_shapes(seed):
+    rng = np.random.default_rng(seed)
+    G = int(rng.choice([1, 2, 4, 5, 8, 16, 24]))
+    Hkv = int(rng.integers(1, 4))
+    d = int(rng.choice([64, 128]))
+    B = int(rng.integers(1, 7))
+    lens = rng.integers(0, 3000, size=B)
+    paged = bool(rng.integers(0, 2))
+    splits = int(rng.choice([0, 1, 2, 7]))
+    cfg, q, kc, vc, lens, table, maxlen = make_decode(B, G * Hkv, Hkv, d, lens, seed, paged)
+    o, lse = run_decode(q, kc, vc, lens, table, maxlen, cfg.scale, splits)
+    ro, rl = decode_ref(q, kc, vc, lens, table, cfg.scale)
+    check(f"decode random seed={seed} B={B} Hq={G * Hkv} Hkv={Hkv} d={d} paged={paged} "
+          f"splits={splits}", o, lse, ro, rl)
+
+
+@pytest.mark.parametrize("seed", list(range(9300, 9308)))
+def test_prefill_varlen_random_shapes(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 6))
+    G = int(rng.choice([1, 2, 4]))
+    Hkv = int(rng.integers(1, 3))
+    d = int(rng.choice([64, 128]))
+    causal = bool(rng.integers(0, 2))
+    lens_k = rng.integers(1, 600, size=B)
+    lens_q = np.array([int(rng.integers(0, n + 1)) for n in lens_k]) if causal \
+        else rng.integers(0, 600, size=B)
+    q, k, v, cu_q, cu_k = ai.varlen_inputs(seed, lens_q, lens_k, G * Hkv, Hkv, d)
+    if cu_q[-1] == 0:
+        pytest.skip("no queries drawn")
+    o, lse = run_varlen(q, k, v, cu_q, cu_k, causal, 1 / math.sqrt(d))
+    ro, rl = attention_prefill_varlen(f64(q), f64(k), f64(v), cu_q, cu_k,
+                                      float(np.float32(1 / math.sqrt(d))), causal)
+    check(f"varlen random seed={seed} lens_q={lens_q.tolist()} lens_k={lens_k.tolist()} "
+          f"Hq={G * Hkv} Hkv={Hkv} d={d} causal={causal}", o, lse, ro, rl)
