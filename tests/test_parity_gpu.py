@@ -949,3 +949,39 @@ def test_prefill_varlen_random_shapes(seed):
                                       float(np.float32(1 / math.sqrt(d))), causal)
     check(f"varlen random seed={seed} lens_q={lens_q.tolist()} lens_k={lens_k.tolist()} "
           f"Hq={G * Hkv} Hkv={Hkv} d={d} causal={causal}", o, lse, ro, rl)
+
+
+@pytest.mark.parametrize("seed", list(range(9400, 9408)))
+def test_prefill_paged_random_shapes(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 5))
+    G = int(rng.choice([1, 2, 4, 8]))
+    Hkv = int(rng.integers(1, 3))
+    d = int(rng.choice([64, 128]))
+    Nq = int(rng.integers(1, 400))
+    lens = Nq + rng.integers(0, 1200, size=B)  # every context holds the Nq chunk queries
+    causal = bool(rng.integers(0, 2))
+    cfg, q, kc, vc, lens, table = make_chunk(B, G * Hkv, Hkv, d, lens, Nq, seed=seed)
+    scale = float(np.float32(rng.choice([1 / math.sqrt(d), -0.1])))
+    o, lse = run_chunk(q, kc, vc, lens, table, causal, scale)
+    ro, rl = attention_prefill_paged(f64(q), f64(kc), f64(vc), table, lens, scale, causal)
+    check(f"prefill_paged random seed={seed} B={B} Hq={G * Hkv} Hkv={Hkv} d={d} Nq={Nq} "
+          f"lens={lens.tolist()} causal={causal}", o, lse, ro, rl)
+
+
+@pytest.mark.parametrize("seed", list(range(9500, 9508)))
+def test_backward_random_shapes(seed):
+    rng = np.random.default_rng(seed)
+    G = int(rng.choice([1, 2, 3, 4]))
+    Hkv = int(rng.integers(1, 3))
+    d = int(rng.choice([64, 128]))
+    causal = bool(rng.integers(0, 2))
+    Nk = int(rng.integers(1, 400))
+    Nq = int(rng.integers(1, Nk + 1)) if causal else int(rng.integers(1, 400))
+    B = int(rng.integers(1, 3))
+    scale = float(np.float32(rng.choice([1 / math.sqrt(d), 0.2, -0.1])))
+    q, k, v, do = bwd_inputs(seed, B, G * Hkv, Hkv, Nq, Nk, d)
+    got = run_bwd(q, k, v, do, causal, scale)
+    ref = attention_backward(f64(q), f64(k), f64(v), f64(do), scale, causal)
+    check_grads(f"bwd random seed={seed} B={B} Hq={G * Hkv} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} "
+                f"causal={causal} scale={scale}", got, ref)
