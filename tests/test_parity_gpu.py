@@ -985,3 +985,30 @@ def test_backward_random_shapes(seed):
     ref = attention_backward(f64(q), f64(k), f64(v), f64(do), scale, causal)
     check_grads(f"bwd random seed={seed} B={B} Hq={G * Hkv} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} "
                 f"causal={causal} scale={scale}", got, ref)
+
+
+@pytest.mark.parametrize("seed", list(range(9600, 9606)))
+def test_decode_fp8_random_shapes(seed):
+    rng = np.random.default_rng(seed)
+    G = int(rng.choice([1, 4, 8, 20]))
+    Hkv = int(rng.integers(1, 3))
+    d = int(rng.choice([64, 128]))
+    B = int(rng.integers(1, 6))
+    lens = rng.integers(0, 2500, size=B)
+    paged = bool(rng.integers(0, 2))
+    cfg, q, kc, vc, lens, table, maxlen = make_decode(B, G * Hkv, Hkv, d, lens, seed, paged,
+                                                      fp8=True)
+    o, lse = run_decode_fp8(q, kc, vc, lens, table, maxlen, cfg.scale)
+    ro, rl = decode_fp8_ref(q, kc, vc, lens, table, cfg.scale)
+    check(f"decode fp8 random seed={seed} B={B} Hq={G * Hkv} Hkv={Hkv} d={d} paged={paged}",
+          o, lse, ro, rl)
+
+
+@pytest.mark.parametrize("seed", list(range(9700, 9706)))
+def test_prefill_f16_random_shapes(seed):
+    s = _random_shape(seed)
+    q, k, v = ai.custom_prefill(seed=seed, B=s["B"], Hq=s["Hq"], Hkv=s["Hkv"], Nq=s["Nq"],
+                                Nk=s["Nk"], d=s["d"], f16=True)
+    o, lse = run_prefill16(q, k, v, s["causal"], s["scale"])
+    ro, rl = attention_prefill(h64(q), h64(k), h64(v), s["scale"], s["causal"])
+    check(f"prefill f16 random seed={seed} {s}", o, lse, ro, rl)
