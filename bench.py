@@ -81,6 +81,39 @@ def kernel_sources_digest() -> str:
     return h.hexdigest()[:16]
 
 
+def device_clock_mhz():
+    """Peak shader clock of device 0 in MHz, from hipDeviceGetAttribute with
+    hipDeviceAttributeClockRate (kHz), asked of the HIP runtime already loaded for the
+    library (never a second copy); the enum's value is read from the installed HIP header.
+    None when any step is unavailable."""
+    try:
+        import ctypes
+        hdr = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "include", "hip",
+                           "hip_runtime_api.h")
+        src = open(hdr).read()
+        i = src.index("typedef enum hipDeviceAttribute_t {")
+        body = src[i:src.index("} hipDeviceAttribute_t;", i)]
+        body = re.sub(r"/\*.*?\*/", "", re.sub(r"//[^\n]*", "", body), flags=re.S)
+        val, names = -1, {}
+        for ent in body[body.index("{") + 1:].split(","):
+            ent = ent.strip()
+            if not ent:
+                continue
+            if "=" in ent:
+                n, e = (x.strip() for x in ent.split("=", 1))
+                val = int(e, 0) if re.fullmatch(r"0x[0-9a-fA-F]+|\d+", e) else names[e]
+            else:
+                n, val = ent, val + 1
+            names[n] = val
+        lib = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD | os.RTLD_GLOBAL)
+        khz = ctypes.c_int(0)
+        if lib.hipDeviceGetAttribute(ctypes.byref(khz), names["hipDeviceAttributeClockRate"], 0):
+            return None
+        return khz.value / 1000.0 if khz.value > 0 else None
+    except Exception:
+        return None
+
+
 def recorded_traffic(kernel: str):
     """HBM bytes per launch recorded from rocprofv3 counter runs in profiles/, if they
     were taken on the current kernel sources (else None)."""
@@ -288,6 +321,7 @@ def main():
     d_bytes = ai.decode_bytes(dcfg, lens)
     d_gbs = d_bytes / (d_avg * 1e-6) / 1e9
     props = torch.cuda.get_device_properties(0)
+    clk_mhz = device_clock_mhz()
 
     out = {
         "metric": METRIC,
@@ -318,9 +352,12 @@ def main():
                      "unit": "TFLOP/s", "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic("prefill_kernel<128,causal>"),
                      "kernel": "prefill_kernel<128, causal>",
-                     "us_per_launch": round(p_avg, 2), "flops_per_launch": p_flops},
+                     "us_per_launch": round(p_avg, 2),
+                     "us_median": round(float(np.median(p_us)), 2),
+                     "us_min": round(float(np.min(p_us)), 2), "flops_per_launch": p_flops},
         "decode": {
             "value": round(d_gbs, 1), "unit": "GB/s", "us_per_step": round(d_avg, 2),
+            "us_median": round(float(np.median(d_us)), 2), "us_min": round(float(np.min(d_us)), 2),
             "roofline": {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(d_gbs / PEAK_HBM_GBS, 4),
                          "traffic": decode_traffic(),
@@ -328,6 +365,12 @@ def main():
                          "bytes_per_launch": d_bytes},
         },
         "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "max_clock_mhz": clk_mhz,
+                   # dense bf16 MFMA peak recomputed from this device: CUs x 4096 FLOP/clk x
+                   # its peak clock (the roofline above uses the published figure)
+                   "peak_bf16_tflops_from_clock": (
+                       round(props.multi_processor_count * 4096 * clk_mhz * 1e6 / 1e12, 1)
+                       if clk_mhz else None),
                    "kernel_sources": kernel_sources_digest()},
     }
 
