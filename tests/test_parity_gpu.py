@@ -208,8 +208,22 @@ def test_prefill_long_context_32k():
                                 rows, cfg.Nq)
         errs.append(np.abs(go[0, h, rows] - ro).ravel())
         lerrs.append(np.abs(gl[0, h, rows] - rl).ravel())
+        # the first 1,024 rows of every head (causal: they see only the first 1,024 keys)
+        first = np.arange(1024)
+        ro, rl = attention_rows(f64(qh[h][:1024]), f64(k[0, h, :1024]), f64(v[0, h, :1024]),
+                                cfg.scale, True, first, 1024)
+        errs.append(np.abs(go[0, h, :1024] - ro).ravel())
+        lerrs.append(np.abs(gl[0, h, :1024] - rl).ravel())
+        # the last 1,024 rows, against all 32K keys, for four heads
+        if h in (0, 11, 22, 31):
+            last = np.arange(cfg.Nq - 1024, cfg.Nq)
+            ro, rl = attention_rows(f64(qh[h][last]), f64(k[0, h]), f64(v[0, h]), cfg.scale,
+                                    True, last, cfg.Nq)
+            errs.append(np.abs(go[0, h, last] - ro).ravel())
+            lerrs.append(np.abs(gl[0, h, last] - rl).ravel())
     err, lerr = np.concatenate(errs), np.concatenate(lerrs)
-    log_case("long_prefill_32k (sampled)", max_abs=float(err.max()), mean_abs=float(err.mean()),
+    log_case("long_prefill_32k (first 1,024 rows of every head, last 1,024 of four, sampled "
+             "rows)", max_abs=float(err.max()), mean_abs=float(err.mean()),
              lse_max_abs=float(lerr.max()), n=int(err.size))
     assert np.isfinite(go).all()
     assert err.max() <= TOL_MAX and err.mean() <= TOL_MEAN and lerr.max() <= TOL_LSE
