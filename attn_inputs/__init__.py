@@ -36,6 +36,8 @@ E4M3_NAN = np.uint8(0x7F)
 # pair of scales shows.
 FP8_K_SCALE = float(np.float32(8.0 / 448.0))
 FP8_V_SCALE = float(np.float32(6.0 / 448.0))
+# Scale of FP8 prefill queries (K and V use the two above).
+FP8_Q_SCALE = float(np.float32(7.0 / 448.0))
 
 
 # ----------------------------------------------------------------------------
@@ -118,10 +120,13 @@ def normal_bf16(seed: int, tensor: int, b: int, h: int, shape, mult: float = 1.0
     return to_f16_bits(x) if f16 else to_bf16_bits(x)
 
 
-def normal_e4m3(seed: int, tensor: int, b: int, h: int, shape, scale: float) -> np.ndarray:
-    """One head's slice of an FP8 cache: the float32 N(0,1) draws of ``normal_bf16`` (same
-    stream), divided by ``scale`` in float32, as E4M3 codes."""
+def normal_e4m3(seed: int, tensor: int, b: int, h: int, shape, scale: float,
+                mult: float = 1.0) -> np.ndarray:
+    """One head's slice of an FP8 tensor: the float32 N(0,1) draws of ``normal_bf16`` (same
+    stream, times ``mult`` in float32), divided by ``scale`` in float32, as E4M3 codes."""
     x = _stream(seed, tensor, b, h).standard_normal(shape, dtype=np.float32)
+    if mult != 1.0:
+        x *= np.float32(mult)
     return to_e4m3_codes(x / np.float32(scale))
 
 
@@ -141,6 +146,7 @@ class PrefillCfg:
     seed: int
     q_mult: float = 1.0
     f16: bool = False             # fp16 elements instead of bf16
+    fp8: bool = False             # Q, K, V as E4M3 codes with FP8_Q/K/V_SCALE (O bf16)
 
     @property
     def scale(self) -> float:
@@ -181,6 +187,9 @@ CONFIGS = {
     # The same draws rounded to fp16 (the fp16 entry points).
     "llama2_7b_prefill_f16": PrefillCfg("llama2_7b_prefill_f16", B=4, Hq=32, Hkv=32, Nq=2048,
                                         Nk=2048, d=128, causal=True, seed=2, f16=True),
+    # The same shape over FP8 (E4M3) Q, K, V with one scale per tensor.
+    "llama2_7b_prefill_fp8": PrefillCfg("llama2_7b_prefill_fp8", B=4, Hq=32, Hkv=32, Nq=2048,
+                                        Nk=2048, d=128, causal=True, seed=2, fp8=True),
     # Long-context prefill, Q scaled by 3 before rounding so softmax rows are peaky.
     "long_prefill_32k": PrefillCfg("long_prefill_32k", B=1, Hq=32, Hkv=32, Nq=32768, Nk=32768,
                                    d=128, causal=True, seed=3, q_mult=3.0),
@@ -210,17 +219,31 @@ CONFIGS = {
 # ----------------------------------------------------------------------------
 # Prefill inputs
 # ----------------------------------------------------------------------------
+def prefill_scales(cfg: PrefillCfg):
+    """(q_scale, k_scale, v_scale) of an FP8 prefill workload; 1.0 each otherwise."""
+    if not cfg.fp8:
+        return 1.0, 1.0, 1.0
+    return FP8_Q_SCALE, FP8_K_SCALE, FP8_V_SCALE
+
+
 def prefill_head(cfg: PrefillCfg, tensor: int, b: int, h: int) -> np.ndarray:
-    """bf16 bits of one head: Q [Nq, d] for tensor T_Q, K/V [Nk, d] for T_K/T_V."""
+    """bf16 bits of one head: Q [Nq, d] for tensor T_Q, K/V [Nk, d] for T_K/T_V (fp16 bits
+    when cfg.f16; E4M3 codes of the same draws over the tensor's scale when cfg.fp8)."""
+    if cfg.fp8:
+        sc = prefill_scales(cfg)[tensor]
+        if tensor == T_Q:
+            return normal_e4m3(cfg.seed, T_Q, b, h, (cfg.Nq, cfg.d), sc, cfg.q_mult)
+        return normal_e4m3(cfg.seed, tensor, b, h, (cfg.Nk, cfg.d), sc)
     if tensor == T_Q:
         return normal_bf16(cfg.seed, T_Q, b, h, (cfg.Nq, cfg.d), cfg.q_mult, cfg.f16)
     return normal_bf16(cfg.seed, tensor, b, h, (cfg.Nk, cfg.d), f16=cfg.f16)
 
 
 def prefill_inputs(cfg: PrefillCfg):
-    """Whole tensors as bf16 bits: q [B,Hq,Nq,d], k and v [B,Hkv,Nk,d]."""
-    q = np.empty((cfg.B, cfg.Hq, cfg.Nq, cfg.d), np.uint16)
-    k = np.empty((cfg.B, cfg.Hkv, cfg.Nk, cfg.d), np.uint16)
+    """Whole tensors as bf16 bits (fp16 bits, E4M3 codes): q [B,Hq,Nq,d], k and v
+    [B,Hkv,Nk,d]."""
+    q = np.empty((cfg.B, cfg.Hq, cfg.Nq, cfg.d), np.uint8 if cfg.fp8 else np.uint16)
+    k = np.empty((cfg.B, cfg.Hkv, cfg.Nk, cfg.d), np.uint8 if cfg.fp8 else np.uint16)
     v = np.empty_like(k)
     for b in range(cfg.B):
         for h in range(cfg.Hq):
@@ -242,9 +265,9 @@ def prefill_dout(cfg: PrefillCfg) -> np.ndarray:
 
 
 def custom_prefill(seed: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int,
-                   q_mult: float = 1.0, f16: bool = False):
+                   q_mult: float = 1.0, f16: bool = False, fp8: bool = False):
     """Inputs for an arbitrary prefill shape (edge cases), same recipe."""
-    cfg = PrefillCfg("custom", B, Hq, Hkv, Nq, Nk, d, True, seed, q_mult, f16)
+    cfg = PrefillCfg("custom", B, Hq, Hkv, Nq, Nk, d, True, seed, q_mult, f16, fp8)
     return prefill_inputs(cfg)
 
 
@@ -410,10 +433,12 @@ def backward_flops(cfg: PrefillCfg) -> int:
 
 
 def prefill_bytes(cfg: PrefillCfg) -> int:
-    """Algorithmic HBM bytes: Q, K, V read once, O written once, LSE written once."""
-    q = cfg.B * cfg.Hq * cfg.Nq * cfg.d * 2
-    kv = 2 * cfg.B * cfg.Hkv * cfg.Nk * cfg.d * 2
-    return q + kv + q + cfg.B * cfg.Hq * cfg.Nq * 4
+    """Algorithmic HBM bytes: Q, K, V read once, O written once, LSE written once (FP8
+    inputs are 1 byte per element; O is 2 bytes either way)."""
+    eb = 1 if cfg.fp8 else 2
+    q = cfg.B * cfg.Hq * cfg.Nq * cfg.d
+    kv = 2 * cfg.B * cfg.Hkv * cfg.Nk * cfg.d * eb
+    return q * eb + kv + q * 2 + cfg.B * cfg.Hq * cfg.Nq * 4
 
 
 def decode_bytes(cfg: DecodeCfg, lengths: np.ndarray) -> int:

@@ -295,6 +295,22 @@ def attention_decode_fp8(q: np.ndarray, kcodes: np.ndarray, vcodes: np.ndarray,
     return o, lse
 
 
+def attention_prefill_fp8(qcodes: np.ndarray, kcodes: np.ndarray, vcodes: np.ndarray,
+                          scale: float, q_scale: float, k_scale: float, v_scale: float,
+                          causal: bool, row_block: int = 1024):
+    """Prefill over FP8 inputs with one scale per tensor (the FP8 forward that the page
+    "Flash Attention: GPU 메모리_IO를 최적화하는..." (holysheep), "FlashAttention 3"
+    subsection, lists; the pages give no format or scale convention, so the reading is
+    OCP E4M3 codes with per-tensor scales, as for the FP8 cache): Q is
+    q_scale * e4m3_value(qcodes), K and V likewise with k_scale and v_scale, laid out as in
+    attention_prefill.  The result is the plain definition on those dequantised values.
+    Returns O [B,Hq,Nq,d], LSE [B,Hq,Nq] (float64)."""
+    Q = q_scale * e4m3_value(qcodes)
+    K = k_scale * e4m3_value(kcodes)
+    V = v_scale * e4m3_value(vcodes)
+    return attention_prefill(Q, K, V, scale, causal, row_block)
+
+
 def attention_prefill_paged(q: np.ndarray, kpool: np.ndarray, vpool: np.ndarray,
                             block_table: np.ndarray, kv_lens: np.ndarray, scale: float,
                             causal: bool, page_size: int = 16, row_block: int = 1024):

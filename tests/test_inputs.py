@@ -140,6 +140,28 @@ def test_fp8_cache_quantises_the_bf16_workload_draws():
     assert ai.decode_bytes(base, lb) - ai.decode_bytes(f8, lb) == kv
 
 
+def test_fp8_prefill_quantises_the_bf16_workload_draws():
+    base = ai.PrefillCfg("t", B=1, Hq=2, Hkv=1, Nq=40, Nk=56, d=8, causal=True, seed=12,
+                         q_mult=2.0)
+    f8 = ai.PrefillCfg("t", B=1, Hq=2, Hkv=1, Nq=40, Nk=56, d=8, causal=True, seed=12,
+                       q_mult=2.0, fp8=True)
+    qs, ks, vs = ai.prefill_scales(f8)
+    assert (qs, ks, vs) == (ai.FP8_Q_SCALE, ai.FP8_K_SCALE, ai.FP8_V_SCALE)
+    assert ai.prefill_scales(base) == (1.0, 1.0, 1.0)
+    q, k, v = ai.prefill_inputs(f8)
+    assert q.dtype == k.dtype == v.dtype == np.uint8
+    draw = lambda t, h, n, m=1.0: np.random.default_rng(np.random.SeedSequence(
+        [12, t, 0, h])).standard_normal((n, 8), dtype=np.float32) * np.float32(m)
+    np.testing.assert_array_equal(q[0, 1], _torch_e4m3(draw(ai.T_Q, 1, 40, 2.0) / np.float32(qs)))
+    np.testing.assert_array_equal(k[0, 0], _torch_e4m3(draw(ai.T_K, 0, 56) / np.float32(ks)))
+    np.testing.assert_array_equal(v[0, 0], _torch_e4m3(draw(ai.T_V, 0, 56) / np.float32(vs)))
+    # one byte per input element, two per output element
+    full = ai.CONFIGS["llama2_7b_prefill_fp8"]
+    elems = full.B * full.Hq * full.Nq * full.d
+    assert ai.prefill_bytes(full) == 3 * elems + 2 * elems + full.B * full.Hq * full.Nq * 4
+    assert ai.prefill_flops(full) == ai.prefill_flops(ai.CONFIGS["llama2_7b_prefill"])
+
+
 # ----------------------------------------------------------------------------- fp16 rounding
 def test_f16_rounding_matches_torch():
     rng = np.random.default_rng(2)

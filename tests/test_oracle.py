@@ -515,6 +515,63 @@ def test_fp8_paged_equals_contiguous():
     np.testing.assert_array_equal(l1, l0)
 
 
+# ----------------------------------------------------------------------------- FP8 prefill
+def _fp8_prefill_case(seed, B=2, Hq=4, Hkv=2, Nq=5, Nk=7, d=3):
+    rng = np.random.default_rng(seed)
+    codes = [c for c in range(256) if c & 0x7F != 0x7F]
+    qc = rng.choice(codes, (B, Hq, Nq, d)).astype(np.uint8)
+    kc = rng.choice(codes, (B, Hkv, Nk, d)).astype(np.uint8)
+    vc = rng.choice(codes, (B, Hkv, Nk, d)).astype(np.uint8)
+    return qc, kc, vc
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_prefill_matches_brute_force_on_torch_dequantised_inputs(causal):
+    import torch
+    from oracle import attention_prefill_fp8
+    qc, kc, vc = _fp8_prefill_case(81)
+    qs, ks, vs = 0.011, 0.0173, 0.031
+    o, lse = attention_prefill_fp8(qc, kc, vc, 0.45, qs, ks, vs, causal)
+    deq = lambda c: torch.from_numpy(c).view(torch.float8_e4m3fn).double().numpy()
+    for b in range(2):
+        for h in range(4):
+            bo, bl = brute_force_attention((qs * deq(qc[b, h])).tolist(),
+                                           (ks * deq(kc[b, h // 2])).tolist(),
+                                           (vs * deq(vc[b, h // 2])).tolist(), 0.45, causal)
+            np.testing.assert_allclose(o[b, h], np.array(bo), rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(lse[b, h], np.array(bl), rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_prefill_scales_fold_into_the_softmax_scale_and_the_output():
+    from oracle import attention_prefill_fp8
+    qc, kc, vc = _fp8_prefill_case(82)
+    o0, l0 = attention_prefill_fp8(qc, kc, vc, 0.3 * 0.02 * 0.05, 1.0, 1.0, 1.0, True)
+    o1, l1 = attention_prefill_fp8(qc, kc, vc, 0.3, 0.02, 0.05, 1.0, True)
+    np.testing.assert_allclose(o1, o0, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l1, l0, rtol=1e-12, atol=1e-13)
+    # Q and K scales enter only through their product
+    o2, l2 = attention_prefill_fp8(qc, kc, vc, 0.3, 0.05, 0.02, 1.0, True)
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l2, l1, rtol=1e-12, atol=1e-13)
+    # the V scale multiplies O and leaves LSE alone
+    o3, l3 = attention_prefill_fp8(qc, kc, vc, 0.3, 0.02, 0.05, 0.125, True)
+    np.testing.assert_allclose(o3, 0.125 * o1, rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(l3, l1)
+    # and is not interchangeable with the K scale
+    o4, _ = attention_prefill_fp8(qc, kc, vc, 0.3, 0.02, 0.125, 0.05, True)
+    assert np.abs(o4 - o3).max() > 1e-3
+
+
+def test_fp8_prefill_negated_query_codes_equal_a_negated_scale():
+    # flipping bit 7 of every Q code negates Q exactly (sign-magnitude format)
+    from oracle import attention_prefill_fp8
+    qc, kc, vc = _fp8_prefill_case(83)
+    o0, l0 = attention_prefill_fp8(qc ^ np.uint8(0x80), kc, vc, 0.4, 0.02, 0.05, 0.1, False)
+    o1, l1 = attention_prefill_fp8(qc, kc, vc, -0.4, 0.02, 0.05, 0.1, False)
+    np.testing.assert_allclose(o0, o1, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l0, l1, rtol=1e-12, atol=1e-13)
+
+
 # ----------------------------------------------------------------------------- backward
 def _bwd_case(seed, B=1, Hq=2, Hkv=1, Nq=5, Nk=7, d=3):
     rng = np.random.default_rng(seed)
