@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 import attn_inputs as ai  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense FP8 MFMA (twice the bf16 rate)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "prefill attention TFLOPS and decode KV GB/s at 1 MI355X, % of roofline"
 PREFILL_CFG = "llama2_7b_prefill"
@@ -140,9 +141,13 @@ def prefill_setup(name):
     import torch
     cfg = ai.CONFIGS[name]
     q, k, v = ai.prefill_inputs(cfg)
-    conv = to_dev16 if cfg.f16 else to_dev
+    if cfg.fp8:   # E4M3 codes stay bytes; O is bf16
+        conv = lambda c: torch.from_numpy(np.ascontiguousarray(c)).cuda()
+    else:
+        conv = to_dev16 if cfg.f16 else to_dev
     dq, dk, dv = conv(q), conv(k), conv(v)
-    o = torch.empty_like(dq)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda") if cfg.fp8 else \
+        torch.empty_like(dq)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
     return cfg, (dq, dk, dv, o, lse)
 
@@ -377,16 +382,29 @@ def main():
     if not args.no_extra:
         extra = {}
         del q, k, v, o, lse
-        for name in ("llama2_7b_prefill_noncausal", "long_prefill_32k", "llama2_7b_prefill_f16"):
+        for name in ("llama2_7b_prefill_noncausal", "long_prefill_32k", "llama2_7b_prefill_f16",
+                     "llama2_7b_prefill_fp8"):
             cfg, (eq, ek, ev_, eo, el) = prefill_setup(name)
-            fwd = mi.attn_fwd_prefill_f16 if cfg.f16 else mi.attn_fwd_prefill
+            if cfg.fp8:
+                qs, ks, vs = ai.prefill_scales(cfg)
+                call = lambda: mi.attn_fwd_prefill_fp8(eq, ek, ev_, eo, el, cfg.causal,
+                                                       cfg.scale, qs, ks, vs, stream)
+            else:
+                fwd = mi.attn_fwd_prefill_f16 if cfg.f16 else mi.attn_fwd_prefill
+                call = lambda: fwd(eq, ek, ev_, eo, el, cfg.causal, cfg.scale, stream)
             avg, med, mn = time_kernel(
-                lambda: fwd(eq, ek, ev_, eo, el, cfg.causal, cfg.scale, stream),
-                max(3, args.steps // 4) if name == "long_prefill_32k" else args.steps,
+                call, max(3, args.steps // 4) if name == "long_prefill_32k" else args.steps,
                 args.warmup)
             tf = ai.prefill_flops(cfg) / (avg * 1e-6) / 1e12
             extra[name] = {"us": round(avg, 2), "us_min": round(mn, 2), "TFLOP/s": round(tf, 2),
                            "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+            if cfg.fp8:
+                # same shape and FLOPs as the bf16 causal prefill timed above
+                extra[name]["speedup_vs_bf16"] = round(p_avg / avg, 3)
+                # half the FLOPs (Q.K^T) on the FP8 MFMA, half (P.V) on the bf16 one
+                mixed = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
+                extra[name]["peak_mixed_tflops"] = round(mixed, 1)
+                extra[name]["frac_mixed"] = round(tf / mixed, 4)
             del eq, ek, ev_, eo, el
             torch.cuda.empty_cache()
         del dq, dkc, dvc, table, seq, do, dlse, ws

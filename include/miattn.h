@@ -87,6 +87,30 @@ int attn_fwd_prefill_f16(const void* q, const void* k, const void* v, void* o, f
                          hipStream_t stream);
 
 /*
+ * Prefill over FP8 inputs: attn_fwd_prefill with q, k and v stored as OCP FP8 E4M3 codes
+ * (1 byte per element, the format of attn_fwd_decode_fp8) and one scale per tensor, so
+ * the query is q_scale * e4m3(code), and likewise the key (k_scale) and value (v_scale).
+ * The FP8 forward of the page "Flash Attention: GPU 메모리_IO를 최적화하는..." (holysheep),
+ * subsection "FlashAttention 3".  Q K^T runs on the FP8 matrix cores with fp32
+ * accumulation (every product is exact); V is widened to bf16 exactly, P is rounded to
+ * bf16 (nearest even) before P*V, and o is bf16 as in attn_fwd_prefill.
+ *
+ *   q    [B, Hq,  Nq, d] uint8 codes, 16-byte aligned
+ *   k, v [B, Hkv, Nk, d] uint8 codes, 16-byte aligned
+ *   o    [B, Hq,  Nq, d] bf16 (written), 16-byte aligned
+ *   lse  [B, Hq,  Nq]    fp32 (written) or NULL, of the dequantised scores
+ *   q_scale, k_scale, v_scale  finite and > 0.
+ *   All other arguments are those of attn_fwd_prefill.
+ *
+ * Errors: those of attn_fwd_prefill (with Nk*d beyond 2^31-1 bytes for UNSUPPORTED),
+ * plus INVALID_ARGUMENT for a non-finite or non-positive q_scale, k_scale or v_scale, or
+ * when |scale| * q_scale * k_scale overflows float.
+ */
+int attn_fwd_prefill_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                         float q_scale, float k_scale, float v_scale, hipStream_t stream);
+
+/*
  * Chunked (append) prefill against a paged KV cache: the Nq newest tokens of every
  * sequence attend to that sequence's whole cached context, which already holds their
  * own keys and values as its last Nq tokens.  This is the prefill step of chunked

@@ -54,6 +54,8 @@ def load_library():
     lib.attn_fwd_prefill.restype = i32
     lib.attn_fwd_prefill_f16.argtypes = lib.attn_fwd_prefill.argtypes
     lib.attn_fwd_prefill_f16.restype = i32
+    lib.attn_fwd_prefill_fp8.argtypes = [vp] * 5 + [i32] * 7 + [f32] * 4 + [vp]
+    lib.attn_fwd_prefill_fp8.restype = i32
     lib.attn_fwd_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp] + [i32] * 10 + [f32, vp]
     lib.attn_fwd_prefill_paged.restype = i32
     lib.attn_fwd_prefill_paged_f16.argtypes = lib.attn_fwd_prefill_paged.argtypes
@@ -108,7 +110,7 @@ def _check(t, name, dtype, ndim, device=None):
         raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
     if device is not None and t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
-    if t.dtype != dtype:
+    if (t.dtype not in dtype) if isinstance(dtype, tuple) else (t.dtype != dtype):
         raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dimensions (got {tuple(t.shape)})")
@@ -117,13 +119,13 @@ def _check(t, name, dtype, ndim, device=None):
 
 
 # -------------------------------------------------------------------------------- prefill
-def _prefill_call(fn, dtype, q, k, v, o, lse, causal, scale, stream):
+def _prefill_call(fn, dtype, q, k, v, o, lse, causal, scale, stream, fp8_scales=None):
     lib = load_library()
     _check(q, "q", dtype, 4)
     dev = q.device
     _check(k, "k", dtype, 4, dev)
     _check(v, "v", dtype, 4, dev)
-    _check(o, "o", dtype, 4, dev)
+    _check(o, "o", torch.bfloat16 if fp8_scales else dtype, 4, dev)
     B, Hq, Nq, d = q.shape
     Bk, Hkv, Nk, dk = k.shape
     if Bk != B or dk != d or tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape):
@@ -132,8 +134,9 @@ def _prefill_call(fn, dtype, q, k, v, o, lse, causal, scale, stream):
         _check(lse, "lse", torch.float32, 3, dev)
         if tuple(lse.shape) != (B, Hq, Nq):
             raise ValueError("lse must be [B, Hq, Nq]")
+    extra = [float(x) for x in fp8_scales] if fp8_scales else []
     st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk,
-                          d, 1 if causal else 0, float(scale), _stream_handle(stream))
+                          d, 1 if causal else 0, float(scale), *extra, _stream_handle(stream))
     if st != ATTN_OK:
         raise AttnError(st, fn)
 
@@ -146,6 +149,25 @@ def attn_fwd_prefill(q, k, v, o, lse, causal: bool, scale: float, stream=None) -
 def attn_fwd_prefill_f16(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
     """attn_fwd_prefill with fp16 q, k, v, o."""
     _prefill_call("attn_fwd_prefill_f16", torch.float16, q, k, v, o, lse, causal, scale, stream)
+
+
+def attn_fwd_prefill_fp8(q, k, v, o, lse, causal: bool, scale: float, q_scale: float,
+                         k_scale: float, v_scale: float, stream=None) -> None:
+    """attn_fwd_prefill over FP8 inputs: q, k, v hold OCP E4M3 codes (torch.uint8 or
+    torch.float8_e4m3fn) standing for q_scale * e4m3(code) (k_scale, v_scale); o is bf16."""
+    _prefill_call("attn_fwd_prefill_fp8", (torch.uint8, torch.float8_e4m3fn), q, k, v, o, lse,
+                  causal, scale, stream, (q_scale, k_scale, v_scale))
+
+
+def prefill_fp8(q, k, v, q_scale: float, k_scale: float, v_scale: float, causal: bool = True,
+                scale: float | None = None):
+    """Allocate O (bf16) and LSE and run attn_fwd_prefill_fp8.  scale None means 1/sqrt(d)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    attn_fwd_prefill_fp8(q, k, v, o, lse, causal, scale, q_scale, k_scale, v_scale)
+    return o, lse
 
 
 def prefill(q, k, v, causal: bool = True, scale: float | None = None):
@@ -486,7 +508,8 @@ def backward(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = N
 __all__ = ["attn_bwd", "attn_bwd_f16", "attn_bwd_workspace_bytes", "backward", "attn_fwd_prefill_varlen",
            "attn_fwd_prefill_varlen_f16",
            "prefill_varlen",
-           "attn_fwd_prefill", "attn_fwd_prefill_f16", "attn_fwd_prefill_paged_f16",
+           "attn_fwd_prefill", "attn_fwd_prefill_f16", "attn_fwd_prefill_fp8", "prefill_fp8",
+           "attn_fwd_prefill_paged_f16",
            "attn_fwd_decode", "attn_fwd_decode_f16", "attn_fwd_decode_fp8",
            "attn_decode_workspace_bytes", "decode_fp8",
            "attn_decode_num_splits", "attn_status_string", "prefill", "decode",

@@ -45,14 +45,6 @@ struct DecodeShape {
   static_assert(RED <= LDS, "reduction scratch fits in the staging LDS");
 };
 
-// Four E4M3 codes (byte k of x is code k) as four bf16, code k in element k:
-// v_cvt_scalef32_pk_bf16_fp8 with unit scale on the low, then the high code pair.
-__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t x) {
-  const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
-  const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true);
-  return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-}
-
 constexpr int kDecodeSetsF8 = 3;  // FP8 blocks in flight per wave
 // Cache policy of the K/V loads: nt (non-temporal), the hint for data read once per step.
 // The KV cache is streamed once per decode step and nothing rereads it; with nt the

@@ -92,6 +92,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Four E4M3 codes (byte k of x is code k) as four bf16, code k in element k:
+// v_cvt_scalef32_pk_bf16_fp8 with unit scale on the low, then the high code pair.  Every
+// E4M3 value is exact in bf16.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t x) {
+  const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
+  const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true);
+  return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
 // acc + lo(x) + hi(x) for a packed bf16 pair x (v_dot2_f32_bf16 against (1, 1)).
 __device__ __forceinline__ float add_bf16x2(uint32_t x, float acc) {
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -112,6 +121,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 struct ElemBf16 {
+  static constexpr bool kFp8 = false;
   // weights stay below 2^32: far inside the fp32 and bf16 ranges
   static constexpr float kRedoBound = 4294967296.0f;
   static __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -135,6 +145,7 @@ struct ElemBf16 {
 };
 
 struct ElemF16 {
+  static constexpr bool kFp8 = false;
   // fp16 tops out at 65504, so a tile's weights (each at most their sum) stay below 2^15
   static constexpr float kRedoBound = 32768.0f;
   static __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -167,6 +178,22 @@ struct ElemF16 {
   }
 };
 
+// FP8 prefill: Q, K and V arrive as OCP E4M3 codes.  Q.K^T runs on the FP8 matrix cores;
+// V is widened to bf16 in LDS (exactly), so P, the P.V products and O are bf16 as for
+// ElemBf16.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+struct ElemFp8 : ElemBf16 {
+  static constexpr bool kFp8 = true;
+  // D = A(32x64) * B(64x32) + C on E4M3 operands (v_mfma_f32_32x32x64_f8f6f4, both formats
+  // E4M3, no block scales).  Lane l holds 32 codes of row l%32 of A and of column l%32 of
+  // B; the K index a byte stands for may be any assignment shared by A and B in which
+  // lanes l and l+32 hold complementary halves.  C is laid out as for mfma32.
+  static __device__ __forceinline__ f32x16 mfma_qk(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  }
+};
+
 // LDS tiles of D-wide bf16/fp16 rows (ROWB = 2*D bytes, unpadded) used by the prefill and
 // backward kernels.
 // XOR applied to the 16-byte chunk index of row R.  Chosen so that both LDS read
@@ -191,6 +218,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// s_waitcnt lgkmcnt(0): this wave's LDS writes (and reads) have completed.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 

@@ -26,6 +26,10 @@ struct PrefillParams {
   int max_blocks;
   uint32_t page_max;  // num_pages - 1: page ids are clamped to it
   int f16;  // Q, K, V, O are fp16 (else bf16)
+  // FP8 (dense layout only): Q, K, V are E4M3 codes, O is bf16; c then carries the Q and
+  // K scales, and v_scale multiplies the normalised output.
+  int fp8;
+  float v_scale;
   // Varlen (cu_q non-null): q, o are [total_q, Hq, D] and k, v [total_k, Hkv, D], sequence
   // b owning rows [cu_q[b], cu_q[b+1]) and [cu_k[b], cu_k[b+1]); lse is [Hq, total_q].
   // Nq and Nk are then the longest sequence's lengths.

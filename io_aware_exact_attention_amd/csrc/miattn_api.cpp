@@ -126,9 +126,11 @@ int decode_impl(const void* q, const void* kcache, const void* vcache,
 }
 
 // The prefill entry points (bf16 or fp16 elements).
+// (and, with fp8, the FP8 one: E4M3 q, k, v with per-tensor scales, bf16 o).
 int prefill_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                  int Hkv, int Nq, int Nk, int d, int causal, float scale, bool f16,
-                 hipStream_t stream) {
+                 hipStream_t stream, bool fp8 = false, float q_scale = 1.f,
+                 float k_scale = 1.f, float v_scale = 1.f) {
   if (!q || !k || !v || !o) return ATTN_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
     return ATTN_ERR_INVALID_ARGUMENT;
@@ -141,8 +143,11 @@ int prefill_impl(const void* q, const void* k, const void* v, void* o, float* ls
   const long qtiles = (Nq + 127) / 128;
   if (qtiles * (long)Hq * B > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
   if ((long)B * Hq > 0x7fffffffL || (long)B * Hkv > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
+  if (fp8 && !(std::isfinite(q_scale) && q_scale > 0.f && std::isfinite(k_scale) &&
+               k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+    return ATTN_ERR_INVALID_ARGUMENT;
   // one head's K (or V) must fit a buffer descriptor's 32-bit byte range
-  if ((long)Nk * d * 2 > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
+  if ((long)Nk * d * (fp8 ? 1 : 2) > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
 
   miattn::PrefillParams p{};
   p.q = static_cast<const uint16_t*>(q);
@@ -152,8 +157,12 @@ int prefill_impl(const void* q, const void* k, const void* v, void* o, float* ls
   p.lse = lse;
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk;
   p.c = std::fabs(scale) * 1.4426950408889634f;
+  if (fp8) p.c *= q_scale * k_scale;
+  if (!std::isfinite(p.c)) return ATTN_ERR_INVALID_ARGUMENT;
   p.negate_q = scale < 0.f;
   p.f16 = f16;
+  p.fp8 = fp8;
+  p.v_scale = v_scale;
   (void)hipGetLastError();  // clear a stale error so the check below is ours
   return miattn::launch_prefill(p, d, causal ? 1 : 0, stream) == hipSuccess ? ATTN_OK
                                                                              : ATTN_ERR_HIP;
@@ -304,6 +313,13 @@ int attn_fwd_prefill_f16(const void* q, const void* k, const void* v, void* o, f
                          int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                          hipStream_t stream) {
   return prefill_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, true, stream);
+}
+
+int attn_fwd_prefill_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                         float q_scale, float k_scale, float v_scale, hipStream_t stream) {
+  return prefill_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, false, stream, true,
+                      q_scale, k_scale, v_scale);
 }
 
 int attn_fwd_prefill_paged(const void* q, const void* kcache, const void* vcache,

@@ -39,22 +39,40 @@
 
 namespace miattn {
 
-template <int D>
+// F8: the ring holds E4M3 K and V tiles (D bytes per row); each V tile is widened to a
+// bf16 tile of ROWB-byte rows in one of two buffers after the ring, which the P.V reads use.
+template <int D, bool F8 = false>
 struct PrefillShape {
   static constexpr int kWaves = 8;
   static constexpr int BM = 32 * kWaves;        // queries per workgroup
   static constexpr int BN = 64;                 // keys per tile
-  static constexpr int ROWB = D * 2;            // bytes per K/V row in LDS (swizzled, unpadded)
-  static constexpr int CPR = D / 8;             // 16-byte chunks per row
-  static constexpr int TILE = BN * ROWB;        // bytes of one K (or V) tile
+  static constexpr int ROWB = D * 2;            // bytes per bf16 K/V row in LDS (swizzled)
+  static constexpr int CPR = D / 8;             // 16-byte chunks per bf16 row
+  static constexpr int KROWB = F8 ? D : ROWB;   // bytes per row of a ring tile
+  static constexpr int TILE = BN * KROWB;       // bytes of one K (or V) tile in the ring
   static constexpr int STAGES = 4;
   static constexpr int STAGE = 2 * TILE;        // K tile then V tile
-  static constexpr int LDS = STAGES * STAGE;
-  static constexpr int DMA = TILE / 16 / (64 * kWaves);  // 16-byte loads per thread per tensor
-  static constexpr int LOADS_PER_TILE = 2 * DMA;
-  static_assert(TILE % (16 * 64 * kWaves) == 0, "tile must split evenly over threads");
+  static constexpr int RING = STAGES * STAGE;
+  static constexpr int VTILE = BN * ROWB;       // F8: one widened V tile
+  static constexpr int LDS = RING + (F8 ? 2 * VTILE : 0);
+  // bf16/fp16: 16-byte loads per thread per tensor and tile
+  static constexpr int DMA = F8 ? 1 : TILE / 16 / (64 * kWaves);
+  // 1 KB LDS DMA blocks per wave and tile (K and V)
+  static constexpr int LOADS_PER_TILE = 2 * TILE / 1024 / kWaves;
+  static_assert(F8 || TILE % (16 * 64 * kWaves) == 0, "tile must split evenly over threads");
+  static_assert((2 * TILE) % (1024 * kWaves) == 0, "tile must split evenly over waves");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
+
+// F8 ring K tiles: XOR applied to the 16-byte chunk index of row R (D-byte rows), chosen
+// so that the K operand read (16 lanes, rows swap_bits_2_3(0..15), one chunk) touches 16
+// different 16-byte bank groups, as does each group of 8 of those lanes within 128 bytes.
+template <int D>
+__device__ __forceinline__ int chunk_swizzle_f8(int R) {
+  const int b0 = R & 1, b1 = (R >> 1) & 1, b2 = (R >> 2) & 1, b3 = (R >> 3) & 1;
+  if constexpr (D == 128) return b1 | (b3 << 1) | ((b0 ^ b2) << 2);
+  else return b3 | ((b1 ^ b2) << 1);
+}
 
 // Workgroup barrier that is also a hard scheduling boundary: no instruction (memory or
 // ALU) is moved across it, so the MFMA and softmax phases of the two wave groups stay
@@ -146,10 +164,14 @@ __device__ __forceinline__ PagedItem paged_work_item(int p, int B, int Hq, int n
 // Layouts: dense [B, H, N, D] (PAGED and VARLEN false); PAGED: K/V in the paged cache,
 // kv_lens per sequence; VARLEN: sequences packed along the token axis, [total, H, D], with
 // cumulative lengths cu_q, cu_k.
+// F8 (E = ElemFp8, dense layout only): Q, K, V are E4M3 codes; Q.K^T runs on the FP8
+// MFMA, V is widened to bf16 in LDS, and O is scaled by v_scale.
 template <int D, bool CAUSAL, bool PAGED, bool VARLEN, typename E>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillParams a) {
-  using S = PrefillShape<D>;
+  constexpr bool F8 = E::kFp8;
+  static_assert(!(F8 && (PAGED || VARLEN)), "FP8 prefill takes the dense layout");
+  using S = PrefillShape<D, F8>;
   __shared__ __attribute__((aligned(1024))) char smem[S::LDS];
 
   const int tid = threadIdx.x;
@@ -208,6 +230,10 @@ void prefill_kernel(PrefillParams a) {
       PAGED ? a.v
             : (VARLEN ? a.v + ((size_t)k_start * a.Hkv + kvh) * D
                       : a.v + (size_t)(b * a.Hkv + kvh) * a.Nk * D);
+  // F8: the same dense tensors as one byte per element
+  const uint8_t* __restrict__ Q8h = (const uint8_t*)a.q + (size_t)(b * a.Hq + hq) * a.Nq * D;
+  const uint8_t* __restrict__ K8h = (const uint8_t*)a.k + (size_t)(b * a.Hkv + kvh) * a.Nk * D;
+  const uint8_t* __restrict__ V8h = (const uint8_t*)a.v + (size_t)(b * a.Hkv + kvh) * a.Nk * D;
 
   // keys the workgroup needs: everything, or up to the diagonal of its last query
   int kend = nk;
@@ -237,12 +263,28 @@ void prefill_kernel(PrefillParams a) {
   // offsets are the same for every tile; all per-tile address work is scalar.
   // (Varlen rows are kstride apart in memory; the LDS layout is the same.)
   const int krow_bytes = VARLEN ? (int)kstride * 2 : S::ROWB;
-  uint32_t dma_off[S::DMA];
+  constexpr int NOFF = F8 ? S::LOADS_PER_TILE : S::DMA;
+  uint32_t dma_off[NOFF];
+  if constexpr (F8) {
+    // block blk = i*kWaves + wave of the stage: K blocks (swizzled rows) first, then the V
+    // blocks, which keep the rows' byte order (the widening reads them linearly)
 #pragma unroll
-  for (int i = 0; i < S::DMA; ++i) {
-    const int p = (i * S::kWaves + wave) * 64 + lane;
-    const int R = p / S::CPR;
-    dma_off[i] = R * krow_bytes + (((p % S::CPR) ^ chunk_swizzle<D>(R)) << 4);
+    for (int i = 0; i < NOFF; ++i) {
+      const int blk = i * S::kWaves + wave;
+      if (blk < S::TILE / 1024) {
+        const int p = blk * 64 + lane, R = p / (D / 16);
+        dma_off[i] = R * D + (((p % (D / 16)) ^ chunk_swizzle_f8<D>(R)) << 4);
+      } else {
+        dma_off[i] = ((blk - S::TILE / 1024) * 64 + lane) * 16;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < S::DMA; ++i) {
+      const int p = (i * S::kWaves + wave) * 64 + lane;
+      const int R = p / S::CPR;
+      dma_off[i] = R * krow_bytes + (((p % S::CPR) ^ chunk_swizzle<D>(R)) << 4);
+    }
   }
   // Paged cache [pages, Hkv, 16, D]: each 1 KB DMA block (RPB rows) lies inside one
   // 16-token page and gets its own descriptor.  The page ids of a tile's blocks are read
@@ -265,7 +307,17 @@ void prefill_kernel(PrefillParams a) {
   auto issue_tile = [&](int j) {
     const int n0 = j * S::BN;
     char* st = smem + (j & (S::STAGES - 1)) * S::STAGE;
-    if (PAGED) {
+    if constexpr (F8) {
+      const int nbytes = (nk - n0) * D;
+      const uint8_t* kt = K8h + (size_t)n0 * D;
+      const uint8_t* vt = V8h + (size_t)n0 * D;
+#pragma unroll
+      for (int i = 0; i < NOFF; ++i) {
+        const int blk = i * S::kWaves + wave;
+        lds_dma16(blk < S::TILE / 1024 ? kt : vt, nbytes, dma_off[i],
+                  (lds_void*)(st + blk * 1024));
+      }
+    } else if (PAGED) {
       int pg[S::DMA];
 #pragma unroll
       for (int i = 0; i < S::DMA; ++i) pg[i] = pg_next[i];
@@ -307,10 +359,25 @@ void prefill_kernel(PrefillParams a) {
     }
   };
 
-  // --- Q^T operand: lane holds query row qrow, head-dim slots 16*s + 8*g .. +7
+  // --- Q^T operand: lane holds query row qrow, head-dim slots 16*s + 8*g .. +7.
+  // F8: 32 codes per 64-dim step s, head-dim slots 64*s + 16*g .. +15 and 64*s + 32 + 16*g
+  // .. +15 (the K operand reads the same slots of its key rows).
   const int qrow = wrow0 + (lane & 31);
-  bf16x8 qop[D / 16];
-  {
+  using QOp = std::conditional_t<F8, i32x8, bf16x8>;
+  QOp qop[F8 ? D / 64 : D / 16];
+  if constexpr (F8) {
+    const uint32_t flip = a.negate_q ? 0x80808080u : 0u;
+    const u32x4* src = (const u32x4*)(Q8h + (size_t)min(qrow, nq - 1) * D);
+#pragma unroll
+    for (int s = 0; s < D / 64; ++s) {
+      u32x4 w0 = src[4 * s + g], w1 = src[4 * s + 2 + g];
+      if (qrow >= nq) w0 = w1 = u32x4{0, 0, 0, 0};
+      w0 ^= flip;
+      w1 ^= flip;
+      qop[s] = i32x8{(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3],
+                     (int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
+    }
+  } else {
     const uint32_t flip = a.negate_q ? 0x80008000u : 0u;
     const u32x4* src = (const u32x4*)(Qh + (size_t)min(qrow, nq - 1) * qstride);
 #pragma unroll
@@ -329,13 +396,23 @@ void prefill_kernel(PrefillParams a) {
 
   // --- lane-constant LDS offsets (within a stage)
   int koff[D / 16];  // K operand: row swap23(lane%32), logical chunk 2*st + g
-  {
+  if constexpr (F8) {
+    // E4M3 K: step st (64 dims) reads logical chunks 4*st + g and 4*st + 2 + g
+    const int R = swap_bits_2_3(lane & 31);
+    const int sw = chunk_swizzle_f8<D>(R);
+#pragma unroll
+    for (int st = 0; st < D / 64; ++st)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) koff[2 * st + h] = R * D + (((4 * st + 2 * h + g) ^ sw) << 4);
+  } else {
     const int R = swap_bits_2_3(lane & 31);
     const int sw = chunk_swizzle<D>(R);
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) koff[st] = R * S::ROWB + (((2 * st + g) ^ sw) << 4);
   }
-  int voff[D / 32][2];  // V^T operand via transposing reads: rows 8g + 4h + (i16>>2)
+  // V^T operand via transposing reads: rows 8g + 4h + (i16>>2), relative to the stage
+  // (F8: to the widened tile)
+  int voff[D / 32][2];
   {
     const int i16 = lane & 15, q4 = lane >> 4;
 #pragma unroll
@@ -345,7 +422,7 @@ void prefill_kernel(PrefillParams a) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const int c = 4 * db + 2 * (q4 & 1) + ((i16 & 3) >> 1);
-        voff[db][h] = S::TILE + R * S::ROWB + ((c ^ sw) << 4) + ((i16 & 1) << 3);
+        voff[db][h] = (F8 ? 0 : S::TILE) + R * S::ROWB + ((c ^ sw) << 4) + ((i16 & 1) << 3);
       }
     }
   }
@@ -368,22 +445,57 @@ void prefill_kernel(PrefillParams a) {
   // ahead as one stream across both parts; the first kLead P.V operands are read during
   // the preceding softmax slot, so the matrix core starts on arrival.
   constexpr int NPV = 4 * (D / 32);  // P.V MFMAs per tile: 16-key steps x 32-dim blocks
-  constexpr int NQK = 2 * (D / 16);  // Q.K^T MFMAs per tile: 16-dim steps x key halves
+  // Q.K^T operand reads per tile: 16-dim steps x key halves, one read per MFMA; F8: 64-dim
+  // steps x key halves x the two 16-byte reads of one MFMA operand
+  constexpr int NQK = F8 ? D / 16 : 2 * (D / 16);
   constexpr int kLead = 6;
   bf16x8 pre[kLead];
 #pragma unroll
   for (int i = 0; i < kLead; ++i) pre[i] = bf16x8{};
   auto stage = [&](int j) -> const char* { return smem + (j & (S::STAGES - 1)) * S::STAGE; };
+  // where the P.V reads of tile j find V: its ring stage, or (F8) its widened buffer
+  auto vstage = [&](int j) -> const char* {
+    if constexpr (F8) return smem + S::RING + (j & 1) * S::VTILE;
+    else return stage(j);
+  };
   auto pv_operand = [&](const char* st, int m) -> bf16x8 {
     const int t4 = m / (D / 32), db = m % (D / 32);
     return concat(lds_read_tr(st + voff[db][0] + t4 * 16 * S::ROWB),
                   lds_read_tr(st + voff[db][1] + t4 * 16 * S::ROWB));
   };
   auto qk_operand = [&](const char* st, int m) -> bf16x8 {
-    return lds_read_b128(st + koff[m >> 1] + (m & 1) * 32 * S::ROWB);
+    if constexpr (F8) {
+      // read m: MFMA t = m/2 (key half t%2, step t/2), 16-byte half m%2
+      const int t = m >> 1;
+      return lds_read_b128(st + koff[2 * (t >> 1) + (m & 1)] + (t & 1) * 32 * D);
+    } else {
+      return lds_read_b128(st + koff[m >> 1] + (m & 1) * 32 * S::ROWB);
+    }
+  };
+  // F8: widen V tile j (E4M3 in its ring stage, rows in byte order) into its bf16 buffer in
+  // the layout the transposing P.V reads expect.  All 512 threads, D/8 codes each.
+  auto widen = [&](int j) {
+    if constexpr (F8) {
+      const char* src = stage(j) + S::TILE;
+      char* dst = smem + S::RING + (j & 1) * S::VTILE;
+      const int R = tid >> 3, c = tid & 7;
+      const int sw = chunk_swizzle<D>(R);
+      if constexpr (D == 128) {
+        const u32x4 w = *(const u32x4*)(src + tid * 16);
+        const u32x2 e0 = e4m3x4_to_bf16x4(w[0]), e1 = e4m3x4_to_bf16x4(w[1]);
+        const u32x2 e2 = e4m3x4_to_bf16x4(w[2]), e3 = e4m3x4_to_bf16x4(w[3]);
+        *(u32x4*)(dst + R * S::ROWB + (((2 * c) ^ sw) << 4)) = u32x4{e0[0], e0[1], e1[0], e1[1]};
+        *(u32x4*)(dst + R * S::ROWB + (((2 * c + 1) ^ sw) << 4)) =
+            u32x4{e2[0], e2[1], e3[0], e3[1]};
+      } else {
+        const u32x2 w = *(const u32x2*)(src + tid * 8);
+        const u32x2 e0 = e4m3x4_to_bf16x4(w[0]), e1 = e4m3x4_to_bf16x4(w[1]);
+        *(u32x4*)(dst + R * S::ROWB + ((c ^ sw) << 4)) = u32x4{e0[0], e0[1], e1[0], e1[1]};
+      }
+    }
   };
   auto prefetch_pv = [&](int j) {
-    const char* st = stage(j);
+    const char* st = vstage(j);
 #pragma unroll
     for (int i = 0; i < kLead; ++i) pre[i] = pv_operand(st, i);
   };
@@ -392,7 +504,7 @@ void prefill_kernel(PrefillParams a) {
     constexpr bool DO_QK = decltype(qk_tag)::value;
     constexpr int P0 = DO_PV ? NPV : 0;
     constexpr int M = P0 + (DO_QK ? NQK : 0);
-    const char* sv = stage(jpv);
+    const char* sv = vstage(jpv);
     const char* sk = stage(jqk);
     auto load = [&](int m) -> bf16x8 {
       if (m < P0) return pv_operand(sv, m);
@@ -410,6 +522,16 @@ void prefill_kernel(PrefillParams a) {
         const u32x4 pw = {pk[t4 >> 1][4 * (t4 & 1) + 0], pk[t4 >> 1][4 * (t4 & 1) + 1],
                           pk[t4 >> 1][4 * (t4 & 1) + 2], pk[t4 >> 1][4 * (t4 & 1) + 3]};
         oacc[db] = E::mfma32(ops[m], __builtin_bit_cast(bf16x8, pw), oacc[db]);
+      } else if constexpr (F8) {
+        const int q = m - P0;
+        if (q & 1) {
+          const int t = q >> 1;
+          const i32x8 kop = __builtin_bit_cast(
+              i32x8, __builtin_shufflevector(ops[m - 1], ops[m], 0, 1, 2, 3, 4, 5, 6, 7, 8, 9,
+                                             10, 11, 12, 13, 14, 15));
+          if (t & 1) s1 = E::mfma_qk(kop, qop[t >> 1], s1);
+          else s0 = E::mfma_qk(kop, qop[t >> 1], s0);
+        }
       } else {
         const int q = m - P0;
         if (q & 1) s1 = E::mfma32(ops[m], qop[q >> 1], s1);
@@ -421,7 +543,8 @@ void prefill_kernel(PrefillParams a) {
     if (!DO_PV) __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      // (F8: a Q.K^T MFMA follows every second read)
+      if (!F8 || m < P0 || ((m - P0) & 1)) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       const int n = m + kLead;
       if (n < P0) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       else if (n < M) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
@@ -489,7 +612,8 @@ void prefill_kernel(PrefillParams a) {
   };
 
   // Slot bookkeeping shared by both groups.  Slot 2j: tile j+2 is prefetched into the
-  // stage tile j-2 used.  End of slot 2j+1: tile j+1 must be resident.
+  // stage tile j-2 used (F8: and V tile j is widened).  End of slot 2j+1: tile j+1 must be
+  // resident.
   auto slot_begin = [&](int s) {
     if ((s & 1) == 0 && (s >> 1) + 2 < ntiles) issue_tile((s >> 1) + 2);
   };
@@ -498,6 +622,8 @@ void prefill_kernel(PrefillParams a) {
       const int jw = (s + 1) >> 1;
       if (jw + 1 < ntiles) wait_vmcnt<S::LOADS_PER_TILE>();
       else wait_vmcnt<0>();
+    } else if constexpr (F8) {
+      wait_lgkmcnt0();  // the widened V is in LDS before any wave reads it
     }
     block_barrier();
   };
@@ -523,6 +649,7 @@ void prefill_kernel(PrefillParams a) {
   const int j1 = max(1, min(jm, n));  // softmax of tiles [1, j1) needs no mask
   if (grp == 0) {
     slot_begin(0);
+    widen(0);
     mfma_slot(0, 0, no, yes);
     slot_end(0);
     slot_begin(1);
@@ -531,6 +658,7 @@ void prefill_kernel(PrefillParams a) {
     slot_end(1);
     auto iter = [&](int j, auto mask_tag) {
       slot_begin(2 * j);
+      widen(j);
       mfma_slot(j - 1, j, yes, yes);
       slot_end(2 * j);
       slot_begin(2 * j + 1);
@@ -547,6 +675,7 @@ void prefill_kernel(PrefillParams a) {
     slot_end(2 * n + 1);
   } else {
     slot_begin(0);
+    widen(0);
     slot_end(0);
     slot_begin(1);
     mfma_slot(0, 0, no, yes);
@@ -554,6 +683,7 @@ void prefill_kernel(PrefillParams a) {
     // iteration j runs the softmax of tile j-1: masked for tile 0 and tiles >= j1
     auto iter = [&](int j, auto mask_tag) {
       slot_begin(2 * j);
+      widen(j);
       prefetch_pv(j - 1);
       softmax(j - 1, mask_tag);
       slot_end(2 * j);
@@ -576,7 +706,7 @@ void prefill_kernel(PrefillParams a) {
   // --- epilogue: O = acc / l -> bf16; LSE = m*scale + ln l
   const float l_tot = l_ex + wave_xor(l_ex, 32);
   if (qrow < nq) {
-    const float inv = 1.f / l_tot;
+    const float inv = (F8 ? a.v_scale : 1.f) / l_tot;
     uint16_t* orow = VARLEN ? a.o + ((size_t)(q_start + qrow) * a.Hq + hq) * D
                             : a.o + ((size_t)(b * a.Hq + hq) * a.Nq + qrow) * D;
 #pragma unroll
@@ -608,6 +738,13 @@ static hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, bool CAUSAL>
+static hipError_t launch_f8(const PrefillParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, false, false, ElemFp8>), dim3(p.total_wg),
+                     dim3(512), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <typename E>
 static hipError_t launch_e(const PrefillParams& p, int d, int causal, hipStream_t stream) {
   if (d == 64)
@@ -628,9 +765,13 @@ hipError_t launch_prefill(PrefillParams p, int d, int causal, hipStream_t stream
   {
     const int BH = p.B * p.Hq;
     const int nh = (BH % 8 == 0) ? BH / 8 : BH;
-    const double kv_bytes = 2.0 * p.Nk * d * 2.0;
+    const double kv_bytes = 2.0 * p.Nk * d * (p.fp8 ? 1.0 : 2.0);
     int hg = (int)((4.0 * 1024 * 1024) / kv_bytes);
     p.head_group = hg < 1 ? 1 : (hg > nh ? nh : hg);
+  }
+  if (p.fp8) {
+    if (d == 64) return causal ? launch_f8<64, true>(p, stream) : launch_f8<64, false>(p, stream);
+    return causal ? launch_f8<128, true>(p, stream) : launch_f8<128, false>(p, stream);
   }
   return p.f16 ? launch_e<ElemF16>(p, d, causal, stream) : launch_e<ElemBf16>(p, d, causal, stream);
 }

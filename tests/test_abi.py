@@ -31,6 +31,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["attn_fwd_prefill", "attn_fwd_prefill_paged",
                                            "attn_fwd_prefill_f16", "attn_fwd_prefill_paged_f16",
+                                           "attn_fwd_prefill_fp8",
                                            "attn_fwd_decode", "attn_fwd_decode_f16",
                                            "attn_fwd_decode_fp8", "attn_bwd", "attn_bwd_f16",
                                            "attn_fwd_prefill_varlen",
@@ -159,6 +160,33 @@ def test_f16_entry_points_validate_like_bf16(lib, kw, status):
                                     a["Hkv"], a["Nq"], a["Nk"], a["d"], a["causal"],
                                     ctypes.c_float(a["scale"]), None) == status
     assert prefill(lib, **kw) == status
+
+
+def prefill_fp8(lib, q_scale=0.02, k_scale=0.03, v_scale=0.04, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, Hq=2, Hkv=1, Nq=4, Nk=4, d=64, causal=1,
+             scale=0.125)
+    a.update(kw)
+    return lib.attn_fwd_prefill_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
+                                    a["Hkv"], a["Nq"], a["Nk"], a["d"], a["causal"],
+                                    ctypes.c_float(a["scale"]), ctypes.c_float(q_scale),
+                                    ctypes.c_float(k_scale), ctypes.c_float(v_scale), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_scale=0.0), INVALID), (dict(q_scale=-0.5), INVALID),
+    (dict(k_scale=0.0), INVALID), (dict(v_scale=-1.0), INVALID),
+    (dict(q_scale=float("nan")), INVALID), (dict(k_scale=float("inf")), INVALID),
+    (dict(v_scale=float("inf")), INVALID),
+    (dict(scale=1e20, q_scale=1e20, k_scale=1e10), INVALID),   # the product overflows
+    # every check of attn_fwd_prefill applies as well
+    (dict(q=None), INVALID), (dict(v=MIS), INVALID), (dict(B=0), INVALID),
+    (dict(Hq=3, Hkv=2), INVALID), (dict(Nq=5, Nk=4, causal=1), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(d=96), UNSUPPORTED),
+    # one byte per element: one head's K may reach 2^31 - 1 bytes, not 2^31
+    (dict(Nq=4, Nk=1 << 24, d=128), UNSUPPORTED),
+])
+def test_prefill_fp8_validation(lib, kw, status):
+    assert prefill_fp8(lib, **kw) == status
 
 
 def test_f16_paged_and_decode_validate_like_bf16(lib):
