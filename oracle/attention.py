@@ -348,6 +348,21 @@ def attention_prefill_paged(q: np.ndarray, kpool: np.ndarray, vpool: np.ndarray,
 # ---------------------------------------------------------------------------
 # Combining partial results over disjoint key sets
 # ---------------------------------------------------------------------------
+def attention_prefill_paged_fp8(qcodes: np.ndarray, kpool: np.ndarray, vpool: np.ndarray,
+                                block_table: np.ndarray, kv_lens: np.ndarray, scale: float,
+                                q_scale: float, k_scale: float, v_scale: float, causal: bool,
+                                page_size: int = 16):
+    """Chunked prefill (attention_prefill_paged) over FP8 inputs: the queries and the paged
+    pools hold E4M3 codes with one scale per tensor, read as in attention_prefill_fp8 (the
+    pools as the FP8 cache of attention_decode_fp8).  Only the live rows a sequence
+    gathers reach the arithmetic, so codes in unused slots never matter.
+    Returns O [B,Hq,Nq,d], LSE [B,Hq,Nq] (float64)."""
+    Q = q_scale * e4m3_value(qcodes)
+    K = k_scale * e4m3_value(kpool)
+    V = v_scale * e4m3_value(vpool)
+    return attention_prefill_paged(Q, K, V, block_table, kv_lens, scale, causal, page_size)
+
+
 def merge_partials(o_parts: np.ndarray, lse_parts: np.ndarray):
     """Combine attention results computed over disjoint key subsets of one row.
 

@@ -572,6 +572,53 @@ def test_fp8_prefill_negated_query_codes_equal_a_negated_scale():
     np.testing.assert_allclose(l0, l1, rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_paged_prefill_equals_dense_fp8_prefill_of_each_sequence(causal):
+    # the chunk's queries against each sequence's gathered context (NaN codes in every
+    # unused slot) equal the dense FP8 prefill over that context
+    from oracle import attention_prefill_fp8, attention_prefill_paged_fp8
+    rng = np.random.default_rng(91)
+    codes = [c for c in range(256) if c & 0x7F != 0x7F]
+    lens = np.array([7, 3, 13], np.int32)
+    Nq = 3
+    qc = rng.choice(codes, (3, 4, Nq, 5)).astype(np.uint8)
+    kc = rng.choice(codes, (3, 2, 13, 5)).astype(np.uint8)
+    vc = rng.choice(codes, (3, 2, 13, 5)).astype(np.uint8)
+    kp, table = _to_paged(kc, lens, 4, 11)
+    vp, _ = _to_paged(vc, lens, 4, 11)
+    o, lse = attention_prefill_paged_fp8(qc, kp, vp, table, lens, 0.4, 0.02, 0.03, 0.05, causal,
+                                         page_size=4)
+    assert np.isfinite(o).all()
+    for b, n in enumerate(lens):
+        od, ld = attention_prefill_fp8(qc[b:b + 1], kc[b:b + 1, :, :n], vc[b:b + 1, :, :n], 0.4,
+                                       0.02, 0.03, 0.05, causal)
+        np.testing.assert_allclose(o[b], od[0], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lse[b], ld[0], rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_paged_prefill_matches_brute_force_on_torch_dequantised_inputs():
+    import torch
+    from oracle import attention_prefill_paged_fp8
+    rng = np.random.default_rng(92)
+    codes = [c for c in range(256) if c & 0x7F != 0x7F]
+    lens = np.array([6, 9], np.int32)
+    qc = rng.choice(codes, (2, 2, 4, 3)).astype(np.uint8)
+    kc = rng.choice(codes, (2, 1, 9, 3)).astype(np.uint8)
+    vc = rng.choice(codes, (2, 1, 9, 3)).astype(np.uint8)
+    kp, table = _to_paged(kc, lens, 4, 12)
+    vp, _ = _to_paged(vc, lens, 4, 12)
+    o, lse = attention_prefill_paged_fp8(qc, kp, vp, table, lens, 0.3, 0.011, 0.017, 0.029, True,
+                                         page_size=4)
+    deq = lambda c: torch.from_numpy(c).view(torch.float8_e4m3fn).double().numpy()
+    for b, n in enumerate(lens):
+        for h in range(2):
+            bo, bl = brute_force_attention((0.011 * deq(qc[b, h])).tolist(),
+                                           (0.017 * deq(kc[b, 0, :n])).tolist(),
+                                           (0.029 * deq(vc[b, 0, :n])).tolist(), 0.3, True)
+            np.testing.assert_allclose(o[b, h], np.array(bo), rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(lse[b, h], np.array(bl), rtol=1e-12, atol=1e-12)
+
+
 # ----------------------------------------------------------------------------- backward
 def _bwd_case(seed, B=1, Hq=2, Hkv=1, Nq=5, Nk=7, d=3):
     rng = np.random.default_rng(seed)
