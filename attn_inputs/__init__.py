@@ -213,6 +213,10 @@ CONFIGS = {
     "chunked_prefill_paged": DecodeCfg("chunked_prefill_paged", B=8, Hq=32, Hkv=8, d=128,
                                        seed=6, paged=True, page_size=16,
                                        len_range=(2048, 16384), chunk=512),
+    # The same chunked prefill over FP8 queries and an FP8 paged cache.
+    "chunked_prefill_paged_fp8": DecodeCfg("chunked_prefill_paged_fp8", B=8, Hq=32, Hkv=8,
+                                           d=128, seed=6, paged=True, page_size=16,
+                                           len_range=(2048, 16384), chunk=512, kv_fp8=True),
 }
 
 
@@ -466,11 +470,15 @@ def varlen_flops(lens_q, lens_k, Hq: int, d: int, causal: bool) -> int:
 
 
 def chunk_q(cfg: DecodeCfg) -> np.ndarray:
-    """Chunked-prefill queries [B, Hq, chunk, d] bf16 bits."""
-    q = np.empty((cfg.B, cfg.Hq, cfg.chunk, cfg.d), np.uint16)
+    """Chunked-prefill queries [B, Hq, chunk, d] bf16 bits (with an FP8 cache: E4M3 codes
+    of the same draws over FP8_Q_SCALE)."""
+    q = np.empty((cfg.B, cfg.Hq, cfg.chunk, cfg.d), np.uint8 if cfg.kv_fp8 else np.uint16)
     for b in range(cfg.B):
         for h in range(cfg.Hq):
-            q[b, h] = normal_bf16(cfg.seed, T_Q, b, h, (cfg.chunk, cfg.d), f16=cfg.f16)
+            if cfg.kv_fp8:
+                q[b, h] = normal_e4m3(cfg.seed, T_Q, b, h, (cfg.chunk, cfg.d), FP8_Q_SCALE)
+            else:
+                q[b, h] = normal_bf16(cfg.seed, T_Q, b, h, (cfg.chunk, cfg.d), f16=cfg.f16)
     return q
 
 

@@ -490,6 +490,27 @@ def main():
                                           "TFLOP/s": round(tf, 2),
                                           "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                                           "chunk": cfg.chunk, "kv_lens": [int(x) for x in plens]}
+        bf16_chunk_us = avg
+        del pq, pkc, pvc, po, pl
+        torch.cuda.empty_cache()
+        # the same chunked prefill over FP8 queries and an FP8 paged cache
+        cfg = ai.CONFIGS["chunked_prefill_paged_fp8"]
+        u8 = lambda c: torch.from_numpy(np.ascontiguousarray(c)).cuda()
+        pq = u8(ai.chunk_q(cfg))
+        pkc = u8(ai.build_paged_cache(cfg, ai.T_K, plens, lay, pad_bits=np.uint8(0)))
+        pvc = u8(ai.build_paged_cache(cfg, ai.T_V, plens, lay, pad_bits=np.uint8(0)))
+        po = torch.empty(pq.shape, dtype=torch.bfloat16, device="cuda")
+        pl = torch.empty(pq.shape[:3], dtype=torch.float32, device="cuda")
+        avg, med, mn = time_kernel(
+            lambda: mi.attn_fwd_prefill_paged_fp8(pq, pkc, pvc, ptab, plen_d, po, pl, pmax, True,
+                                                  cfg.scale, ai.FP8_Q_SCALE, ai.FP8_K_SCALE,
+                                                  ai.FP8_V_SCALE, stream=stream),
+            args.steps, args.warmup)
+        tf = ai.chunk_prefill_flops(cfg, plens) / (avg * 1e-6) / 1e12
+        extra["chunked_prefill_paged_fp8"] = {"us": round(avg, 2), "us_min": round(mn, 2),
+                                              "TFLOP/s": round(tf, 2),
+                                              "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                                              "speedup_vs_bf16": round(bf16_chunk_us / avg, 3)}
         out["other_workloads"] = extra
 
     if args.copy_mib > 0:

@@ -143,6 +143,30 @@ int attn_fwd_prefill_paged(const void* q, const void* kcache, const void* vcache
                            int page_size, int max_blocks_per_seq, int num_pages, int causal,
                            float scale, hipStream_t stream);
 
+/*
+ * Chunked prefill against an FP8 paged cache: attn_fwd_prefill_paged with the caches in
+ * the E4M3 format and per-tensor scales of attn_fwd_decode_fp8 (the cache that FP8 decode
+ * reads) and the queries as E4M3 codes with their own scale, computed as
+ * attn_fwd_prefill_fp8 computes (Q K^T on the FP8 matrix cores, V widened to bf16, bf16
+ * P and o).
+ *
+ *   q      [B, Hq, Nq, d] uint8 codes, 16-byte aligned
+ *   kcache, vcache [num_pages, Hkv, 16, d] uint8 codes, 16-byte aligned
+ *   o      [B, Hq, Nq, d] bf16 (written)
+ *   q_scale, k_scale, v_scale  finite and > 0.
+ *   All other arguments, the table and length contracts and the outputs are those of
+ *   attn_fwd_prefill_paged.
+ *
+ * Errors: those of attn_fwd_prefill_paged, plus INVALID_ARGUMENT for a non-finite or
+ * non-positive scale, or when |scale| * q_scale * k_scale overflows float.
+ */
+int attn_fwd_prefill_paged_fp8(const void* q, const void* kcache, const void* vcache,
+                               const int32_t* block_table, const int32_t* kv_lens, void* o,
+                               float* lse, int B, int Hq, int Hkv, int Nq, int d, int max_kv_len,
+                               int page_size, int max_blocks_per_seq, int num_pages, int causal,
+                               float scale, float q_scale, float k_scale, float v_scale,
+                               hipStream_t stream);
+
 /* attn_fwd_prefill_paged with fp16 q, caches and o (as in attn_fwd_prefill_f16). */
 int attn_fwd_prefill_paged_f16(const void* q, const void* kcache, const void* vcache,
                                const int32_t* block_table, const int32_t* kv_lens, void* o,

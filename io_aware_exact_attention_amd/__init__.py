@@ -60,6 +60,8 @@ def load_library():
     lib.attn_fwd_prefill_paged.restype = i32
     lib.attn_fwd_prefill_paged_f16.argtypes = lib.attn_fwd_prefill_paged.argtypes
     lib.attn_fwd_prefill_paged_f16.restype = i32
+    lib.attn_fwd_prefill_paged_fp8.argtypes = [vp] * 7 + [i32] * 10 + [f32] * 4 + [vp]
+    lib.attn_fwd_prefill_paged_fp8.restype = i32
     lib.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                     i32, f32, i32, vp, ctypes.c_size_t, vp]
     lib.attn_fwd_decode.restype = i32
@@ -183,13 +185,13 @@ def prefill(q, k, v, causal: bool = True, scale: float | None = None):
 
 
 def _prefill_paged_call(fn, dtype, q, kcache, vcache, block_table, kv_lens, o, lse, max_kv_len,
-                        causal, scale, page_size, num_pages, stream):
+                        causal, scale, page_size, num_pages, stream, fp8_scales=None):
     lib = load_library()
     _check(q, "q", dtype, 4)
     dev = q.device
     _check(kcache, "kcache", dtype, 4, dev)
     _check(vcache, "vcache", dtype, 4, dev)
-    _check(o, "o", dtype, 4, dev)
+    _check(o, "o", torch.bfloat16 if fp8_scales else dtype, 4, dev)
     _check(block_table, "block_table", torch.int32, 2, dev)
     _check(kv_lens, "kv_lens", torch.int32, 1, dev)
     B, Hq, Nq, d = q.shape
@@ -209,9 +211,22 @@ def _prefill_paged_call(fn, dtype, q, kcache, vcache, block_table, kv_lens, o, l
                           _ptr(kv_lens), _ptr(o), _ptr(lse), B, Hq, kcache.shape[1], Nq,
                           d, int(max_kv_len), int(page_size), int(block_table.shape[1]),
                           int(num_pages), 1 if causal else 0, float(scale),
+                          *([float(x) for x in fp8_scales] if fp8_scales else []),
                           _stream_handle(stream))
     if st != ATTN_OK:
         raise AttnError(st, fn)
+
+
+def attn_fwd_prefill_paged_fp8(q, kcache, vcache, block_table, kv_lens, o, lse, max_kv_len: int,
+                               causal: bool, scale: float, q_scale: float, k_scale: float,
+                               v_scale: float, page_size: int = 16, num_pages: int | None = None,
+                               stream=None) -> None:
+    """attn_fwd_prefill_paged over FP8 inputs: q and the caches hold OCP E4M3 codes
+    (torch.uint8 or torch.float8_e4m3fn) standing for q_scale * e4m3(code) (k_scale,
+    v_scale); o is bf16."""
+    _prefill_paged_call("attn_fwd_prefill_paged_fp8", (torch.uint8, torch.float8_e4m3fn), q,
+                        kcache, vcache, block_table, kv_lens, o, lse, max_kv_len, causal, scale,
+                        page_size, num_pages, stream, (q_scale, k_scale, v_scale))
 
 
 def attn_fwd_prefill_paged(q, kcache, vcache, block_table, kv_lens, o, lse, max_kv_len: int,
@@ -509,7 +524,7 @@ __all__ = ["attn_bwd", "attn_bwd_f16", "attn_bwd_workspace_bytes", "backward", "
            "attn_fwd_prefill_varlen_f16",
            "prefill_varlen",
            "attn_fwd_prefill", "attn_fwd_prefill_f16", "attn_fwd_prefill_fp8", "prefill_fp8",
-           "attn_fwd_prefill_paged_f16",
+           "attn_fwd_prefill_paged_f16", "attn_fwd_prefill_paged_fp8",
            "attn_fwd_decode", "attn_fwd_decode_f16", "attn_fwd_decode_fp8",
            "attn_decode_workspace_bytes", "decode_fp8",
            "attn_decode_num_splits", "attn_status_string", "prefill", "decode",

@@ -172,7 +172,8 @@ int prefill_paged_impl(const void* q, const void* kcache, const void* vcache,
                        const int32_t* block_table, const int32_t* kv_lens, void* o, float* lse,
                        int B, int Hq, int Hkv, int Nq, int d, int max_kv_len, int page_size,
                        int max_blocks_per_seq, int num_pages, int causal, float scale, bool f16,
-                       hipStream_t stream) {
+                       hipStream_t stream, bool fp8 = false, float q_scale = 1.f,
+                       float k_scale = 1.f, float v_scale = 1.f) {
   if (!q || !kcache || !vcache || !block_table || !kv_lens || !o) return ATTN_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16) || !aligned(kcache, 16) || !aligned(vcache, 16) || !aligned(o, 16) ||
       !aligned(block_table, 4) || !aligned(kv_lens, 4))
@@ -183,6 +184,9 @@ int prefill_paged_impl(const void* q, const void* kcache, const void* vcache,
   if (Hq % Hkv || Nq > max_kv_len || !std::isfinite(scale)) return ATTN_ERR_INVALID_ARGUMENT;
   if (page_size != 16) return ATTN_ERR_UNSUPPORTED;
   if (max_blocks_per_seq < (max_kv_len + 15) / 16) return ATTN_ERR_INVALID_ARGUMENT;
+  if (fp8 && !(std::isfinite(q_scale) && q_scale > 0.f && std::isfinite(k_scale) &&
+               k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+    return ATTN_ERR_INVALID_ARGUMENT;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   const long qtiles = (Nq + 127) / 128;
   if (qtiles * (long)Hq * B > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
@@ -201,6 +205,10 @@ int prefill_paged_impl(const void* q, const void* kcache, const void* vcache,
   p.max_blocks = max_blocks_per_seq;
   p.page_max = (uint32_t)(num_pages - 1);
   p.f16 = f16;
+  if (fp8) p.c *= q_scale * k_scale;
+  if (!std::isfinite(p.c)) return ATTN_ERR_INVALID_ARGUMENT;
+  p.fp8 = fp8;
+  p.v_scale = v_scale;
   (void)hipGetLastError();
   return miattn::launch_prefill(p, d, causal ? 1 : 0, stream) == hipSuccess ? ATTN_OK
                                                                              : ATTN_ERR_HIP;
@@ -330,6 +338,17 @@ int attn_fwd_prefill_paged(const void* q, const void* kcache, const void* vcache
   return prefill_paged_impl(q, kcache, vcache, block_table, kv_lens, o, lse, B, Hq, Hkv, Nq, d,
                             max_kv_len, page_size, max_blocks_per_seq, num_pages, causal, scale,
                             false, stream);
+}
+
+int attn_fwd_prefill_paged_fp8(const void* q, const void* kcache, const void* vcache,
+                               const int32_t* block_table, const int32_t* kv_lens, void* o,
+                               float* lse, int B, int Hq, int Hkv, int Nq, int d, int max_kv_len,
+                               int page_size, int max_blocks_per_seq, int num_pages, int causal,
+                               float scale, float q_scale, float k_scale, float v_scale,
+                               hipStream_t stream) {
+  return prefill_paged_impl(q, kcache, vcache, block_table, kv_lens, o, lse, B, Hq, Hkv, Nq, d,
+                            max_kv_len, page_size, max_blocks_per_seq, num_pages, causal, scale,
+                            false, stream, true, q_scale, k_scale, v_scale);
 }
 
 int attn_fwd_prefill_paged_f16(const void* q, const void* kcache, const void* vcache,

@@ -164,13 +164,13 @@ __device__ __forceinline__ PagedItem paged_work_item(int p, int B, int Hq, int n
 // Layouts: dense [B, H, N, D] (PAGED and VARLEN false); PAGED: K/V in the paged cache,
 // kv_lens per sequence; VARLEN: sequences packed along the token axis, [total, H, D], with
 // cumulative lengths cu_q, cu_k.
-// F8 (E = ElemFp8, dense layout only): Q, K, V are E4M3 codes; Q.K^T runs on the FP8
+// F8 (E = ElemFp8, dense or paged layout): Q, K, V are E4M3 codes; Q.K^T runs on the FP8
 // MFMA, V is widened to bf16 in LDS, and O is scaled by v_scale.
 template <int D, bool CAUSAL, bool PAGED, bool VARLEN, typename E>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillParams a) {
   constexpr bool F8 = E::kFp8;
-  static_assert(!(F8 && (PAGED || VARLEN)), "FP8 prefill takes the dense layout");
+  static_assert(!(F8 && VARLEN), "FP8 prefill takes the dense or the paged layout");
   using S = PrefillShape<D, F8>;
   __shared__ __attribute__((aligned(1024))) char smem[S::LDS];
 
@@ -230,10 +230,12 @@ void prefill_kernel(PrefillParams a) {
       PAGED ? a.v
             : (VARLEN ? a.v + ((size_t)k_start * a.Hkv + kvh) * D
                       : a.v + (size_t)(b * a.Hkv + kvh) * a.Nk * D);
-  // F8: the same dense tensors as one byte per element
+  // F8: the same tensors as one byte per element (paged: the pools)
   const uint8_t* __restrict__ Q8h = (const uint8_t*)a.q + (size_t)(b * a.Hq + hq) * a.Nq * D;
-  const uint8_t* __restrict__ K8h = (const uint8_t*)a.k + (size_t)(b * a.Hkv + kvh) * a.Nk * D;
-  const uint8_t* __restrict__ V8h = (const uint8_t*)a.v + (size_t)(b * a.Hkv + kvh) * a.Nk * D;
+  const uint8_t* __restrict__ K8h =
+      (const uint8_t*)a.k + (PAGED ? 0 : (size_t)(b * a.Hkv + kvh) * a.Nk * D);
+  const uint8_t* __restrict__ V8h =
+      (const uint8_t*)a.v + (PAGED ? 0 : (size_t)(b * a.Hkv + kvh) * a.Nk * D);
 
   // keys the workgroup needs: everything, or up to the diagonal of its last query
   int kend = nk;
@@ -289,16 +291,20 @@ void prefill_kernel(PrefillParams a) {
   // Paged cache [pages, Hkv, 16, D]: each 1 KB DMA block (RPB rows) lies inside one
   // 16-token page and gets its own descriptor.  The page ids of a tile's blocks are read
   // with scalar loads one tile ahead of its DMA.
-  constexpr int RPB = 1024 / S::ROWB;
+  // (F8: 1024 / D rows of E4M3 codes, block blk of a stage covering K rows when blk < NB8
+  // and V rows otherwise)
+  constexpr int RPB = F8 ? 1024 / D : 1024 / S::ROWB;
+  constexpr int NB8 = S::TILE / 1024;
   // The table is read through the constant address space: it does not change during the
   // kernel, and wave-uniform loads from there are scalar loads.
   typedef __attribute__((address_space(4))) const int32_t const_i32;
   const_i32* tbl = (const_i32*)(PAGED ? a.block_table + (size_t)b * a.max_blocks : nullptr);
-  int pg_next[S::DMA];
+  int pg_next[NOFF];
   auto fetch_pages = [&](int j) {
 #pragma unroll
-    for (int i = 0; i < S::DMA; ++i) {
-      const int tok0 = j * S::BN + (i * S::kWaves + wave) * RPB;
+    for (int i = 0; i < NOFF; ++i) {
+      const int blk = i * S::kWaves + wave;
+      const int tok0 = j * S::BN + (F8 ? blk % NB8 : blk) * RPB;
       // clamped into the pool: a bad table entry reads a wrong page, never memory outside
       pg_next[i] = tok0 < nk ? (int)min((uint32_t)tbl[tok0 >> 4], a.page_max) : 0;
     }
@@ -307,7 +313,22 @@ void prefill_kernel(PrefillParams a) {
   auto issue_tile = [&](int j) {
     const int n0 = j * S::BN;
     char* st = smem + (j & (S::STAGES - 1)) * S::STAGE;
-    if constexpr (F8) {
+    if constexpr (F8 && PAGED) {
+      int pg[NOFF];
+#pragma unroll
+      for (int i = 0; i < NOFF; ++i) pg[i] = pg_next[i];
+      fetch_pages(j + 1);
+#pragma unroll
+      for (int i = 0; i < NOFF; ++i) {
+        const int blk = i * S::kWaves + wave;
+        const int bi = blk % NB8;  // block index within its K or V tile
+        const int tok0 = n0 + bi * RPB;
+        const int nbytes = __builtin_amdgcn_readfirstlane(max(0, min(RPB, nk - tok0)) * D);
+        const size_t off = ((size_t)pg[i] * a.Hkv + kvh) * 16 * D + (size_t)(tok0 & 15) * D;
+        lds_dma16((blk < NB8 ? K8h : V8h) + off, nbytes, dma_off[i] - bi * 1024,
+                  (lds_void*)(st + blk * 1024));
+      }
+    } else if constexpr (F8) {
       const int nbytes = (nk - n0) * D;
       const uint8_t* kt = K8h + (size_t)n0 * D;
       const uint8_t* vt = V8h + (size_t)n0 * D;
@@ -740,8 +761,12 @@ static hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
 
 template <int D, bool CAUSAL>
 static hipError_t launch_f8(const PrefillParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, false, false, ElemFp8>), dim3(p.total_wg),
-                     dim3(512), 0, stream, p);
+  if (p.block_table)
+    hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, true, false, ElemFp8>), dim3(p.total_wg),
+                       dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, false, false, ElemFp8>), dim3(p.total_wg),
+                       dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["attn_fwd_prefill", "attn_fwd_prefill_paged",
                                            "attn_fwd_prefill_f16", "attn_fwd_prefill_paged_f16",
-                                           "attn_fwd_prefill_fp8",
+                                           "attn_fwd_prefill_fp8", "attn_fwd_prefill_paged_fp8",
                                            "attn_fwd_decode", "attn_fwd_decode_f16",
                                            "attn_fwd_decode_fp8", "attn_bwd", "attn_bwd_f16",
                                            "attn_fwd_prefill_varlen",
@@ -187,6 +187,22 @@ def prefill_fp8(lib, q_scale=0.02, k_scale=0.03, v_scale=0.04, **kw):
 ])
 def test_prefill_fp8_validation(lib, kw, status):
     assert prefill_fp8(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_scale=0.0), INVALID), (dict(k_scale=-1.0), INVALID), (dict(v_scale=float("nan")), INVALID),
+    (dict(scale=1e20, q_scale=1e20, k_scale=1e10), INVALID),
+    (dict(table=None), INVALID), (dict(page_size=32), UNSUPPORTED), (dict(max_blocks=6), INVALID),
+    (dict(d=80), UNSUPPORTED), (dict(Nq=101), INVALID), (dict(kc=MIS), INVALID)])
+def test_prefill_paged_fp8_validation(lib, kw, status):
+    a = dict(q=P, kc=P, vc=P, table=P, kv_lens=P, o=P, lse=None, B=2, Hq=8, Hkv=2, Nq=16, d=128,
+             max_kv=100, page_size=16, max_blocks=7, num_pages=10, causal=1, scale=0.1,
+             q_scale=0.02, k_scale=0.03, v_scale=0.04)
+    a.update(kw)
+    args = [a[n] for n in ("q", "kc", "vc", "table", "kv_lens", "o", "lse", "B", "Hq", "Hkv",
+                           "Nq", "d", "max_kv", "page_size", "max_blocks", "num_pages", "causal")]
+    args += [ctypes.c_float(a[n]) for n in ("scale", "q_scale", "k_scale", "v_scale")] + [None]
+    assert lib.attn_fwd_prefill_paged_fp8(*args) == status
 
 
 def test_f16_paged_and_decode_validate_like_bf16(lib):

@@ -162,6 +162,18 @@ def test_fp8_prefill_quantises_the_bf16_workload_draws():
     assert ai.prefill_flops(full) == ai.prefill_flops(ai.CONFIGS["llama2_7b_prefill"])
 
 
+def test_fp8_chunk_queries_quantise_the_bf16_chunk_draws():
+    base = ai.CONFIGS["chunked_prefill_paged"]
+    f8 = ai.CONFIGS["chunked_prefill_paged_fp8"]
+    np.testing.assert_array_equal(ai.decode_lengths(base), ai.decode_lengths(f8))
+    small = ai.DecodeCfg("t", B=2, Hq=2, Hkv=1, d=8, seed=13, paged=True, chunk=5, kv_fp8=True)
+    q = ai.chunk_q(small)
+    assert q.dtype == np.uint8 and q.shape == (2, 2, 5, 8)
+    x = np.random.default_rng(np.random.SeedSequence([13, ai.T_Q, 1, 0])).standard_normal(
+        (5, 8), dtype=np.float32)
+    np.testing.assert_array_equal(q[1, 0], _torch_e4m3(x / np.float32(ai.FP8_Q_SCALE)))
+
+
 # ----------------------------------------------------------------------------- fp16 rounding
 def test_f16_rounding_matches_torch():
     rng = np.random.default_rng(2)

@@ -18,7 +18,8 @@ import attn_inputs as ai
 import io_aware_exact_attention_amd as mi
 from oracle import (attention_backward, attention_decode, attention_decode_fp8,
                     attention_prefill, attention_prefill_fp8, attention_prefill_paged,
-                    attention_prefill_varlen, attention_rows, e4m3_value, gather_paged)
+                    attention_prefill_paged_fp8, attention_prefill_varlen, attention_rows,
+                    e4m3_value, gather_paged)
 
 pytestmark = pytest.mark.gpu
 
@@ -1150,6 +1151,99 @@ def test_prefill_fp8_llama2_shape():
     err, lerr = np.concatenate(errs), np.concatenate(lerrs)
     tol = fp8_lse_tol(q, k, cfg.scale, qs, ks)
     log_case("llama2_7b_prefill_fp8 (sampled)", max_abs=float(err.max()),
+             mean_abs=float(err.mean()), lse_max_abs=float(lerr.max()), n=int(err.size),
+             lse_tol=tol)
+    assert np.isfinite(go).all()
+    assert err.max() <= TOL_MAX and err.mean() <= TOL_MEAN and lerr.max() <= tol
+
+
+# ------------------------------------------------------------------ FP8 chunked prefill
+def make_chunk_fp8(B, Hq, Hkv, d, lens, Nq, seed, extra_pages=3):
+    """FP8 chunk queries plus an FP8 paged cache whose unused slots and pages hold the NaN
+    code."""
+    cfg = ai.DecodeCfg("chunk8", B=B, Hq=Hq, Hkv=Hkv, d=d, seed=seed, paged=True, chunk=Nq,
+                       kv_fp8=True)
+    lens = np.asarray(lens, np.int32)
+    lay = ai.paged_layout(lens, 16, seed, extra_pages=extra_pages)
+    return (cfg, ai.chunk_q(cfg), ai.build_paged_cache(cfg, ai.T_K, lens, lay),
+            ai.build_paged_cache(cfg, ai.T_V, lens, lay), lens, lay.block_table)
+
+
+def run_chunk_fp8(q, kc, vc, lens, table, causal, scale, qs=QS, ks=KS, vs=VS):
+    t = lambda c: torch.from_numpy(np.ascontiguousarray(c)).cuda()
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    mi.attn_fwd_prefill_paged_fp8(t(q), t(kc), t(vc), t(table), t(lens), o, lse, int(lens.max()),
+                                  causal, scale, qs, ks, vs)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def paged_fp8_lse_tol(q, kc, scale, qs=QS, ks=KS):
+    # the accumulation bound of fp8_lse_tol over every cached row (NaN codes excluded)
+    K = np.abs(ks * e4m3_value(kc))
+    K = np.where(np.isnan(K), 0.0, K).max(axis=(0, 2))           # [Hkv, d]
+    Q = np.abs(qs * e4m3_value(q)).max(axis=(0, 2))              # [Hq, d]
+    G = q.shape[1] // kc.shape[1]
+    maxprod = max(float((Q[h] * K[h // G]).max()) for h in range(q.shape[1]))
+    return TOL_LSE + (q.shape[3] // 64) * 2.0 ** -11 * abs(float(np.float32(scale))) * maxprod
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("Nq,lens", [(1, (1, 17, 300)), (77, (77, 200, 1000)),
+                                     (256, (256, 300, 1031)), (300, (300, 301, 700))])
+def test_prefill_paged_fp8_chunks(d, causal, Nq, lens):
+    cfg, q, kc, vc, lens, table = make_chunk_fp8(3, 4, 2, d, lens, Nq, seed=2400 + Nq + d)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    o, lse = run_chunk_fp8(q, kc, vc, lens, table, causal, scale)
+    ro, rl = attention_prefill_paged_fp8(q, kc, vc, table, lens, scale, QS, KS, VS, causal)
+    check(f"prefill_paged_fp8 d={d} causal={causal} Nq={Nq} "
+          f"lens={tuple(int(x) for x in lens)}", o, lse, ro, rl,
+          paged_fp8_lse_tol(q, kc, scale))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_paged_fp8_equals_dense_fp8_prefill(causal):
+    # every sequence as long as the chunk (self-attention over the chunk): the paged result
+    # equals the dense FP8 prefill of the same codes bit for bit
+    B, Hq, Hkv, d, N = 2, 4, 2, 128, 300
+    cfg, q, kc, vc, lens, table = make_chunk_fp8(B, Hq, Hkv, d, (N, N), N, seed=2450)
+    o, lse = run_chunk_fp8(q, kc, vc, lens, table, causal, 0.09)
+    kd = np.stack([np.stack([gather_paged(kc, table, b, h, N, 16) for h in range(Hkv)])
+                   for b in range(B)])
+    vd = np.stack([np.stack([gather_paged(vc, table, b, h, N, 16) for h in range(Hkv)])
+                   for b in range(B)])
+    od, ld = run_prefill_fp8(q, kd, vd, causal, 0.09, QS, KS, VS)
+    assert torch.equal(o, od) and torch.equal(lse, ld)
+
+
+def test_chunked_prefill_paged_fp8_config():
+    cfg = ai.CONFIGS["chunked_prefill_paged_fp8"]
+    lens = ai.decode_lengths(cfg)
+    q = ai.chunk_q(cfg)
+    lay = ai.paged_layout(lens, 16, cfg.seed)
+    kc = ai.build_paged_cache(cfg, ai.T_K, lens, lay)
+    vc = ai.build_paged_cache(cfg, ai.T_V, lens, lay)
+    o, lse = run_chunk_fp8(q, kc, vc, lens, lay.block_table, True, cfg.scale)
+    go = o.float().cpu().numpy().astype(np.float64)
+    gl = lse.float().cpu().numpy().astype(np.float64)
+    G = cfg.Hq // cfg.Hkv
+    errs, lerrs = [], []
+    for b in range(cfg.B):  # one query head per sequence, every row of it
+        h = (5 * b + 3) % cfg.Hq
+        kvh = h // G
+        n = int(lens[b])
+        K = KS * e4m3_value(gather_paged(kc, lay.block_table, b, kvh, n, 16))
+        V = VS * e4m3_value(gather_paged(vc, lay.block_table, b, kvh, n, 16))
+        rows = np.arange(cfg.chunk)
+        ro, rl = attention_rows(QS * e4m3_value(q[b, h]), K, V, cfg.scale, True, rows,
+                                cfg.chunk)
+        errs.append(np.abs(go[b, h] - ro))
+        lerrs.append(np.abs(gl[b, h] - rl))
+    err, lerr = np.concatenate([e.ravel() for e in errs]), np.concatenate(lerrs)
+    tol = paged_fp8_lse_tol(q, kc, cfg.scale)
+    log_case("chunked_prefill_paged_fp8 (sampled)", max_abs=float(err.max()),
              mean_abs=float(err.mean()), lse_max_abs=float(lerr.max()), n=int(err.size),
              lse_tol=tol)
     assert np.isfinite(go).all()
