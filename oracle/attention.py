@@ -363,6 +363,16 @@ def attention_prefill_paged_fp8(qcodes: np.ndarray, kpool: np.ndarray, vpool: np
     return attention_prefill_paged(Q, K, V, block_table, kv_lens, scale, causal, page_size)
 
 
+def attention_prefill_varlen_fp8(qcodes: np.ndarray, kcodes: np.ndarray, vcodes: np.ndarray,
+                                 cu_q: np.ndarray, cu_k: np.ndarray, scale: float,
+                                 q_scale: float, k_scale: float, v_scale: float, causal: bool):
+    """Ragged batch (attention_prefill_varlen) over FP8 inputs: the packed tensors hold E4M3
+    codes with one scale per tensor, read as in attention_prefill_fp8.
+    Returns O [total_q, Hq, d], LSE [Hq, total_q] (float64)."""
+    return attention_prefill_varlen(q_scale * e4m3_value(qcodes), k_scale * e4m3_value(kcodes),
+                                    v_scale * e4m3_value(vcodes), cu_q, cu_k, scale, causal)
+
+
 def merge_partials(o_parts: np.ndarray, lse_parts: np.ndarray):
     """Combine attention results computed over disjoint key subsets of one row.
 

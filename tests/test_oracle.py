@@ -619,6 +619,28 @@ def test_fp8_paged_prefill_matches_brute_force_on_torch_dequantised_inputs():
             np.testing.assert_allclose(lse[b, h], np.array(bl), rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_varlen_prefill_equals_dense_fp8_prefill_of_each_sequence(causal):
+    from oracle import attention_prefill_fp8, attention_prefill_varlen_fp8
+    rng = np.random.default_rng(93)
+    codes = [c for c in range(256) if c & 0x7F != 0x7F]
+    lens_q, lens_k = [2, 0, 5], [4, 3, 5]
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    qc = rng.choice(codes, (int(cu_q[-1]), 4, 3)).astype(np.uint8)
+    kc = rng.choice(codes, (int(cu_k[-1]), 2, 3)).astype(np.uint8)
+    vc = rng.choice(codes, (int(cu_k[-1]), 2, 3)).astype(np.uint8)
+    o, lse = attention_prefill_varlen_fp8(qc, kc, vc, cu_q, cu_k, 0.4, 0.02, 0.03, 0.05, causal)
+    for b in range(3):
+        if lens_q[b] == 0:
+            continue
+        sq, sk = slice(cu_q[b], cu_q[b + 1]), slice(cu_k[b], cu_k[b + 1])
+        od, ld = attention_prefill_fp8(qc[sq].transpose(1, 0, 2)[None], kc[sk].transpose(1, 0, 2)[None],
+                                       vc[sk].transpose(1, 0, 2)[None], 0.4, 0.02, 0.03, 0.05, causal)
+        np.testing.assert_allclose(o[sq], od[0].transpose(1, 0, 2), rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lse[:, sq], ld[0], rtol=1e-12, atol=1e-12)
+
+
 # ----------------------------------------------------------------------------- backward
 def _bwd_case(seed, B=1, Hq=2, Hkv=1, Nq=5, Nk=7, d=3):
     rng = np.random.default_rng(seed)
