@@ -278,24 +278,33 @@ def custom_prefill(seed: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: in
 # ----------------------------------------------------------------------------
 # Variable-length (ragged) prefill inputs
 # ----------------------------------------------------------------------------
-def varlen_inputs(seed: int, lens_q, lens_k, Hq: int, Hkv: int, d: int, f16: bool = False):
+def varlen_inputs(seed: int, lens_q, lens_k, Hq: int, Hkv: int, d: int, f16: bool = False,
+                  fp8: bool = False):
     """Packed ragged batch: q [total_q, Hq, d], k, v [total_k, Hkv, d] bf16 bits (fp16 when
-    f16) and the cumulative lengths cu_q, cu_k (int32 [B+1]).  Sequence b, head h draws its
-    rows from the same per-(b, h) streams as the dense layout does, so each sequence equals
-    a dense prefill input of its own length."""
+    f16; E4M3 codes over FP8_Q/K/V_SCALE when fp8) and the cumulative lengths cu_q, cu_k
+    (int32 [B+1]).  Sequence b, head h draws its rows from the same per-(b, h) streams as
+    the dense layout does, so each sequence equals a dense prefill input of its own length."""
     lens_q = np.asarray(lens_q, np.int64)
     lens_k = np.asarray(lens_k, np.int64)
     cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
     cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
-    q = np.empty((int(cu_q[-1]), Hq, d), np.uint16)
-    k = np.empty((int(cu_k[-1]), Hkv, d), np.uint16)
+    dt = np.uint8 if fp8 else np.uint16
+    q = np.empty((int(cu_q[-1]), Hq, d), dt)
+    k = np.empty((int(cu_k[-1]), Hkv, d), dt)
     v = np.empty_like(k)
+
+    def draw(tensor, b, h, n):
+        if fp8:
+            sc = {T_Q: FP8_Q_SCALE, T_K: FP8_K_SCALE, T_V: FP8_V_SCALE}[tensor]
+            return normal_e4m3(seed, tensor, b, h, (n, d), sc)
+        return normal_bf16(seed, tensor, b, h, (n, d), f16=f16)
+
     for b in range(len(lens_q)):
         for h in range(Hq):
-            q[cu_q[b]:cu_q[b + 1], h] = normal_bf16(seed, T_Q, b, h, (int(lens_q[b]), d), f16=f16)
+            q[cu_q[b]:cu_q[b + 1], h] = draw(T_Q, b, h, int(lens_q[b]))
         for h in range(Hkv):
-            k[cu_k[b]:cu_k[b + 1], h] = normal_bf16(seed, T_K, b, h, (int(lens_k[b]), d), f16=f16)
-            v[cu_k[b]:cu_k[b + 1], h] = normal_bf16(seed, T_V, b, h, (int(lens_k[b]), d), f16=f16)
+            k[cu_k[b]:cu_k[b + 1], h] = draw(T_K, b, h, int(lens_k[b]))
+            v[cu_k[b]:cu_k[b + 1], h] = draw(T_V, b, h, int(lens_k[b]))
     return q, k, v, cu_q, cu_k
 
 

@@ -451,6 +451,22 @@ def main():
         extra["varlen_prefill"] = {"us": round(avg, 2), "us_min": round(mn, 2),
                                    "TFLOP/s": round(tf, 2), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                                    "lengths": [int(x) for x in vl]}
+        bf16_varlen_us = avg
+        del vq, vk, vv, vo
+        torch.cuda.empty_cache()
+        # the same ragged batch over FP8 inputs
+        vq, vk, vv, _, _ = ai.varlen_inputs(cfg.seed, vl, vl, cfg.Hq, cfg.Hkv, cfg.d, fp8=True)
+        vq, vk, vv = (torch.from_numpy(x).cuda() for x in (vq, vk, vv))
+        vo = torch.empty(vq.shape, dtype=torch.bfloat16, device="cuda")
+        avg, med, mn = time_kernel(
+            lambda: mi.attn_fwd_prefill_varlen_fp8(vq, vk, vv, vo, vlse, vcq, vck, mx, mx, True,
+                                                   cfg.scale, ai.FP8_Q_SCALE, ai.FP8_K_SCALE,
+                                                   ai.FP8_V_SCALE, stream), args.steps, args.warmup)
+        tf = fl / (avg * 1e-6) / 1e12
+        extra["varlen_prefill_fp8"] = {"us": round(avg, 2), "us_min": round(mn, 2),
+                                       "TFLOP/s": round(tf, 2),
+                                       "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                                       "speedup_vs_bf16": round(bf16_varlen_us / avg, 3)}
         del vq, vk, vv, vcq, vck, vo, vlse
         torch.cuda.empty_cache()
         # backward of the causal Llama-2-shaped prefill (dQ, dK, dV from the stored LSE)

@@ -202,6 +202,21 @@ int attn_fwd_prefill_varlen(const void* q, const void* k, const void* v, void* o
                             int max_seqlen_k, int d, int causal, float scale,
                             hipStream_t stream);
 
+/*
+ * Variable-length prefill over FP8 inputs: attn_fwd_prefill_varlen with q, k and v packed
+ * as E4M3 codes (the token-major layouts, one byte per element) and the per-tensor scales
+ * of attn_fwd_prefill_fp8, computed as attn_fwd_prefill_fp8 computes; o is bf16.
+ *
+ * Errors: those of attn_fwd_prefill_varlen, plus INVALID_ARGUMENT for a non-finite or
+ * non-positive q_scale, k_scale or v_scale, or when |scale| * q_scale * k_scale overflows
+ * float.
+ */
+int attn_fwd_prefill_varlen_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
+                                int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                                int max_seqlen_k, int d, int causal, float scale, float q_scale,
+                                float k_scale, float v_scale, hipStream_t stream);
+
 /* attn_fwd_prefill_varlen with fp16 q, k, v and o (as in attn_fwd_prefill_f16). */
 int attn_fwd_prefill_varlen_f16(const void* q, const void* k, const void* v, void* o, float* lse,
                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,

@@ -78,6 +78,8 @@ def load_library():
     lib.attn_fwd_prefill_varlen.restype = i32
     lib.attn_fwd_prefill_varlen_f16.argtypes = lib.attn_fwd_prefill_varlen.argtypes
     lib.attn_fwd_prefill_varlen_f16.restype = i32
+    lib.attn_fwd_prefill_varlen_fp8.argtypes = [vp] * 7 + [i32] * 9 + [f32] * 4 + [vp]
+    lib.attn_fwd_prefill_varlen_fp8.restype = i32
     lib.attn_bwd.argtypes = [vp] * 9 + [i32] * 7 + [f32, vp, ctypes.c_size_t, vp]
     lib.attn_bwd.restype = i32
     lib.attn_bwd_f16.argtypes = lib.attn_bwd.argtypes
@@ -261,13 +263,13 @@ def prefill_paged(q, kcache, vcache, block_table, kv_lens, max_kv_len: int, caus
 
 
 def _varlen_call(fn, dtype, q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-                 max_seqlen_k, causal, scale, stream):
+                 max_seqlen_k, causal, scale, stream, fp8_scales=None):
     lib = load_library()
     _check(q, "q", dtype, 3)
     dev = q.device
     _check(k, "k", dtype, 3, dev)
     _check(v, "v", dtype, 3, dev)
-    _check(o, "o", dtype, 3, dev)
+    _check(o, "o", torch.bfloat16 if fp8_scales else dtype, 3, dev)
     _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1, dev)
     _check(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1, dev)
     total_q, Hq, d = q.shape
@@ -283,9 +285,20 @@ def _varlen_call(fn, dtype, q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seq
     st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q),
                           _ptr(cu_seqlens_k), B, Hq, Hkv, total_q, total_k, int(max_seqlen_q),
                           int(max_seqlen_k), d, 1 if causal else 0, float(scale),
+                          *([float(x) for x in fp8_scales] if fp8_scales else []),
                           _stream_handle(stream))
     if st != ATTN_OK:
         raise AttnError(st, fn)
+
+
+def attn_fwd_prefill_varlen_fp8(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+                                max_seqlen_k: int, causal: bool, scale: float, q_scale: float,
+                                k_scale: float, v_scale: float, stream=None) -> None:
+    """attn_fwd_prefill_varlen over FP8 inputs: q, k, v hold OCP E4M3 codes (torch.uint8 or
+    torch.float8_e4m3fn) standing for q_scale * e4m3(code) (k_scale, v_scale); o is bf16."""
+    _varlen_call("attn_fwd_prefill_varlen_fp8", (torch.uint8, torch.float8_e4m3fn), q, k, v, o,
+                 lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, causal, scale,
+                 stream, (q_scale, k_scale, v_scale))
 
 
 def attn_fwd_prefill_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
@@ -521,7 +534,7 @@ def backward(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = N
 
 
 __all__ = ["attn_bwd", "attn_bwd_f16", "attn_bwd_workspace_bytes", "backward", "attn_fwd_prefill_varlen",
-           "attn_fwd_prefill_varlen_f16",
+           "attn_fwd_prefill_varlen_f16", "attn_fwd_prefill_varlen_fp8",
            "prefill_varlen",
            "attn_fwd_prefill", "attn_fwd_prefill_f16", "attn_fwd_prefill_fp8", "prefill_fp8",
            "attn_fwd_prefill_paged_f16", "attn_fwd_prefill_paged_fp8",

@@ -26,7 +26,7 @@ struct PrefillParams {
   int max_blocks;
   uint32_t page_max;  // num_pages - 1: page ids are clamped to it
   int f16;  // Q, K, V, O are fp16 (else bf16)
-  // FP8 (dense layout only): Q, K, V are E4M3 codes, O is bf16; c then carries the Q and
+  // FP8 (dense or paged layout): Q, K, V are E4M3 codes, O is bf16; c then carries the Q and
   // K scales, and v_scale multiplies the normalised output.
   int fp8;
   float v_scale;

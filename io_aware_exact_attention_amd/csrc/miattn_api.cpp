@@ -218,7 +218,9 @@ int prefill_paged_impl(const void* q, const void* kcache, const void* vcache,
 int prefill_varlen_impl(const void* q, const void* k, const void* v, void* o, float* lse,
                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int Hq,
                         int Hkv, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
-                        int d, int causal, float scale, bool f16, hipStream_t stream) {
+                        int d, int causal, float scale, bool f16, hipStream_t stream,
+                        bool fp8 = false, float q_scale = 1.f, float k_scale = 1.f,
+                        float v_scale = 1.f) {
   if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
@@ -228,6 +230,9 @@ int prefill_varlen_impl(const void* q, const void* k, const void* v, void* o, fl
       max_seqlen_k < 1 || d < 1)
     return ATTN_ERR_INVALID_ARGUMENT;
   if (Hq % Hkv || max_seqlen_q > total_q || max_seqlen_k > total_k || !std::isfinite(scale))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (fp8 && !(std::isfinite(q_scale) && q_scale > 0.f && std::isfinite(k_scale) &&
+               k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
     return ATTN_ERR_INVALID_ARGUMENT;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   const long qtiles = (max_seqlen_q + 255) / 256;
@@ -249,6 +254,10 @@ int prefill_varlen_impl(const void* q, const void* k, const void* v, void* o, fl
   p.total_q = total_q;
   p.total_k = total_k;
   p.f16 = f16;
+  if (fp8) p.c *= q_scale * k_scale;
+  if (!std::isfinite(p.c)) return ATTN_ERR_INVALID_ARGUMENT;
+  p.fp8 = fp8;
+  p.v_scale = v_scale;
   (void)hipGetLastError();
   return miattn::launch_prefill(p, d, causal ? 1 : 0, stream) == hipSuccess ? ATTN_OK
                                                                              : ATTN_ERR_HIP;
@@ -368,6 +377,16 @@ int attn_fwd_prefill_varlen(const void* q, const void* k, const void* v, void* o
                             hipStream_t stream) {
   return prefill_varlen_impl(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q,
                              total_k, max_seqlen_q, max_seqlen_k, d, causal, scale, false, stream);
+}
+
+int attn_fwd_prefill_varlen_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
+                                int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                                int max_seqlen_k, int d, int causal, float scale, float q_scale,
+                                float k_scale, float v_scale, hipStream_t stream) {
+  return prefill_varlen_impl(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q,
+                             total_k, max_seqlen_q, max_seqlen_k, d, causal, scale, false, stream,
+                             true, q_scale, k_scale, v_scale);
 }
 
 int attn_fwd_prefill_varlen_f16(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -164,13 +164,12 @@ __device__ __forceinline__ PagedItem paged_work_item(int p, int B, int Hq, int n
 // Layouts: dense [B, H, N, D] (PAGED and VARLEN false); PAGED: K/V in the paged cache,
 // kv_lens per sequence; VARLEN: sequences packed along the token axis, [total, H, D], with
 // cumulative lengths cu_q, cu_k.
-// F8 (E = ElemFp8, dense or paged layout): Q, K, V are E4M3 codes; Q.K^T runs on the FP8
-// MFMA, V is widened to bf16 in LDS, and O is scaled by v_scale.
+// F8 (E = ElemFp8, any layout): Q, K, V are E4M3 codes; Q.K^T runs on the FP8 MFMA, V is
+// widened to bf16 in LDS, and O is scaled by v_scale.
 template <int D, bool CAUSAL, bool PAGED, bool VARLEN, typename E>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillParams a) {
   constexpr bool F8 = E::kFp8;
-  static_assert(!(F8 && VARLEN), "FP8 prefill takes the dense or the paged layout");
   using S = PrefillShape<D, F8>;
   __shared__ __attribute__((aligned(1024))) char smem[S::LDS];
 
@@ -230,12 +229,19 @@ void prefill_kernel(PrefillParams a) {
       PAGED ? a.v
             : (VARLEN ? a.v + ((size_t)k_start * a.Hkv + kvh) * D
                       : a.v + (size_t)(b * a.Hkv + kvh) * a.Nk * D);
-  // F8: the same tensors as one byte per element (paged: the pools)
-  const uint8_t* __restrict__ Q8h = (const uint8_t*)a.q + (size_t)(b * a.Hq + hq) * a.Nq * D;
+  // F8: the same tensors as one byte per element (paged: the pools); varlen rows are still
+  // qstride (kstride) elements, now bytes, apart
+  const uint8_t* __restrict__ Q8h =
+      (const uint8_t*)a.q + (VARLEN ? ((size_t)q_start * a.Hq + hq) * D
+                                    : (size_t)(b * a.Hq + hq) * a.Nq * D);
   const uint8_t* __restrict__ K8h =
-      (const uint8_t*)a.k + (PAGED ? 0 : (size_t)(b * a.Hkv + kvh) * a.Nk * D);
+      (const uint8_t*)a.k + (PAGED ? 0
+                             : VARLEN ? ((size_t)k_start * a.Hkv + kvh) * D
+                                      : (size_t)(b * a.Hkv + kvh) * a.Nk * D);
   const uint8_t* __restrict__ V8h =
-      (const uint8_t*)a.v + (PAGED ? 0 : (size_t)(b * a.Hkv + kvh) * a.Nk * D);
+      (const uint8_t*)a.v + (PAGED ? 0
+                             : VARLEN ? ((size_t)k_start * a.Hkv + kvh) * D
+                                      : (size_t)(b * a.Hkv + kvh) * a.Nk * D);
 
   // keys the workgroup needs: everything, or up to the diagonal of its last query
   int kend = nk;
@@ -270,14 +276,16 @@ void prefill_kernel(PrefillParams a) {
   if constexpr (F8) {
     // block blk = i*kWaves + wave of the stage: K blocks (swizzled rows) first, then the V
     // blocks, which keep the rows' byte order (the widening reads them linearly)
+    const int row8 = VARLEN ? (int)kstride : D;  // bytes between consecutive key rows
 #pragma unroll
     for (int i = 0; i < NOFF; ++i) {
       const int blk = i * S::kWaves + wave;
       if (blk < S::TILE / 1024) {
         const int p = blk * 64 + lane, R = p / (D / 16);
-        dma_off[i] = R * D + (((p % (D / 16)) ^ chunk_swizzle_f8<D>(R)) << 4);
+        dma_off[i] = R * row8 + (((p % (D / 16)) ^ chunk_swizzle_f8<D>(R)) << 4);
       } else {
-        dma_off[i] = ((blk - S::TILE / 1024) * 64 + lane) * 16;
+        const int p = (blk - S::TILE / 1024) * 64 + lane;
+        dma_off[i] = VARLEN ? (p / (D / 16)) * row8 + (p % (D / 16)) * 16 : p * 16;
       }
     }
   } else {
@@ -329,9 +337,12 @@ void prefill_kernel(PrefillParams a) {
                   (lds_void*)(st + blk * 1024));
       }
     } else if constexpr (F8) {
-      const int nbytes = (nk - n0) * D;
-      const uint8_t* kt = K8h + (size_t)n0 * D;
-      const uint8_t* vt = V8h + (size_t)n0 * D;
+      // varlen: the range ends with the sequence's last key row inside this tile
+      const int nbytes =
+          VARLEN ? __builtin_amdgcn_readfirstlane((min(nk - n0, S::BN) - 1) * (int)kstride + D)
+                 : (nk - n0) * D;
+      const uint8_t* kt = K8h + (size_t)n0 * (VARLEN ? kstride : D);
+      const uint8_t* vt = V8h + (size_t)n0 * (VARLEN ? kstride : D);
 #pragma unroll
       for (int i = 0; i < NOFF; ++i) {
         const int blk = i * S::kWaves + wave;
@@ -388,7 +399,7 @@ void prefill_kernel(PrefillParams a) {
   QOp qop[F8 ? D / 64 : D / 16];
   if constexpr (F8) {
     const uint32_t flip = a.negate_q ? 0x80808080u : 0u;
-    const u32x4* src = (const u32x4*)(Q8h + (size_t)min(qrow, nq - 1) * D);
+    const u32x4* src = (const u32x4*)(Q8h + (size_t)min(qrow, nq - 1) * (VARLEN ? qstride : D));
 #pragma unroll
     for (int s = 0; s < D / 64; ++s) {
       u32x4 w0 = src[4 * s + g], w1 = src[4 * s + 2 + g];
@@ -763,6 +774,9 @@ template <int D, bool CAUSAL>
 static hipError_t launch_f8(const PrefillParams& p, hipStream_t stream) {
   if (p.block_table)
     hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, true, false, ElemFp8>), dim3(p.total_wg),
+                       dim3(512), 0, stream, p);
+  else if (p.cu_q)
+    hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, false, true, ElemFp8>), dim3(p.total_wg),
                        dim3(512), 0, stream, p);
   else
     hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, false, false, ElemFp8>), dim3(p.total_wg),

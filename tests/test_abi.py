@@ -32,6 +32,7 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["attn_fwd_prefill", "attn_fwd_prefill_paged",
                                            "attn_fwd_prefill_f16", "attn_fwd_prefill_paged_f16",
                                            "attn_fwd_prefill_fp8", "attn_fwd_prefill_paged_fp8",
+                                           "attn_fwd_prefill_varlen_fp8",
                                            "attn_fwd_decode", "attn_fwd_decode_f16",
                                            "attn_fwd_decode_fp8", "attn_bwd", "attn_bwd_f16",
                                            "attn_fwd_prefill_varlen",
@@ -203,6 +204,22 @@ def test_prefill_paged_fp8_validation(lib, kw, status):
                            "Nq", "d", "max_kv", "page_size", "max_blocks", "num_pages", "causal")]
     args += [ctypes.c_float(a[n]) for n in ("scale", "q_scale", "k_scale", "v_scale")] + [None]
     assert lib.attn_fwd_prefill_paged_fp8(*args) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_scale=-1.0), INVALID), (dict(k_scale=float("inf")), INVALID), (dict(v_scale=0.0), INVALID),
+    (dict(scale=1e20, q_scale=1e20, k_scale=1e10), INVALID),
+    (dict(cu_q=None), INVALID), (dict(Hq=3, Hkv=2), INVALID), (dict(max_q=300), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(q=MIS), INVALID)])
+def test_prefill_varlen_fp8_validation(lib, kw, status):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, cu_q=P, cu_k=P, B=2, Hq=4, Hkv=2, total_q=200,
+             total_k=250, max_q=150, max_k=200, d=128, causal=1, scale=0.1, q_scale=0.02,
+             k_scale=0.03, v_scale=0.04)
+    a.update(kw)
+    args = [a[n] for n in ("q", "k", "v", "o", "lse", "cu_q", "cu_k", "B", "Hq", "Hkv", "total_q",
+                           "total_k", "max_q", "max_k", "d", "causal")]
+    args += [ctypes.c_float(a[n]) for n in ("scale", "q_scale", "k_scale", "v_scale")] + [None]
+    assert lib.attn_fwd_prefill_varlen_fp8(*args) == status
 
 
 def test_f16_paged_and_decode_validate_like_bf16(lib):

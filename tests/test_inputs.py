@@ -174,6 +174,18 @@ def test_fp8_chunk_queries_quantise_the_bf16_chunk_draws():
     np.testing.assert_array_equal(q[1, 0], _torch_e4m3(x / np.float32(ai.FP8_Q_SCALE)))
 
 
+def test_fp8_varlen_inputs_pack_the_dense_fp8_streams():
+    q, k, v, cu_q, cu_k = ai.varlen_inputs(14, [5, 9], [7, 9], 2, 1, 8, fp8=True)
+    assert q.dtype == k.dtype == v.dtype == np.uint8
+    cfg = ai.PrefillCfg("t", 1, 2, 1, 9, 9, 8, True, 14, fp8=True)
+    dq, dk, dv = ai.prefill_inputs(cfg)
+    # sequence 1 has 9 query and 9 key rows: batch index 1 of the streams
+    np.testing.assert_array_equal(q[5:14, 1], ai.normal_e4m3(14, ai.T_Q, 1, 1, (9, 8), ai.FP8_Q_SCALE))
+    np.testing.assert_array_equal(k[7:16, 0], ai.normal_e4m3(14, ai.T_K, 1, 0, (9, 8), ai.FP8_K_SCALE))
+    np.testing.assert_array_equal(v[0:7, 0], ai.normal_e4m3(14, ai.T_V, 0, 0, (7, 8), ai.FP8_V_SCALE))
+    np.testing.assert_array_equal(dq[0, 0], ai.normal_e4m3(14, ai.T_Q, 0, 0, (9, 8), ai.FP8_Q_SCALE))
+
+
 # ----------------------------------------------------------------------------- fp16 rounding
 def test_f16_rounding_matches_torch():
     rng = np.random.default_rng(2)

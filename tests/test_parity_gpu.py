@@ -18,8 +18,8 @@ import attn_inputs as ai
 import io_aware_exact_attention_amd as mi
 from oracle import (attention_backward, attention_decode, attention_decode_fp8,
                     attention_prefill, attention_prefill_fp8, attention_prefill_paged,
-                    attention_prefill_paged_fp8, attention_prefill_varlen, attention_rows,
-                    e4m3_value, gather_paged)
+                    attention_prefill_paged_fp8, attention_prefill_varlen,
+                    attention_prefill_varlen_fp8, attention_rows, e4m3_value, gather_paged)
 
 pytestmark = pytest.mark.gpu
 
@@ -1248,3 +1248,51 @@ def test_chunked_prefill_paged_fp8_config():
              lse_tol=tol)
     assert np.isfinite(go).all()
     assert err.max() <= TOL_MAX and err.mean() <= TOL_MEAN and lerr.max() <= tol
+
+
+# ------------------------------------------------------------------ FP8 varlen prefill
+def run_varlen_fp8(q, k, v, cu_q, cu_k, causal, scale):
+    t = lambda c: torch.from_numpy(np.ascontiguousarray(c)).cuda()
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device="cuda")
+    lq, lk = np.diff(cu_q), np.diff(cu_k)
+    mi.attn_fwd_prefill_varlen_fp8(t(q), t(k), t(v), o, lse, t(cu_q), t(cu_k), int(lq.max()),
+                                   int(lk.max()), causal, scale, QS, KS, VS)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def varlen_fp8_lse_tol(q, k, scale):
+    Q = np.abs(QS * e4m3_value(q)).max(axis=0)     # [Hq, d]
+    K = np.abs(KS * e4m3_value(k)).max(axis=0)     # [Hkv, d]
+    G = q.shape[1] // k.shape[1]
+    maxprod = max(float((Q[h] * K[h // G]).max()) for h in range(q.shape[1]))
+    return TOL_LSE + (q.shape[2] // 64) * 2.0 ** -11 * abs(float(np.float32(scale))) * maxprod
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_varlen_fp8(d, causal):
+    lens_k = [1, 300, 77, 513, 64, 2]
+    lens_q = [1, 300, 10, 257, 0, 2] if causal else [5, 300, 77, 100, 64, 1]
+    q, k, v, cu_q, cu_k = ai.varlen_inputs(13000 + d, lens_q, lens_k, 4, 2, d, fp8=True)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    o, lse = run_varlen_fp8(q, k, v, cu_q, cu_k, causal, scale)
+    ro, rl = attention_prefill_varlen_fp8(q, k, v, cu_q, cu_k, scale, QS, KS, VS, causal)
+    check(f"prefill_varlen_fp8 d={d} causal={causal}", o, lse, ro, rl,
+          varlen_fp8_lse_tol(q, k, scale))
+
+
+def test_prefill_varlen_fp8_equals_dense_fp8_prefill():
+    # each packed sequence equals the dense FP8 prefill of its own draws, bit for bit
+    lens = [300, 129, 1]
+    q, k, v, cu_q, cu_k = ai.varlen_inputs(13100, lens, lens, 4, 2, 128, fp8=True)
+    o, lse = run_varlen_fp8(q, k, v, cu_q, cu_k, True, 0.09)
+    for b, n in enumerate(lens):
+        s = slice(cu_q[b], cu_q[b + 1])
+        qd = np.ascontiguousarray(q[s].transpose(1, 0, 2))[None]
+        kd = np.ascontiguousarray(k[s].transpose(1, 0, 2))[None]
+        vd = np.ascontiguousarray(v[s].transpose(1, 0, 2))[None]
+        od, ld = run_prefill_fp8(qd, kd, vd, True, 0.09, QS, KS, VS)
+        assert torch.equal(o[s], od[0].transpose(0, 1)), b
+        assert torch.equal(lse[:, s], ld[0]), b
