@@ -298,9 +298,9 @@ def attention_decode_fp8(q: np.ndarray, kcodes: np.ndarray, vcodes: np.ndarray,
 def attention_prefill_fp8(qcodes: np.ndarray, kcodes: np.ndarray, vcodes: np.ndarray,
                           scale: float, q_scale: float, k_scale: float, v_scale: float,
                           causal: bool, row_block: int = 1024):
-    """Prefill over FP8 inputs with one scale per tensor (the FP8 forward that the page
-    "Flash Attention: GPU 메모리_IO를 최적화하는..." (holysheep), "FlashAttention 3"
-    subsection, lists; the pages give no format or scale convention, so the reading is
+    """Prefill over FP8 inputs with one scale per tensor (the FP8 support that the page
+    "FlashAttention 완전 정리" (cell-devlog), section "FlashAttention 버전별 발전", subsection
+    "FlashAttention 3", lists; the pages give no format or scale convention, so the reading is
     OCP E4M3 codes with per-tensor scales, as for the FP8 cache): Q is
     q_scale * e4m3_value(qcodes), K and V likewise with k_scale and v_scale, laid out as in
     attention_prefill.  The result is the plain definition on those dequantised values.
