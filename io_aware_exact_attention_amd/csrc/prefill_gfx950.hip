@@ -505,24 +505,32 @@ void prefill_kernel(PrefillParams a) {
     }
   };
   // F8: widen V tile j (E4M3 in its ring stage, rows in byte order) into its bf16 buffer in
-  // the layout the transposing P.V reads expect.  All 512 threads, D/8 codes each.
+  // the layout the transposing P.V reads expect.  Widening happens in even slots, where
+  // group 0 issues MFMAs and group 1 runs the softmax; group 0's 256 threads do it all
+  // (D/4 codes each), which keeps the softmax slot's vector work unchanged.
   auto widen = [&](int j) {
     if constexpr (F8) {
+      if (grp != 0) return;
       const char* src = stage(j) + S::TILE;
       char* dst = smem + S::RING + (j & 1) * S::VTILE;
-      const int R = tid >> 3, c = tid & 7;
-      const int sw = chunk_swizzle<D>(R);
-      if constexpr (D == 128) {
-        const u32x4 w = *(const u32x4*)(src + tid * 16);
-        const u32x2 e0 = e4m3x4_to_bf16x4(w[0]), e1 = e4m3x4_to_bf16x4(w[1]);
-        const u32x2 e2 = e4m3x4_to_bf16x4(w[2]), e3 = e4m3x4_to_bf16x4(w[3]);
-        *(u32x4*)(dst + R * S::ROWB + (((2 * c) ^ sw) << 4)) = u32x4{e0[0], e0[1], e1[0], e1[1]};
-        *(u32x4*)(dst + R * S::ROWB + (((2 * c + 1) ^ sw) << 4)) =
-            u32x4{e2[0], e2[1], e3[0], e3[1]};
-      } else {
-        const u32x2 w = *(const u32x2*)(src + tid * 8);
-        const u32x2 e0 = e4m3x4_to_bf16x4(w[0]), e1 = e4m3x4_to_bf16x4(w[1]);
-        *(u32x4*)(dst + R * S::ROWB + ((c ^ sw) << 4)) = u32x4{e0[0], e0[1], e1[0], e1[1]};
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int t = tid + 256 * hh;
+        const int R = t >> 3, c = t & 7;
+        const int sw = chunk_swizzle<D>(R);
+        if constexpr (D == 128) {
+          const u32x4 w = *(const u32x4*)(src + t * 16);
+          const u32x2 e0 = e4m3x4_to_bf16x4(w[0]), e1 = e4m3x4_to_bf16x4(w[1]);
+          const u32x2 e2 = e4m3x4_to_bf16x4(w[2]), e3 = e4m3x4_to_bf16x4(w[3]);
+          *(u32x4*)(dst + R * S::ROWB + (((2 * c) ^ sw) << 4)) =
+              u32x4{e0[0], e0[1], e1[0], e1[1]};
+          *(u32x4*)(dst + R * S::ROWB + (((2 * c + 1) ^ sw) << 4)) =
+              u32x4{e2[0], e2[1], e3[0], e3[1]};
+        } else {
+          const u32x2 w = *(const u32x2*)(src + t * 8);
+          const u32x2 e0 = e4m3x4_to_bf16x4(w[0]), e1 = e4m3x4_to_bf16x4(w[1]);
+          *(u32x4*)(dst + R * S::ROWB + ((c ^ sw) << 4)) = u32x4{e0[0], e0[1], e1[0], e1[1]};
+        }
       }
     }
   };
