@@ -10,6 +10,10 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    # The oracle's process pool forks its workers from a server process; start it now,
+    # before anything in this process initialises the GPU.
+    from oracle import pool
+    pool.start()
 
 
 def pytest_collection_modifyitems(config, items):

@@ -2,8 +2,9 @@
 
 Bar, for bf16 inputs with fp32 accumulation, O compared after upcasting the GPU's bf16
 output: max abs error <= 2e-2, mean abs error <= 2e-3, LSE max abs error <= 1e-3.
-Small shapes are compared element by element over the whole output; the full-size
-workloads are compared on sampled heads and rows the oracle computes one by one.
+Small shapes and the full-size prefill workloads are compared element by element over the
+whole output (the full sizes through the oracle's process pool); the largest decode and
+FP8 workloads on sampled heads and rows the oracle computes one by one.
 Set MIATTN_PARITY_LOG=<path> to append every case's errors as JSON lines.
 """
 import json
@@ -16,6 +17,7 @@ import torch
 
 import attn_inputs as ai
 import io_aware_exact_attention_amd as mi
+from oracle import pool as oracle_pool
 from oracle import (attention_backward, attention_decode, attention_decode_fp8,
                     attention_prefill, attention_prefill_fp8, attention_prefill_paged,
                     attention_prefill_paged_fp8, attention_prefill_varlen,
@@ -154,33 +156,19 @@ def test_prefill_constant_values():
 
 
 # ------------------------------------------------------------------ prefill, full sizes
-def sampled_prefill_check(cfg, o, lse, q, k, v, heads_full, rows_per_head, seed):
-    """Compare whole heads in heads_full, and rows_per_head sampled rows of every head
-    (always including the first and last row)."""
-    rng = np.random.default_rng(seed)
-    go = o.float().cpu().numpy()
+def whole_prefill_check(name, o, lse):
+    """Every output of a full-size prefill workload against the oracle, head by head in
+    the oracle's process pool (each worker regenerates its head's inputs from the seeds)."""
+    o_bits = o.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
     gl = lse.cpu().numpy()
-    errs, lerrs = [], []
-    for b in range(cfg.B):
-        for h in range(cfg.Hq):
-            if (b, h) in heads_full:
-                rows = np.arange(cfg.Nq)
-            else:
-                rows = np.unique(np.concatenate([[0, cfg.Nq - 1],
-                                                 rng.integers(0, cfg.Nq, rows_per_head)]))
-            kvh = h // (cfg.Hq // cfg.Hkv)
-            K, V = f64(k[b, kvh]), f64(v[b, kvh])
-            for i0 in range(0, len(rows), 1024):
-                r = rows[i0:i0 + 1024]
-                ro, rl = attention_rows(f64(q[b, h, r]), K, V, cfg.scale, cfg.causal, r, cfg.Nq)
-                errs.append(np.abs(go[b, h, r] - ro).ravel())
-                lerrs.append(np.abs(gl[b, h, r] - rl).ravel())
-    err = np.concatenate(errs)
-    lerr = np.concatenate(lerrs)
-    log_case(cfg.name + " (sampled)", max_abs=float(err.max()), mean_abs=float(err.mean()),
-             lse_max_abs=float(lerr.max()), n=int(err.size))
-    assert np.isfinite(go).all()
-    assert err.max() <= TOL_MAX and err.mean() <= TOL_MEAN and lerr.max() <= TOL_LSE
+    r = oracle_pool.check_prefill_heads(name, o_bits, gl,
+                                        progress=lambda m: print(m, flush=True))
+    log_case(name + " (whole output)", max_abs=r["max_abs"], mean_abs=r["mean_abs"],
+             lse_max_abs=r["lse_max_abs"], n=r["n"], max_at=list(r["max_at"]))
+    cfg = ai.CONFIGS[name]
+    assert r["n"] == cfg.B * cfg.Hq * cfg.Nq * cfg.d
+    assert r["finite"]
+    assert r["max_abs"] <= TOL_MAX and r["mean_abs"] <= TOL_MEAN and r["lse_max_abs"] <= TOL_LSE
 
 
 @pytest.mark.parametrize("name", ["llama2_7b_prefill", "llama2_7b_prefill_noncausal"])
@@ -188,47 +176,17 @@ def test_prefill_llama2_shape(name):
     cfg = ai.CONFIGS[name]
     q, k, v = ai.prefill_inputs(cfg)
     o, lse = run_prefill(q, k, v, cfg.causal, cfg.scale)
-    sampled_prefill_check(cfg, o, lse, q, k, v, heads_full={(0, 0), (3, 31), (1, 17)},
-                          rows_per_head=16, seed=7)
+    whole_prefill_check(name, o, lse)
 
 
 def test_prefill_long_context_32k():
+    # every row of every head; a block of 1,024 causal rows is compared against the keys
+    # it can see (~9 TFLOP of fp64 oracle work over the pool)
     cfg = ai.CONFIGS["long_prefill_32k"]
     q, k, v = ai.prefill_inputs(cfg)
     o, lse = run_prefill(q, k, v, cfg.causal, cfg.scale)
-    del q
-    qh = {h: ai.prefill_head(cfg, ai.T_Q, 0, h) for h in range(cfg.Hq)}
-    rng = np.random.default_rng(8)
-    go = o.float().cpu().numpy()
-    gl = lse.cpu().numpy()
-    errs, lerrs = [], []
-    for h in range(cfg.Hq):
-        n = 96 if h in (0, 31) else 6
-        rows = np.unique(np.concatenate([[0, 1, cfg.Nq - 2, cfg.Nq - 1],
-                                         rng.integers(0, cfg.Nq, n)]))
-        ro, rl = attention_rows(f64(qh[h][rows]), f64(k[0, h]), f64(v[0, h]), cfg.scale, True,
-                                rows, cfg.Nq)
-        errs.append(np.abs(go[0, h, rows] - ro).ravel())
-        lerrs.append(np.abs(gl[0, h, rows] - rl).ravel())
-        # the first 1,024 rows of every head (causal: they see only the first 1,024 keys)
-        first = np.arange(1024)
-        ro, rl = attention_rows(f64(qh[h][:1024]), f64(k[0, h, :1024]), f64(v[0, h, :1024]),
-                                cfg.scale, True, first, 1024)
-        errs.append(np.abs(go[0, h, :1024] - ro).ravel())
-        lerrs.append(np.abs(gl[0, h, :1024] - rl).ravel())
-        # the last 1,024 rows, against all 32K keys, for four heads
-        if h in (0, 11, 22, 31):
-            last = np.arange(cfg.Nq - 1024, cfg.Nq)
-            ro, rl = attention_rows(f64(qh[h][last]), f64(k[0, h]), f64(v[0, h]), cfg.scale,
-                                    True, last, cfg.Nq)
-            errs.append(np.abs(go[0, h, last] - ro).ravel())
-            lerrs.append(np.abs(gl[0, h, last] - rl).ravel())
-    err, lerr = np.concatenate(errs), np.concatenate(lerrs)
-    log_case("long_prefill_32k (first 1,024 rows of every head, last 1,024 of four, sampled "
-             "rows)", max_abs=float(err.max()), mean_abs=float(err.mean()),
-             lse_max_abs=float(lerr.max()), n=int(err.size))
-    assert np.isfinite(go).all()
-    assert err.max() <= TOL_MAX and err.mean() <= TOL_MEAN and lerr.max() <= TOL_LSE
+    del q, k, v
+    whole_prefill_check("long_prefill_32k", o, lse)
 
 
 # ------------------------------------------------------------------ decode
@@ -583,21 +541,7 @@ def test_prefill_f16_llama2_shape():
     cfg = ai.CONFIGS["llama2_7b_prefill_f16"]
     q, k, v = ai.prefill_inputs(cfg)
     o, lse = run_prefill16(q, k, v, cfg.causal, cfg.scale)
-    go = o.float().cpu().numpy()
-    gl = lse.cpu().numpy()
-    rng = np.random.default_rng(17)
-    errs, lerrs = [], []
-    for (b, h) in [(0, 0), (3, 31), (2, 9)]:
-        rows = np.unique(np.concatenate([[0, cfg.Nq - 1], rng.integers(0, cfg.Nq, 64)]))
-        ro, rl = attention_rows(h64(q[b, h, rows]), h64(k[b, h]), h64(v[b, h]), cfg.scale,
-                                cfg.causal, rows, cfg.Nq)
-        errs.append(np.abs(go[b, h, rows] - ro).ravel())
-        lerrs.append(np.abs(gl[b, h, rows] - rl).ravel())
-    err, lerr = np.concatenate(errs), np.concatenate(lerrs)
-    log_case("llama2_7b_prefill_f16 (sampled)", max_abs=float(err.max()),
-             mean_abs=float(err.mean()), lse_max_abs=float(lerr.max()))
-    assert np.isfinite(go).all()
-    assert err.max() <= TOL_MAX and err.mean() <= TOL_MEAN and lerr.max() <= TOL_LSE
+    whole_prefill_check("llama2_7b_prefill_f16", o, lse)
 
 
 @pytest.mark.parametrize("causal", [True, False])
@@ -1057,31 +1001,34 @@ def test_prefill_fp8_shapes(N, Nk, causal, d):
     o, lse = run_prefill_fp8(q, k, v, causal, scale, QS, KS, VS)
     assert o.dtype == torch.bfloat16
     ro, rl = attention_prefill_fp8(q, k, v, scale, QS, KS, VS, causal)
-    check(f"prefill fp8 N={N} Nk={Nk} causal={causal} d={d}", o, lse, ro, rl,
-          fp8_lse_tol(q, k, scale, QS, KS))
+    check(f"prefill fp8 N={N} Nk={Nk} causal={causal} d={d}", o, lse, ro, rl)
 
 
 # The bar is absolute, for outputs of unit scale: v_scale stays near FP8_V_SCALE so that the
-# dequantised V (and O) keep magnitudes of about 1.
-@pytest.mark.parametrize("scale,qs,ks,vs", [(0.125, QS, KS, VS), (-0.09, 0.02, 0.01, 0.02),
-                                             (0.0, QS, KS, VS), (0.3, 0.05, 0.004, 0.0021),
-                                             (0.05, 0.1, 0.1, 0.01)])
+# dequantised V (and O) keep magnitudes of about 1.  The last set (q_scale = k_scale = 0.1)
+# makes scores of tens: it is held to the accumulation bound below, the others to 1e-3.
+@pytest.mark.parametrize("scale,qs,ks,vs,large", [(0.125, QS, KS, VS, False),
+                                                   (-0.09, 0.02, 0.01, 0.02, False),
+                                                   (0.0, QS, KS, VS, False),
+                                                   (0.3, 0.05, 0.004, 0.0021, False),
+                                                   (0.05, 0.1, 0.1, 0.01, True)])
 @pytest.mark.parametrize("Hq,Hkv", [(8, 2), (6, 3)])
-def test_prefill_fp8_gqa_and_scales(Hq, Hkv, scale, qs, ks, vs):
+def test_prefill_fp8_gqa_and_scales(Hq, Hkv, scale, qs, ks, vs, large):
     q, k, v = fp8_case(12500 + Hq, 3, Hq, Hkv, 190, 260, 128)
     o, lse = run_prefill_fp8(q, k, v, True, scale, qs, ks, vs)
     ro, rl = attention_prefill_fp8(q, k, v, float(np.float32(scale)), float(np.float32(qs)),
                                    float(np.float32(ks)), float(np.float32(vs)), True)
     check(f"prefill fp8 GQA Hq={Hq} Hkv={Hkv} scales={(scale, qs, ks, vs)}", o, lse, ro, rl,
-          fp8_lse_tol(q, k, scale, qs, ks))
+          fp8_lse_tol(q, k, scale, qs, ks) if large else TOL_LSE)
 
 
-# Measured on MI355X: one FP8 MFMA (64 products) returns its dot product with an error of
-# up to 3.2e-4 of its largest product (under 2^-11), where an fp32 sum in order errs by
-# under 1e-6: the FP8 matrix core accumulates with reduced precision.  A score therefore
-# carries an error of at most (d/64) * 2^-11 * max_d |c q_d k_d| on top of the fp32 path's,
-# negligible for unit-scale scores (the workloads' draws) but not for scores in the tens or
-# hundreds; the LSE bar of FP8 cases widens by that bound.
+# The FP8 matrix core sums the 64 products of one MFMA with reduced precision: its error
+# is at most 2^-11 of the largest product (test_fp8_matrix_core_accumulation_bound pins
+# that through the FP8 prefill entry point).  A score therefore carries an error of at most
+# (d/64) * 2^-11 * max_d |c q_d k_d| on top of the fp32 path's, which the LSE inherits.  For
+# unit-scale scores (the workloads' draws) that is far inside the plain 1e-3 bar, which
+# those cases keep; the cases built to have large scores (tens to hundreds) are held to
+# 1e-3 plus that bound instead.
 def fp8_lse_tol(q, k, scale, qs, ks):
     s32 = lambda x: float(np.float32(x))
     Q = np.abs(s32(qs) * e4m3_value(q)).max(axis=2)     # [B, Hq, d]: max |q_d| of each head
@@ -1102,6 +1049,36 @@ def test_prefill_fp8_large_scores_within_the_accumulation_bound():
     check("prefill fp8 large scores", o, lse, ro, rl, fp8_lse_tol(q, k, scale, qs, ks))
 
 
+def test_fp8_matrix_core_accumulation_bound():
+    # One query and one key per head, non-causal, unit scales: the LSE is then the score
+    # q . k exactly as the FP8 matrix core returns it (one MFMA of 64 products at d=64, two
+    # accumulated in fp32 at d=128), times log2(e) and then ln 2 in fp32.  Codes are drawn
+    # uniformly over every non-NaN E4M3 code for half the heads and as E4M3 roundings of
+    # 16*N(0,1) for the other half.
+    rng = np.random.default_rng(4242)
+    H = 2048
+    for d in (64, 128):
+        nonnan = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+        uni = rng.choice(nonnan, size=(2, H // 2, d))
+        gau = ai.to_e4m3_codes((16 * rng.standard_normal((2, H // 2, d))).astype(np.float32))
+        codes = np.concatenate([uni, gau], axis=1)
+        q = np.ascontiguousarray(codes[0].reshape(1, H, 1, d))
+        k = np.ascontiguousarray(codes[1].reshape(1, H, 1, d))
+        v = np.zeros_like(k)
+        _, lse = run_prefill_fp8(q, k, v, False, 1.0, 1.0, 1.0, 1.0)
+        prod = e4m3_value(q[0, :, 0]) * e4m3_value(k[0, :, 0])          # [H, d], exact
+        exact = prod.sum(axis=1)                                         # fp64, exact here
+        chunk_max = np.abs(prod.reshape(H, d // 64, 64)).max(axis=2)     # per MFMA
+        got = lse.cpu().numpy()[0, :, 0].astype(np.float64)
+        err = np.abs(got - exact)
+        # 2^-11 of each MFMA's largest product, plus the epilogue's fp32 roundings
+        bound = 2.0 ** -11 * chunk_max.sum(axis=1) + 2.0 ** -21 * np.abs(exact)
+        rel = err / np.maximum(chunk_max.sum(axis=1), 1e-30)
+        log_case(f"fp8 matrix core accumulation d={d}", max_err_over_max_product=float(rel.max()),
+                 bound=2.0 ** -11)
+        assert (err <= bound).all(), f"d={d}: worst {rel.max():.3e} of the largest product"
+
+
 def test_prefill_fp8_gqa_equals_repeated_heads_and_is_deterministic():
     q, k, v = fp8_case(12600, 2, 8, 2, 300, 300, 64)
     o, lse = run_prefill_fp8(q, k, v, True, 0.125, QS, KS, VS)
@@ -1117,6 +1094,7 @@ def test_prefill_fp8_peaky_rows():
     q, k, v = fp8_case(12700, 1, 4, 4, 700, 700, 128, q_mult=4.0)
     o, lse = run_prefill_fp8(q, k, v, True, 0.088, QS, KS, VS)
     ro, rl = attention_prefill_fp8(q, k, v, float(np.float32(0.088)), QS, KS, VS, True)
+    # queries x4: scores of about 4x the unit-scale workloads' (a large-score case)
     check("prefill fp8 peaky rows", o, lse, ro, rl, fp8_lse_tol(q, k, 0.088, QS, KS))
 
 
@@ -1126,8 +1104,7 @@ def test_prefill_fp8_random_shapes(seed):
     q, k, v = fp8_case(seed, s["B"], s["Hq"], s["Hkv"], s["Nq"], s["Nk"], s["d"])
     o, lse = run_prefill_fp8(q, k, v, s["causal"], s["scale"], QS, KS, VS)
     ro, rl = attention_prefill_fp8(q, k, v, s["scale"], QS, KS, VS, s["causal"])
-    check(f"prefill fp8 random seed={seed} {s}", o, lse, ro, rl,
-          fp8_lse_tol(q, k, s["scale"], QS, KS))
+    check(f"prefill fp8 random seed={seed} {s}", o, lse, ro, rl)
 
 
 def test_prefill_fp8_llama2_shape():
@@ -1149,12 +1126,10 @@ def test_prefill_fp8_llama2_shape():
             errs.append(np.abs(go[b, h, rows] - ro).ravel())
             lerrs.append(np.abs(gl[b, h, rows] - rl).ravel())
     err, lerr = np.concatenate(errs), np.concatenate(lerrs)
-    tol = fp8_lse_tol(q, k, cfg.scale, qs, ks)
     log_case("llama2_7b_prefill_fp8 (sampled)", max_abs=float(err.max()),
-             mean_abs=float(err.mean()), lse_max_abs=float(lerr.max()), n=int(err.size),
-             lse_tol=tol)
+             mean_abs=float(err.mean()), lse_max_abs=float(lerr.max()), n=int(err.size))
     assert np.isfinite(go).all()
-    assert err.max() <= TOL_MAX and err.mean() <= TOL_MEAN and lerr.max() <= tol
+    assert err.max() <= TOL_MAX and err.mean() <= TOL_MEAN and lerr.max() <= TOL_LSE
 
 
 # ------------------------------------------------------------------ FP8 chunked prefill
@@ -1179,16 +1154,6 @@ def run_chunk_fp8(q, kc, vc, lens, table, causal, scale, qs=QS, ks=KS, vs=VS):
     return o, lse
 
 
-def paged_fp8_lse_tol(q, kc, scale, qs=QS, ks=KS):
-    # the accumulation bound of fp8_lse_tol over every cached row (NaN codes excluded)
-    K = np.abs(ks * e4m3_value(kc))
-    K = np.where(np.isnan(K), 0.0, K).max(axis=(0, 2))           # [Hkv, d]
-    Q = np.abs(qs * e4m3_value(q)).max(axis=(0, 2))              # [Hq, d]
-    G = q.shape[1] // kc.shape[1]
-    maxprod = max(float((Q[h] * K[h // G]).max()) for h in range(q.shape[1]))
-    return TOL_LSE + (q.shape[3] // 64) * 2.0 ** -11 * abs(float(np.float32(scale))) * maxprod
-
-
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("Nq,lens", [(1, (1, 17, 300)), (77, (77, 200, 1000)),
@@ -1199,8 +1164,7 @@ def test_prefill_paged_fp8_chunks(d, causal, Nq, lens):
     o, lse = run_chunk_fp8(q, kc, vc, lens, table, causal, scale)
     ro, rl = attention_prefill_paged_fp8(q, kc, vc, table, lens, scale, QS, KS, VS, causal)
     check(f"prefill_paged_fp8 d={d} causal={causal} Nq={Nq} "
-          f"lens={tuple(int(x) for x in lens)}", o, lse, ro, rl,
-          paged_fp8_lse_tol(q, kc, scale))
+          f"lens={tuple(int(x) for x in lens)}", o, lse, ro, rl)
 
 
 @pytest.mark.parametrize("causal", [True, False])
@@ -1242,12 +1206,10 @@ def test_chunked_prefill_paged_fp8_config():
         errs.append(np.abs(go[b, h] - ro))
         lerrs.append(np.abs(gl[b, h] - rl))
     err, lerr = np.concatenate([e.ravel() for e in errs]), np.concatenate(lerrs)
-    tol = paged_fp8_lse_tol(q, kc, cfg.scale)
     log_case("chunked_prefill_paged_fp8 (sampled)", max_abs=float(err.max()),
-             mean_abs=float(err.mean()), lse_max_abs=float(lerr.max()), n=int(err.size),
-             lse_tol=tol)
+             mean_abs=float(err.mean()), lse_max_abs=float(lerr.max()), n=int(err.size))
     assert np.isfinite(go).all()
-    assert err.max() <= TOL_MAX and err.mean() <= TOL_MEAN and lerr.max() <= tol
+    assert err.max() <= TOL_MAX and err.mean() <= TOL_MEAN and lerr.max() <= TOL_LSE
 
 
 # ------------------------------------------------------------------ FP8 varlen prefill
@@ -1262,14 +1224,6 @@ def run_varlen_fp8(q, k, v, cu_q, cu_k, causal, scale):
     return o, lse
 
 
-def varlen_fp8_lse_tol(q, k, scale):
-    Q = np.abs(QS * e4m3_value(q)).max(axis=0)     # [Hq, d]
-    K = np.abs(KS * e4m3_value(k)).max(axis=0)     # [Hkv, d]
-    G = q.shape[1] // k.shape[1]
-    maxprod = max(float((Q[h] * K[h // G]).max()) for h in range(q.shape[1]))
-    return TOL_LSE + (q.shape[2] // 64) * 2.0 ** -11 * abs(float(np.float32(scale))) * maxprod
-
-
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [True, False])
 def test_prefill_varlen_fp8(d, causal):
@@ -1279,8 +1233,7 @@ def test_prefill_varlen_fp8(d, causal):
     scale = float(np.float32(1 / math.sqrt(d)))
     o, lse = run_varlen_fp8(q, k, v, cu_q, cu_k, causal, scale)
     ro, rl = attention_prefill_varlen_fp8(q, k, v, cu_q, cu_k, scale, QS, KS, VS, causal)
-    check(f"prefill_varlen_fp8 d={d} causal={causal}", o, lse, ro, rl,
-          varlen_fp8_lse_tol(q, k, scale))
+    check(f"prefill_varlen_fp8 d={d} causal={causal}", o, lse, ro, rl)
 
 
 def test_prefill_varlen_fp8_equals_dense_fp8_prefill():
