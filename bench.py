@@ -10,8 +10,8 @@ also bracketed by HIP events on the stream it runs on.
 Prints ONE JSON line.  `value` is the prefill throughput in TFLOP/s (algorithmic FLOPs
 4*d per visible query-key pair); the decode half of the metric (KV GB/s) is reported in
 the `decode` object.  Each carries a `roofline` (dense bf16 MFMA peak for prefill, HBM
-peak for decode).  `cpu_baseline` times the CPU oracle on a bounded sample of the same
-prefill workload on this host's cores.
+peak for decode).  `cpu_baseline` times the CPU oracle over the same prefill and decode
+workloads on this host's cores (a process pool).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
 """
@@ -49,8 +49,6 @@ def parse():
     p.add_argument("--no-extra", action="store_true",
                    help="skip the other workloads (non-causal, 32K and fp16 prefill, contiguous and "
                         "FP8-cache decode, varlen prefill, backward, chunked prefill)")
-    p.add_argument("--cpu-seconds", type=float, default=15.0,
-                   help="approximate CPU time budget of the oracle sample")
     p.add_argument("--settle-ms", type=float, default=300.0,
                    help="after the W warmup steps, keep running untimed steps until the warmup "
                         "has lasted this long: the GPU raises its clocks over tens of ms of "
@@ -137,7 +135,7 @@ def decode_traffic():
 
 
 # ------------------------------------------------------------------------------ workloads
-def prefill_setup(name):
+def prefill_setup(name, keep_host=False):
     import torch
     cfg = ai.CONFIGS[name]
     q, k, v = ai.prefill_inputs(cfg)
@@ -149,10 +147,12 @@ def prefill_setup(name):
     o = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda") if cfg.fp8 else \
         torch.empty_like(dq)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    if keep_host:
+        return cfg, (dq, dk, dv, o, lse), (q, k, v)
     return cfg, (dq, dk, dv, o, lse)
 
 
-def decode_setup(name):
+def decode_setup(name, keep_host=False):
     import torch
     cfg = ai.CONFIGS[name]
     lens = ai.decode_lengths(cfg)
@@ -173,10 +173,13 @@ def decode_setup(name):
         dkc, dvc = torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda()
     else:
         dkc, dvc = to_dev(kc), to_dev(vc)
+    host = (q, kc, vc, lay.block_table, lens) if keep_host and cfg.paged else None
     del kc, vc
     o = torch.empty_like(dq)
     lse = torch.empty((cfg.B, cfg.Hq), dtype=torch.float32, device="cuda")
     seq = torch.from_numpy(lens).cuda()
+    if keep_host:
+        return cfg, lens, maxlen, (dq, dkc, dvc, table, seq, o, lse), host
     return cfg, lens, maxlen, (dq, dkc, dvc, table, seq, o, lse)
 
 
@@ -217,56 +220,41 @@ def time_kernel(fn, steps, warmup):
 
 
 # ------------------------------------------------------------------------------ CPU baseline
-def cpu_baseline(budget_s: float):
-    """Time the fp64 oracle on whole heads of the prefill workload until ~budget_s."""
-    from oracle import attention_rows
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+def cpu_baseline(prefill_host, decode_host):
+    """The fp64 oracle as it stands, on this host's cores: a process pool (one BLAS thread
+    per worker) over the prefill workload's (b, head, 1,024-row block) units and the paged
+    decode workload's (sequence, KV head) units, inputs placed in shared memory first.
+    Throughput is the GPU's algorithmic work (FLOPs, bytes) over the pool's wall time."""
+    from oracle import pool
     cfg = ai.CONFIGS[PREFILL_CFG]
-    rows = np.arange(cfg.Nq)
-    flops = 0
-    heads = 0
-    t_total = 0.0
-    passes = 0
-    # whole heads in (b, h) order; the whole workload is repeated until the budget is used
-    while t_total < budget_s:
-        for b in range(cfg.B):
-            for h in range(cfg.Hq):
-                kvh = h // (cfg.Hq // cfg.Hkv)
-                q = ai.bf16_bits_to_f64(ai.prefill_head(cfg, ai.T_Q, b, h))
-                k = ai.bf16_bits_to_f64(ai.prefill_head(cfg, ai.T_K, b, kvh))
-                v = ai.bf16_bits_to_f64(ai.prefill_head(cfg, ai.T_V, b, kvh))
-                t0 = time.perf_counter()
-                for i0 in range(0, cfg.Nq, 1024):
-                    attention_rows(q[i0:i0 + 1024], k, v, cfg.scale, cfg.causal,
-                                   rows[i0:i0 + 1024], cfg.Nq)
-                t_total += time.perf_counter() - t0
-                heads += 1
-                flops += 4 * cfg.d * ai.visible_pairs(cfg.Nq, cfg.Nk, cfg.causal)
-                if t_total >= budget_s:
-                    break
-            if t_total >= budget_s:
-                break
-        passes += 1
-    whole = heads // (cfg.B * cfg.Hq)
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{heads} whole heads of {PREFILL_CFG} ({whole} full passes over its "
-                      f"{cfg.B * cfg.Hq} heads), {t_total:.1f} s of numpy fp64 three-pass "
-                      "attention; FLOPs counted as for the GPU (4*d per visible pair)"}
-
-
-def cpu_model():
+    q, k, v = prefill_host
+    heads = [(b, h) for b in range(cfg.B) for h in range(cfg.Hq)]
+    rp = pool.time_prefill(q, k, v, cfg.scale, cfg.causal, heads)
+    flops = ai.prefill_flops(cfg)
+    dcfg = ai.CONFIGS[DECODE_CFG]
+    dq, kp, vp, table, lens = decode_host
+    units = [(b, h) for b in range(dcfg.B) for h in range(dcfg.Hkv)]
+    rd = pool.time_decode(dq, kp, vp, table, lens, dcfg.scale, units)
+    dbytes = ai.decode_bytes(dcfg, lens)
     try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
-    except OSError:
-        pass
-    return "unknown"
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    return {"value": round(flops / rp["seconds"] / 1e12, 4), "unit": "TFLOP/s",
+            "cores": cores, "workers": rp["workers"], "kind": "oracle",
+            "cpu_model": pool.cpu_model(),
+            "sample": f"the whole {PREFILL_CFG} workload ({len(heads)} heads, {rp['units']} "
+                      f"units of up to 1,024 query rows), {rp['seconds']:.2f} s wall on "
+                      f"{rp['workers']} worker processes of numpy fp64 three-pass attention "
+                      "(full rows even where causal masks them); FLOPs counted as for the GPU "
+                      "(4*d per visible pair)",
+            "decode": {"value": round(dbytes / rd["seconds"] / 1e9, 3), "unit": "GB/s",
+                       "workers": rd["workers"],
+                       "sample": f"the whole {DECODE_CFG} workload ({rd['units']} (sequence, "
+                                 f"KV head) units, sum(len)={int(lens.sum())}), "
+                                 f"{rd['seconds']:.2f} s wall; bytes counted as for the GPU "
+                                 "(bf16 K and V of the live tokens plus q, o, lse, lengths and "
+                                 "block-table entries)"}}
 
 
 # ------------------------------------------------------------------------------ main
@@ -276,15 +264,22 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the attention kernels "
               "here have no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
+    if not args.no_cpu:
+        # the oracle pool's workers fork from a server started before the GPU is touched
+        from oracle import pool
+        pool.start()
     import torch
     import io_aware_exact_attention_amd as mi
 
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
 
-    pcfg, (q, k, v, o, lse) = prefill_setup(PREFILL_CFG)
-    dcfg, lens, maxlen, (dq, dkc, dvc, table, seq, do, dlse) = decode_setup(DECODE_CFG)
-    ws = mi.decode_workspace(dcfg.B, dcfg.Hq, dcfg.Hkv, dcfg.d, maxlen, 0)
+    pcfg, (q, k, v, o, lse), prefill_host = prefill_setup(PREFILL_CFG, keep_host=True)
+    dcfg, lens, maxlen, (dq, dkc, dvc, table, seq, do, dlse), decode_host = decode_setup(
+        DECODE_CFG, keep_host=True)
+    if args.no_cpu:
+        prefill_host = decode_host = None
+    ws = mi.decode_workspace(dcfg.B, dcfg.Hq, dcfg.d, maxlen, 0)
 
     def prefill_call():
         mi.attn_fwd_prefill(q, k, v, o, lse, pcfg.causal, pcfg.scale, stream)
@@ -392,9 +387,9 @@ def main():
             else:
                 fwd = mi.attn_fwd_prefill_f16 if cfg.f16 else mi.attn_fwd_prefill
                 call = lambda: fwd(eq, ek, ev_, eo, el, cfg.causal, cfg.scale, stream)
+            # (the 32K prefill: 10 timed launches, 7 ms each)
             avg, med, mn = time_kernel(
-                call, max(3, args.steps // 4) if name == "long_prefill_32k" else args.steps,
-                args.warmup)
+                call, 10 if name == "long_prefill_32k" else args.steps, args.warmup)
             tf = ai.prefill_flops(cfg) / (avg * 1e-6) / 1e12
             extra[name] = {"us": round(avg, 2), "us_min": round(mn, 2), "TFLOP/s": round(tf, 2),
                            "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
@@ -410,7 +405,7 @@ def main():
         del dq, dkc, dvc, table, seq, do, dlse, ws
         torch.cuda.empty_cache()
         cfg, clens, cmax, (cq, ckc, cvc, ctab, cseq, co, cl) = decode_setup("gqa_decode_contig")
-        cws = mi.decode_workspace(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cmax, 0)
+        cws = mi.decode_workspace(cfg.B, cfg.Hq, cfg.d, cmax, 0)
         avg, med, mn = time_kernel(
             lambda: mi.attn_fwd_decode(cq, ckc, cvc, None, cseq, co, cl, cmax, cfg.scale, 0, cws,
                                        stream=stream), args.steps, args.warmup)
@@ -421,7 +416,7 @@ def main():
         torch.cuda.empty_cache()
         # the paged decode workload over an FP8 E4M3 cache (same lengths and pages)
         cfg, flens, fmax, (fq, fkc, fvc, ftab, fseq, fo, fl) = decode_setup("paged_gqa_decode_fp8")
-        fws = mi.decode_workspace(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, fmax, 0)
+        fws = mi.decode_workspace(cfg.B, cfg.Hq, cfg.d, fmax, 0)
         avg, med, mn = time_kernel(
             lambda: mi.attn_fwd_decode_fp8(fq, fkc, fvc, ftab, fseq, fo, fl, fmax, cfg.scale,
                                            ai.FP8_K_SCALE, ai.FP8_V_SCALE, 0, fws,
@@ -538,9 +533,7 @@ def main():
         del src, dst
 
     if not args.no_cpu:
-        cb = cpu_baseline(args.cpu_seconds)
-        cb["cpu_model"] = cpu_model()
-        out["cpu_baseline"] = cb
+        out["cpu_baseline"] = cpu_baseline(prefill_host, decode_host)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -62,6 +62,16 @@ typedef enum {
 /*
  * Prefill: many queries per sequence.
  *
+ * Defined by: the forward call of the page "메모리 장벽을 넘어: LLM 연산자 가속 라이브러리
+ * 심층 분석" (tiptinker), section "최적화된 어텐션 순전파 (Forward Pass)" (q, k, v, a softmax
+ * scale and a causal flag; bf16 device tensors in contiguous memory), computing the
+ * attention of the page "FlashAttention 완전 정리" (cell-devlog), section "Attention이
+ * 뭔가", tile by tile as in its section "FlashAttention의 핵심 아이디어 — Tiling" (Q, K,
+ * V read once and O written once; the score matrix never leaves the chip).  The layout is
+ * [B, H, N, d] as in that page's scaled-dot-product example (the tiptinker page's call
+ * documents [B, N, H, d]; the two conflict and [B, H, N, d] is kept).  Dropout, which that
+ * call also takes, is not offered (probability 0).
+ *
  *   q    [B, Hq,  Nq, d] bf16, 16-byte aligned
  *   k, v [B, Hkv, Nk, d] bf16, 16-byte aligned
  *   o    [B, Hq,  Nq, d] bf16 (written), 16-byte aligned
@@ -128,7 +138,9 @@ int attn_fwd_prefill_fp8(const void* q, const void* k, const void* v, void* o, f
  *          must lie in [0, num_pages); other entries are never read.  Entries outside
  *          that range are clamped into it on the device: the result is then unspecified,
  *          but no read leaves the cache.
- *   kv_lens [B] int32, DEVICE memory, each in [Nq, max_kv_len] (not read on the host)
+ *   kv_lens [B] int32, DEVICE memory, each in [Nq, max_kv_len] (not read on the host);
+ *          a value outside that range is clamped into it on the device: the result is
+ *          then unspecified, but no read leaves the block table or the cache.
  *   o      [B, Hq, Nq, d] bf16 (written), 16-byte aligned
  *   lse    [B, Hq, Nq] fp32 (written) or NULL
  *   Needs max_blocks_per_seq >= ceil(max_kv_len / 16).  Cache rows at or past
@@ -230,6 +242,15 @@ int attn_fwd_prefill_varlen_f16(const void* q, const void* k, const void* v, voi
  * Decode: one query per sequence against the sequence's KV cache, split along the
  * KV length into chunks whose partial results are merged by log-sum-exp.
  *
+ * Defined by: the page "메모리 장벽을 넘어: LLM 연산자 가속 라이브러리 심층 분석"
+ * (tiptinker), section "2. FlashInfer": decode as a separate kernel in which the newest
+ * token's query attends to the KV cache of everything before it, with the cache held in
+ * fixed-size pages (PagedAttention) reached through a per-sequence page table.  The
+ * chunked split and its merge are not on the pages: a chunk's (m, l) and partial output
+ * combine exactly under the m, f, l definitions of the page "Flash Attention: GPU
+ * 메모리_IO를 최적화하는 어텐션 메커니즘 완전 가이드" (holysheep), section "수학적 원리:
+ * Online Softmax 알고리즘".
+ *
  *   q        [B, Hq, d] bf16
  *   o        [B, Hq, d] bf16 (written)
  *   lse      [B, Hq] fp32 (written) or NULL
@@ -301,11 +322,15 @@ int attn_fwd_decode_fp8(const void* q, const void* kcache, const void* vcache,
  * Returns 0 for invalid arguments.  Pure host arithmetic; no HIP call. */
 int attn_decode_num_splits(int B, int Hq, int Hkv, int d, int max_seqlen, int num_splits);
 
-/* Workspace bytes attn_fwd_decode needs for these arguments: fp32 partial outputs and
- * log-sum-exps, B*Hq*splits*(d+1)*4 rounded up to 256, or 0 when one chunk suffices.
- * Returns 0 for invalid arguments.  Pure host arithmetic; no HIP call. */
-size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seqlen,
-                                   int num_splits);
+/* Workspace bytes that suffice for attn_fwd_decode (and its _f16 and _fp8 variants) with
+ * these B, Hq, d, max_seqlen and num_splits (0 = auto) and any valid Hkv: fp32 partial
+ * outputs and log-sum-exps, B*Hq*splits*(d+1)*4 rounded up to 256, where splits is the
+ * largest chunk count the plan picks for any Hkv dividing Hq (the automatic plan uses more
+ * chunks when fewer KV heads fill the grid), or 0 when one chunk always suffices.  The
+ * count for a given Hkv is attn_decode_num_splits.
+ * Returns 0 for invalid arguments (any size < 1, num_splits < 0).  Pure host arithmetic;
+ * no HIP call. */
+size_t attn_decode_workspace_bytes(int B, int Hq, int d, int max_seqlen, int num_splits);
 
 /*
  * Backward of attn_fwd_prefill (bf16): the gradients dq, dk, dv of the attention output

@@ -8,7 +8,7 @@ Entry points (same names and argument order as include/miattn.h):
     attn_fwd_prefill(q, k, v, o, lse, causal, scale, stream=None)
     attn_fwd_decode(q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen, scale,
                     num_splits=0, workspace=None, page_size=16, num_pages=None, stream=None)
-    attn_decode_workspace_bytes(B, Hq, Hkv, d, max_seqlen, num_splits)
+    attn_decode_workspace_bytes(B, Hq, d, max_seqlen, num_splits)
     attn_decode_num_splits(B, Hq, Hkv, d, max_seqlen, num_splits)
     attn_status_string(status)
 Conveniences that allocate the outputs with torch and call the above:
@@ -25,7 +25,9 @@ import os
 import torch
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG_DIR, "libmiattn.so")
+# MIATTN_LIB names another build of the same library to load instead (the host-sanitizer
+# build that the CPU tests use); by default the in-tree libmiattn.so.
+LIB_PATH = os.environ.get("MIATTN_LIB") or os.path.join(_PKG_DIR, "libmiattn.so")
 
 ATTN_OK = 0
 _lib = None
@@ -70,7 +72,7 @@ def load_library():
     lib.attn_fwd_decode_fp8.argtypes = [vp] * 7 + [i32] * 8 + [f32, f32, f32, i32, vp,
                                                                ctypes.c_size_t, vp]
     lib.attn_fwd_decode_fp8.restype = i32
-    lib.attn_decode_workspace_bytes.argtypes = [i32] * 6
+    lib.attn_decode_workspace_bytes.argtypes = [i32] * 5
     lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_decode_num_splits.argtypes = [i32] * 6
     lib.attn_decode_num_splits.restype = i32
@@ -330,8 +332,8 @@ def prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_s
 
 
 # -------------------------------------------------------------------------------- decode
-def attn_decode_workspace_bytes(B, Hq, Hkv, d, max_seqlen, num_splits=0) -> int:
-    return int(load_library().attn_decode_workspace_bytes(B, Hq, Hkv, d, max_seqlen, num_splits))
+def attn_decode_workspace_bytes(B, Hq, d, max_seqlen, num_splits=0) -> int:
+    return int(load_library().attn_decode_workspace_bytes(B, Hq, d, max_seqlen, num_splits))
 
 
 def attn_decode_num_splits(B, Hq, Hkv, d, max_seqlen, num_splits=0) -> int:
@@ -436,9 +438,9 @@ def attn_fwd_decode_fp8(q, kcache, vcache, block_table, seqlens, o, lse, max_seq
         raise AttnError(st, "attn_fwd_decode_fp8")
 
 
-def decode_workspace(B, Hq, Hkv, d, max_seqlen, num_splits=0, device="cuda"):
+def decode_workspace(B, Hq, d, max_seqlen, num_splits=0, device="cuda"):
     """A workspace tensor of the size attn_fwd_decode needs (None when it needs none)."""
-    n = attn_decode_workspace_bytes(B, Hq, Hkv, d, max_seqlen, num_splits)
+    n = attn_decode_workspace_bytes(B, Hq, d, max_seqlen, num_splits)
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
@@ -451,7 +453,7 @@ def decode(q, kcache, vcache, seqlens, max_seqlen: int, block_table=None,
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     if workspace is None:
-        workspace = decode_workspace(B, Hq, kcache.shape[1], d, max_seqlen, num_splits, q.device)
+        workspace = decode_workspace(B, Hq, d, max_seqlen, num_splits, q.device)
     fn = attn_fwd_decode_f16 if q.dtype == torch.float16 else attn_fwd_decode
     fn(q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen, scale, num_splits, workspace)
     return o, lse
@@ -467,7 +469,7 @@ def decode_fp8(q, kcache, vcache, seqlens, max_seqlen: int, k_scale: float, v_sc
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     if workspace is None:
-        workspace = decode_workspace(B, Hq, kcache.shape[1], d, max_seqlen, num_splits, q.device)
+        workspace = decode_workspace(B, Hq, d, max_seqlen, num_splits, q.device)
     attn_fwd_decode_fp8(q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen, scale,
                         k_scale, v_scale, num_splits, workspace)
     return o, lse

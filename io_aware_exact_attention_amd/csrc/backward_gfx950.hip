@@ -45,6 +45,7 @@ struct BwdShape {
   static constexpr int TILE = TROWS * ROWB;
   static constexpr int DMA = TILE / 16 / (64 * kWaves);  // 16-byte DMA ops per thread per tensor
   static constexpr int ROWS_WG = 32 * kWaves;          // queries (dQ) or keys (dK/dV) per workgroup
+  static_assert(ROWS_WG == kBwdRows, "host grid guards assume kBwdRows rows per workgroup");
   static_assert(TILE % (16 * 64 * kWaves) == 0, "tile must split evenly over threads");
 };
 

@@ -60,6 +60,12 @@ struct DecodeParams {
   int f16;        // Q, O and the cache are fp16 (else bf16; never with kv_fp8)
 };
 
+// Queries one prefill workgroup owns (8 waves of 32): the grid has ceil(Nq / this) query
+// tiles per head.
+constexpr int kPrefillRows = 256;
+// Queries (dQ pass) or keys (dK/dV pass) one backward workgroup owns.
+constexpr int kBwdRows = 128;
+
 // Query heads sharing one KV head that a decode workgroup serves at once.
 constexpr int kDecodeHeadsPerGroup = 16;
 // Keys one decode wave consumes per step; chunks are multiples of it.

@@ -140,7 +140,7 @@ int prefill_impl(const void* q, const void* k, const void* v, void* o, float* ls
   if (causal && Nq > Nk) return ATTN_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARGUMENT;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  const long qtiles = (Nq + 127) / 128;
+  const long qtiles = (Nq + miattn::kPrefillRows - 1) / miattn::kPrefillRows;
   if (qtiles * (long)Hq * B > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
   if ((long)B * Hq > 0x7fffffffL || (long)B * Hkv > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
   if (fp8 && !(std::isfinite(q_scale) && q_scale > 0.f && std::isfinite(k_scale) &&
@@ -188,7 +188,7 @@ int prefill_paged_impl(const void* q, const void* kcache, const void* vcache,
                k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
     return ATTN_ERR_INVALID_ARGUMENT;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  const long qtiles = (Nq + 127) / 128;
+  const long qtiles = (Nq + miattn::kPrefillRows - 1) / miattn::kPrefillRows;
   if (qtiles * (long)Hq * B > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
 
   miattn::PrefillParams p{};
@@ -235,7 +235,7 @@ int prefill_varlen_impl(const void* q, const void* k, const void* v, void* o, fl
                k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
     return ATTN_ERR_INVALID_ARGUMENT;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  const long qtiles = (max_seqlen_q + 255) / 256;
+  const long qtiles = (max_seqlen_q + miattn::kPrefillRows - 1) / miattn::kPrefillRows;
   if (qtiles * (long)Hq * B > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
   // 64 key rows of the packed K (row stride Hkv*d*2 bytes) must fit a buffer descriptor
   if (64L * Hkv * d * 2 > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
@@ -276,7 +276,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return ATTN_ERR_INVALID_ARGUMENT;
   if (Hq % Hkv || (causal && Nq > Nk) || !std::isfinite(scale)) return ATTN_ERR_INVALID_ARGUMENT;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  const long qtiles = (Nq + 127) / 128, ktiles = (Nk + 127) / 128;
+  const long qtiles = (Nq + miattn::kBwdRows - 1) / miattn::kBwdRows;
+  const long ktiles = (Nk + miattn::kBwdRows - 1) / miattn::kBwdRows;
   if (qtiles * (long)Hq * B > 0x7fffffffL || ktiles * (long)Hkv * B > 0x7fffffffL)
     return ATTN_ERR_UNSUPPORTED;
   // one head's K (or Q) rows must fit a buffer descriptor's 32-bit byte range
@@ -403,10 +404,17 @@ int attn_decode_num_splits(int B, int Hq, int Hkv, int d, int max_seqlen, int nu
   return plan_decode(B, Hq, Hkv, max_seqlen, num_splits).splits;
 }
 
-size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seqlen,
-                                   int num_splits) {
-  if (!decode_sizes_ok(B, Hq, Hkv, d, max_seqlen) || num_splits < 0) return 0;
-  return workspace_for(B, Hq, d, plan_decode(B, Hq, Hkv, max_seqlen, num_splits));
+size_t attn_decode_workspace_bytes(int B, int Hq, int d, int max_seqlen, int num_splits) {
+  if (B < 1 || Hq < 1 || d < 1 || max_seqlen < 1 || num_splits < 0) return 0;
+  // The automatic plan depends on the KV-head count (fewer KV heads, more chunks), which
+  // this call does not take: return the largest need over every Hkv that divides Hq.
+  size_t most = 0;
+  for (int hkv = 1; hkv <= Hq; ++hkv) {
+    if (Hq % hkv) continue;
+    const size_t w = workspace_for(B, Hq, d, plan_decode(B, Hq, hkv, max_seqlen, num_splits));
+    if (w > most) most = w;
+  }
+  return most;
 }
 
 int attn_fwd_decode(const void* q, const void* kcache, const void* vcache,

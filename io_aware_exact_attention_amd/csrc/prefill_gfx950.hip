@@ -45,6 +45,7 @@ template <int D, bool F8 = false>
 struct PrefillShape {
   static constexpr int kWaves = 8;
   static constexpr int BM = 32 * kWaves;        // queries per workgroup
+  static_assert(BM == kPrefillRows, "host grid guards assume kPrefillRows queries per tile");
   static constexpr int BN = 64;                 // keys per tile
   static constexpr int ROWB = D * 2;            // bytes per bf16 K/V row in LDS (swizzled)
   static constexpr int CPR = D / 8;             // 16-byte chunks per bf16 row
@@ -199,7 +200,9 @@ void prefill_kernel(PrefillParams a) {
   // context length (which includes the Nq new queries as its last tokens).  Varlen: the
   // sequence's rows [cu[b], cu[b+1]) of the packed tensors, clamped to the totals so that
   // no cumulative-length value can send a read outside them.
-  int nq = a.Nq, nk = PAGED ? a.kv_lens[b] : a.Nk;
+  // (paged: kv_lens[b] clamped into [Nq, max_kv_len], so that no value sends a block-table
+  // read past the sequence's row)
+  int nq = a.Nq, nk = PAGED ? min(max(a.kv_lens[b], a.Nq), a.Nk) : a.Nk;
   int q_start = 0, k_start = 0;
   if (VARLEN) {
     q_start = min(max(a.cu_q[b], 0), a.total_q);
@@ -461,7 +464,11 @@ void prefill_kernel(PrefillParams a) {
 
   const float c = a.c;      // |scale| * log2(e)
   float m_run = -INFINITY;  // reference max (raw score units) of this lane's query
-  float l_ex = 0.f;         // sum of the unrounded weights over this lane's half of the keys
+  // Sums over this lane's half of the keys: of the unrounded weights (for the LSE) and of
+  // the rounded weights the P.V products consume (for normalising O, which then is an
+  // exact convex combination of the V rows under those weights).
+  float l_ex = 0.f;
+  float l_rd = 0.f;
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
@@ -554,6 +561,9 @@ void prefill_kernel(PrefillParams a) {
 #pragma unroll
     for (int m = 0; m < kLead; ++m) ops[m] = DO_PV ? pre[m] : load(m);
     f32x16 s0 = f32x16{}, s1 = f32x16{};
+    // P.V also adds the tile's rounded weights to l_rd (one dot product with (1, 1) per
+    // packed pair, one per P.V MFMA), so O is normalised by exactly the weights it summed
+    float r0 = 0.f, r1 = 0.f;
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       if (m + kLead < M) ops[m + kLead] = load(m + kLead);
@@ -562,6 +572,14 @@ void prefill_kernel(PrefillParams a) {
         const u32x4 pw = {pk[t4 >> 1][4 * (t4 & 1) + 0], pk[t4 >> 1][4 * (t4 & 1) + 1],
                           pk[t4 >> 1][4 * (t4 & 1) + 2], pk[t4 >> 1][4 * (t4 & 1) + 3]};
         oacc[db] = E::mfma32(ops[m], __builtin_bit_cast(bf16x8, pw), oacc[db]);
+        if constexpr (NPV == 16) {
+          if (m & 1) r1 = E::add2(pk[m >> 3][m & 7], r1);
+          else r0 = E::add2(pk[m >> 3][m & 7], r0);
+        } else if (m < 16) {
+          // (d = 64: 8 P.V MFMAs, two pairs each)
+          r0 = E::add2(pk[m >> 3][m & 7], r0);
+          r1 = E::add2(pk[(m + 8) >> 3][(m + 8) & 7], r1);
+        }
       } else if constexpr (F8) {
         const int q = m - P0;
         if (q & 1) {
@@ -585,6 +603,7 @@ void prefill_kernel(PrefillParams a) {
     for (int m = 0; m < M; ++m) {
       // (F8: a Q.K^T MFMA follows every second read)
       if (!F8 || m < P0 || ((m - P0) & 1)) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (m < P0 && (NPV == 16 || m < 8)) __builtin_amdgcn_sched_group_barrier(0x002, NPV == 16 ? 1 : 2, 0);
       const int n = m + kLead;
       if (n < P0) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       else if (n < M) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
@@ -593,6 +612,7 @@ void prefill_kernel(PrefillParams a) {
       sacc[0] = s0;
       sacc[1] = s1;
     }
+    if (DO_PV) l_rd += r0 + r1;
   };
 
   // Online softmax of tile j held in sacc; MASK applies the causal diagonal and the ragged
@@ -616,10 +636,11 @@ void prefill_kernel(PrefillParams a) {
         for (int r = 0; r < 16; ++r)
           sacc[kb][r] = (kb * 32 + 16 * (r >> 3) + (r & 7) > vis) ? -INFINITY : sacc[kb][r];
     }
-    // P = exp2(S*c - m*c) -> bf16 pairs, and the tile's sum of the unrounded weights
+    // P = exp2(S*c - m*c) -> bf16 pairs, and the tile's sum of the unrounded weights (the
+    // sum of the rounded pairs is taken in the MFMA slot that consumes them)
     auto weights = [&]() {
       const float nmc = -(m_run * c);
-      float ex0 = 0.f, ex1 = 0.f;
+      float ex0, ex1;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -627,8 +648,13 @@ void prefill_kernel(PrefillParams a) {
           const float p0 = fast_exp2(fmaf(sacc[kb][2 * jj], c, nmc));
           const float p1 = fast_exp2(fmaf(sacc[kb][2 * jj + 1], c, nmc));
           pk[kb][jj] = E::pack2(p0, p1);
-          ex0 += p0;
-          ex1 += p1;
+          if (kb == 0 && jj == 0) {
+            ex0 = p0;
+            ex1 = p1;
+          } else {
+            ex0 += p0;
+            ex1 += p1;
+          }
         }
       return ex0 + ex1;
     };
@@ -644,6 +670,7 @@ void prefill_kernel(PrefillParams a) {
       const float alpha = m_run == -INFINITY ? 0.f : fast_exp2((m_run - m_new) * c);
       m_run = m_new;
       l_ex *= alpha;
+      l_rd *= alpha;
 #pragma unroll
       for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
       ts = weights();
@@ -743,10 +770,12 @@ void prefill_kernel(PrefillParams a) {
     slot_end(2 * n + 1);
   }
 
-  // --- epilogue: O = acc / l -> bf16; LSE = m*scale + ln l
+  // --- epilogue: O = acc / (sum of rounded weights) -> bf16; LSE = m*scale + ln l with l
+  // the sum of the unrounded weights
   const float l_tot = l_ex + wave_xor(l_ex, 32);
+  const float l_rtot = l_rd + wave_xor(l_rd, 32);
   if (qrow < nq) {
-    const float inv = (F8 ? a.v_scale : 1.f) / l_tot;
+    const float inv = (F8 ? a.v_scale : 1.f) / l_rtot;
     uint16_t* orow = VARLEN ? a.o + ((size_t)(q_start + qrow) * a.Hq + hq) * D
                             : a.o + ((size_t)(b * a.Hq + hq) * a.Nq + qrow) * D;
 #pragma unroll

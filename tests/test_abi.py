@@ -311,11 +311,26 @@ def test_decode_split_plan(lib):
 
 
 def test_decode_workspace_arithmetic(lib):
-    assert mi.attn_decode_workspace_bytes(2, 8, 2, 128, 100, 1) == 0
+    # the signature is (B, Hq, d, max_seqlen, num_splits), with no KV-head count
+    assert list(lib.attn_decode_workspace_bytes.argtypes) == [ctypes.c_int] * 5
+    assert mi.attn_decode_workspace_bytes(2, 8, 128, 100, 1) == 0
     n = 2 * 8 * 4
     want = (n * 128 * 4 + n * 4 + 255) // 256 * 256
-    assert mi.attn_decode_workspace_bytes(2, 8, 2, 128, 4096, 4) == want
-    assert mi.attn_decode_workspace_bytes(2, 8, 3, 128, 4096, 4) == 0  # invalid heads
+    assert mi.attn_decode_workspace_bytes(2, 8, 128, 4096, 4) == want
+    assert mi.attn_decode_workspace_bytes(0, 8, 128, 4096, 4) == 0     # invalid sizes
+    assert mi.attn_decode_workspace_bytes(2, 8, 128, 4096, -1) == 0
+
+
+@pytest.mark.parametrize("B,Hq,L", [(8, 32, 131072), (64, 32, 8192), (1, 1, 1000), (3, 12, 5000),
+                                    (2, 64, 300)])
+def test_decode_workspace_covers_every_kv_head_count(lib, B, Hq, L):
+    # the automatic plan's need for every valid Hkv, the largest of them returned
+    needs = []
+    for hkv in [h for h in range(1, Hq + 1) if Hq % h == 0]:
+        s = mi.attn_decode_num_splits(B, Hq, hkv, 128, L, 0)
+        n = B * Hq * s
+        needs.append(0 if s <= 1 else (n * 128 * 4 + n * 4 + 255) // 256 * 256)
+    assert mi.attn_decode_workspace_bytes(B, Hq, 128, L, 0) == max(needs)
 
 
 def test_binding_rejects_host_tensors(lib):
@@ -323,3 +338,14 @@ def test_binding_rejects_host_tensors(lib):
     x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         mi.attn_fwd_prefill(x, x, x, x, None, True, 0.125)
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(),
+                    reason="the accepted call would launch a kernel on dummy pointers")
+def test_prefill_grid_guard_counts_256_query_tiles(lib):
+    # 2^20 heads: 2047 query tiles of 256 rows fit in 2^31 - 1 workgroups (validation
+    # passes; without a device the launch then fails), 2048 do not
+    H = 1 << 20
+    assert prefill(lib, Hq=H, Hkv=H, Nq=2047 * 256, Nk=2047 * 256, d=64, causal=0) == HIPERR
+    assert prefill(lib, Hq=H, Hkv=H, Nq=2047 * 256 + 1, Nk=2047 * 256 + 1, d=64,
+                   causal=0) == UNSUPPORTED
