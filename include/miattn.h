@@ -285,6 +285,35 @@ int attn_fwd_decode(const void* q, const void* kcache, const void* vcache,
                     int max_blocks_per_seq, int num_pages, float scale, int num_splits,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Size in bytes of the per-GPU array that attn_fwd_decode_noalloc keeps its split-KV
+ * partials in: 32 MiB. */
+#define ATTN_DECODE_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+
+/*
+ * attn_fwd_decode without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, serving loops that must not call hipMalloc, and
+ * harnesses that forbid allocation.  The call itself calls no hipMalloc, hipFree or other
+ * allocating routine.
+ *
+ * The split-KV partials go to a static device array of ATTN_DECODE_NOALLOC_MAX_BYTES that
+ * the library holds on every GPU it runs on until the process ends (one copy per GPU,
+ * looked up once per device on that device's first call).  Arguments, layouts, chunking,
+ * outputs and results are those of attn_fwd_decode with the same arguments; the need is
+ * attn_decode_workspace_bytes of them (for the call's own Hkv), and a call whose need
+ * exceeds ATTN_DECODE_NOALLOC_MAX_BYTES returns WORKSPACE without launching anything.
+ * Nothing in the array has to start at zero (every partial the merge reads is written by
+ * the same call).  All calls on one GPU share its array: calls that may overlap on one GPU
+ * (different streams without ordering between them) race and give wrong results.
+ *
+ * Errors: those of attn_fwd_decode (WORKSPACE as above); HIP if the array's device address
+ * cannot be obtained or a launch fails.
+ */
+int attn_fwd_decode_noalloc(const void* q, const void* kcache, const void* vcache,
+                            const int32_t* block_table, const int32_t* seqlens, void* o,
+                            float* lse, int B, int Hq, int Hkv, int d, int max_seqlen,
+                            int page_size, int max_blocks_per_seq, int num_pages, float scale,
+                            int num_splits, hipStream_t stream);
+
 /* attn_fwd_decode with fp16 q, caches and o (as in attn_fwd_prefill_f16): the same
  * layouts, chunking, workspace and errors. */
 int attn_fwd_decode_f16(const void* q, const void* kcache, const void* vcache,

@@ -67,6 +67,8 @@ def load_library():
     lib.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                     i32, f32, i32, vp, ctypes.c_size_t, vp]
     lib.attn_fwd_decode.restype = i32
+    lib.attn_fwd_decode_noalloc.argtypes = [vp] * 7 + [i32] * 8 + [f32, i32, vp]
+    lib.attn_fwd_decode_noalloc.restype = i32
     lib.attn_fwd_decode_f16.argtypes = lib.attn_fwd_decode.argtypes
     lib.attn_fwd_decode_f16.restype = i32
     lib.attn_fwd_decode_fp8.argtypes = [vp] * 7 + [i32] * 8 + [f32, f32, f32, i32, vp,
@@ -410,6 +412,28 @@ def attn_fwd_decode(q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen:
                  lse, max_seqlen, scale, num_splits, workspace, page_size, num_pages, stream)
 
 
+ATTN_DECODE_NOALLOC_MAX_BYTES = 32 << 20
+
+
+def attn_fwd_decode_noalloc(q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen: int,
+                            scale: float, num_splits: int = 0, page_size: int = 16,
+                            num_pages: int | None = None, stream=None) -> None:
+    """attn_fwd_decode with its split partials in the library's per-GPU static array
+    (ATTN_DECODE_NOALLOC_MAX_BYTES) instead of a workspace: allocates nothing.  Calls
+    that may overlap on one GPU race."""
+    lib = load_library()
+    B, Hq, Hkv, d, max_blocks, num_pages, _ = _decode_args(
+        q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen, None, page_size,
+        num_pages, (torch.bfloat16,), torch.bfloat16)
+    st = lib.attn_fwd_decode_noalloc(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(block_table),
+                                     _ptr(seqlens), _ptr(o), _ptr(lse), B, Hq, Hkv, d,
+                                     int(max_seqlen), int(page_size), int(max_blocks),
+                                     int(num_pages), float(scale), int(num_splits),
+                                     _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_decode_noalloc")
+
+
 def attn_fwd_decode_f16(q, kcache, vcache, block_table, seqlens, o, lse, max_seqlen: int,
                         scale: float, num_splits: int = 0, workspace=None, page_size: int = 16,
                         num_pages: int | None = None, stream=None) -> None:
@@ -544,4 +568,5 @@ __all__ = ["attn_bwd", "attn_bwd_f16", "attn_bwd_workspace_bytes", "backward", "
            "attn_decode_workspace_bytes", "decode_fp8",
            "attn_decode_num_splits", "attn_status_string", "prefill", "decode",
            "attn_fwd_prefill_paged", "prefill_paged",
-           "decode_workspace", "load_library", "AttnError", "LIB_PATH"]
+           "decode_workspace", "load_library", "AttnError", "LIB_PATH",
+           "attn_fwd_decode_noalloc", "ATTN_DECODE_NOALLOC_MAX_BYTES"]

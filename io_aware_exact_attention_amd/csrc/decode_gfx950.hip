@@ -28,6 +28,8 @@
 // (holysheep), section "Online Softmax": a chunk with statistics (m_s, l_s) contributes
 // exp(m_s) l_s = exp(lse_s) to the row's normaliser.
 
+#include <mutex>
+
 #include "gfx950_common.h"
 #include "launch.h"
 
@@ -422,6 +424,33 @@ static hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   const int rows = p.B * p.Hq;
   hipLaunchKernelGGL((decode_merge_kernel<D, E>), dim3(rows), dim3(kMergeThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+// Split-KV partials of the allocation-free decode entry point: one fixed-size array per
+// GPU, which the library holds until the process ends.  Host code never uses the name
+// `scratch` as an address (in host code it is only a stand-in for the symbol): it asks
+// the runtime for the array's device address once per device, with that device current,
+// and uses that address from then on.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 // The FP8 cache widens to bf16 and is paired with bf16 Q and O only.

@@ -98,4 +98,10 @@ hipError_t launch_prefill(PrefillParams p, int d, int causal, hipStream_t stream
 hipError_t launch_backward(const BwdParams& p, int d, int causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t stream);
 
+// Bytes of the per-GPU static array that holds the split-KV partials of the
+// allocation-free decode entry point.
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+// Device address of that array on the current device (looked up once per device).
+hipError_t decode_scratch(void** ptr);
+
 }  // namespace miattn

@@ -13,6 +13,9 @@
 #include "../../include/miattn.h"
 #include "launch.h"
 
+static_assert(miattn::kDecodeScratchBytes == ATTN_DECODE_NOALLOC_MAX_BYTES,
+              "the header states the size of the allocation-free decode's array");
+
 namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -72,7 +75,8 @@ int decode_impl(const void* q, const void* kcache, const void* vcache,
                 const int32_t* block_table, const int32_t* seqlens, void* o, float* lse, int B,
                 int Hq, int Hkv, int d, int max_seqlen, int page_size, int max_blocks_per_seq,
                 int num_pages, float scale, bool fp8, bool f16, float k_scale, float v_scale,
-                int num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                int num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                bool static_scratch = false) {
   if (!q || !kcache || !vcache || !seqlens || !o) return ATTN_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16) || !aligned(kcache, 16) || !aligned(vcache, 16) || !aligned(o, 16) ||
       !aligned(seqlens, 4))
@@ -94,6 +98,12 @@ int decode_impl(const void* q, const void* kcache, const void* vcache,
 
   const Plan pl = plan_decode(B, Hq, Hkv, max_seqlen, num_splits);
   const size_t need = workspace_for(B, Hq, d, pl);
+  if (static_scratch && need) {
+    // the library's per-GPU array instead of a caller workspace (after all validation)
+    if (need > miattn::kDecodeScratchBytes) return ATTN_ERR_WORKSPACE;
+    if (miattn::decode_scratch(&workspace) != hipSuccess) return ATTN_ERR_HIP;
+    workspace_bytes = miattn::kDecodeScratchBytes;
+  }
   if (need) {
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return ATTN_ERR_WORKSPACE;
   }
@@ -425,6 +435,16 @@ int attn_fwd_decode(const void* q, const void* kcache, const void* vcache,
   return decode_impl(q, kcache, vcache, block_table, seqlens, o, lse, B, Hq, Hkv, d, max_seqlen,
                      page_size, max_blocks_per_seq, num_pages, scale, false, false, 1.f, 1.f,
                      num_splits, workspace, workspace_bytes, stream);
+}
+
+int attn_fwd_decode_noalloc(const void* q, const void* kcache, const void* vcache,
+                            const int32_t* block_table, const int32_t* seqlens, void* o,
+                            float* lse, int B, int Hq, int Hkv, int d, int max_seqlen,
+                            int page_size, int max_blocks_per_seq, int num_pages, float scale,
+                            int num_splits, hipStream_t stream) {
+  return decode_impl(q, kcache, vcache, block_table, seqlens, o, lse, B, Hq, Hkv, d, max_seqlen,
+                     page_size, max_blocks_per_seq, num_pages, scale, false, false, 1.f, 1.f,
+                     num_splits, nullptr, 0, stream, true);
 }
 
 int attn_fwd_decode_f16(const void* q, const void* kcache, const void* vcache,

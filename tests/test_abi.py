@@ -39,6 +39,7 @@ def test_header_declares_the_entry_points():
                                            "attn_fwd_prefill_varlen_f16",
                                            "attn_bwd_workspace_bytes",
                                            "attn_decode_workspace_bytes",
+                                           "attn_fwd_decode_noalloc",
                                            "attn_decode_num_splits", "attn_status_string"])
 
 
@@ -349,3 +350,32 @@ def test_prefill_grid_guard_counts_256_query_tiles(lib):
     assert prefill(lib, Hq=H, Hkv=H, Nq=2047 * 256, Nk=2047 * 256, d=64, causal=0) == HIPERR
     assert prefill(lib, Hq=H, Hkv=H, Nq=2047 * 256 + 1, Nk=2047 * 256 + 1, d=64,
                    causal=0) == UNSUPPORTED
+
+
+def decode_noalloc(lib, q=P, kc=P, vc=P, table=None, seqlens=P, o=P, lse=None, B=2, Hq=8, Hkv=2,
+                   d=128, max_seqlen=100, page_size=16, max_blocks=7, num_pages=10, scale=0.1,
+                   splits=1):
+    return lib.attn_fwd_decode_noalloc(q, kc, vc, table, seqlens, o, lse, B, Hq, Hkv, d,
+                                       max_seqlen, page_size, max_blocks, num_pages,
+                                       ctypes.c_float(scale), splits, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(seqlens=None), INVALID), (dict(kc=MIS), INVALID),
+    (dict(B=0), INVALID), (dict(Hq=6, Hkv=4), INVALID), (dict(splits=-1), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(d=80), UNSUPPORTED),
+    (dict(table=P, page_size=32), UNSUPPORTED),
+    # partials beyond the static array: B*Hq*splits*(d+1)*4 > 32 MiB
+    (dict(B=64, Hq=64, Hkv=8, max_seqlen=1 << 17, splits=128), WORKSPACE),
+])
+def test_decode_noalloc_validation(lib, kw, status):
+    assert decode_noalloc(lib, **kw) == status
+
+
+def test_decode_noalloc_limit_is_the_header_constant(lib):
+    assert "#define ATTN_DECODE_NOALLOC_MAX_BYTES ((size_t)32 << 20)" in open(HEADER).read()
+    assert mi.ATTN_DECODE_NOALLOC_MAX_BYTES == 32 << 20
+    # the workloads' needs fit: paged (B=8, Hq=32, up to 128K keys) and contiguous
+    # (B=64, Hq=32, 8K keys) decode at the automatic split count
+    assert 0 < mi.attn_decode_workspace_bytes(8, 32, 128, 131072, 0) <= 32 << 20
+    assert 0 < mi.attn_decode_workspace_bytes(64, 32, 128, 8192, 0) <= 32 << 20
