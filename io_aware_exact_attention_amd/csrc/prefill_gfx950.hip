@@ -557,9 +557,11 @@ void prefill_kernel(PrefillParams a) {
       if (m < P0) return pv_operand(sv, m);
       return qk_operand(sk, m - P0);
     };
+    // (an FP8 d = 64 slot without P.V has fewer operand reads than the read-ahead depth)
+    constexpr int L0 = kLead < M ? kLead : M;
     bf16x8 ops[M];
 #pragma unroll
-    for (int m = 0; m < kLead; ++m) ops[m] = DO_PV ? pre[m] : load(m);
+    for (int m = 0; m < L0; ++m) ops[m] = DO_PV ? pre[m] : load(m);
     f32x16 s0 = f32x16{}, s1 = f32x16{};
     // P.V also adds the tile's rounded weights to l_rd (one dot product with (1, 1) per
     // packed pair, one per P.V MFMA), so O is normalised by exactly the weights it summed
@@ -598,7 +600,7 @@ void prefill_kernel(PrefillParams a) {
     }
     // issue order: [the first kLead Q.K^T reads when nothing was prefetched], then per MFMA
     // m the reads of operand m + kLead (two transposing reads for P.V, one for Q.K^T)
-    if (!DO_PV) __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
+    if (!DO_PV) __builtin_amdgcn_sched_group_barrier(0x100, L0, 0);
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       // (F8: a Q.K^T MFMA follows every second read)
