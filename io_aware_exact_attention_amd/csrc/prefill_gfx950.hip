@@ -32,6 +32,7 @@
 // section "FlashAttention-3가 다른 이유") describes for Hopper is done here with LDS
 // DMA prefetch and the two-group schedule.
 
+#include <algorithm>
 #include <type_traits>
 
 #include "gfx950_common.h"
@@ -162,6 +163,43 @@ __device__ __forceinline__ PagedItem paged_work_item(int p, int B, int Hq, int n
   return it;
 }
 
+// Work order for a ragged (varlen) batch of at most 64 sequences, with no idle workgroups.
+// The grid holds, per query head, a bound on the batch's query tiles that the host knows
+// without reading the lengths: floor((total_q + B*(BM-1)) / BM).  Sequences are ranked by
+// key count, longest first, as above; in that order sequence b takes hpx * ntiles_b
+// consecutive slots of every XCD's list (its heads outer, its query tiles inner), where
+// ntiles_b = ceil(nq_b / BM).  Lane l holds sequence l's query tiles and key count; a
+// workgroup past the batch's last tile gets b = -1.
+__device__ __forceinline__ PagedItem varlen_work_item(int p, int B, int Hq, int ntiles,
+                                                      int mine, int lane) {
+  int hpx = Hq, k = p, hbase = 0;
+  if ((Hq & 7) == 0) {
+    hpx = Hq >> 3;
+    k = p >> 3;
+    hbase = (p & 7) * hpx;
+  }
+  const int w = lane < B ? hpx * ntiles : 0;  // this lane's sequence's slots
+  int before = 0;                             // slots of the sequences ranked ahead of it
+  for (int j = 0; j < B; ++j) {
+    const int o = __builtin_amdgcn_readlane(mine, j);
+    const int wj = __builtin_amdgcn_readlane(w, j);
+    before += ((o > mine) || (o == mine && j < lane)) ? wj : 0;
+  }
+  const uint64_t hit = __builtin_amdgcn_ballot_w64(w > 0 && k >= before && k < before + w);
+  PagedItem it;
+  if (hit == 0) {
+    it.b = -1;
+    it.hq = it.qrank = 0;
+    return it;
+  }
+  it.b = (int)__builtin_ctzll(hit);
+  const int rem = k - __builtin_amdgcn_readlane(before, it.b);
+  const int nt = __builtin_amdgcn_readlane(ntiles, it.b);
+  it.hq = hbase + rem / nt;
+  it.qrank = rem % nt;
+  return it;
+}
+
 // Layouts: dense [B, H, N, D] (PAGED and VARLEN false); PAGED: K/V in the paged cache,
 // kv_lens per sequence; VARLEN: sequences packed along the token axis, [total, H, D], with
 // cumulative lengths cu_q, cu_k.
@@ -182,7 +220,21 @@ void prefill_kernel(PrefillParams a) {
 
   // --- workgroup -> (query tile, head, batch)
   int hq, b, qrank;
-  if (PAGED || VARLEN) {
+  if (VARLEN && a.B <= 64) {
+    // lane l: sequence l's query tiles and key count (the clamped lengths used below)
+    int ntiles = 0, mine = -1;
+    if (lane < a.B) {
+      const int qs = min(max(a.cu_q[lane], 0), a.total_q);
+      const int ks = min(max(a.cu_k[lane], 0), a.total_k);
+      ntiles = (min(max(a.cu_q[lane + 1], qs), a.total_q) - qs + S::BM - 1) / S::BM;
+      mine = min(max(a.cu_k[lane + 1], ks), a.total_k) - ks;
+    }
+    const PagedItem pi = varlen_work_item(blockIdx.x, a.B, a.Hq, ntiles, mine, lane);
+    if (pi.b < 0) return;  // past the batch's last query tile
+    hq = pi.hq;
+    b = pi.b;
+    qrank = pi.qrank;
+  } else if (PAGED || VARLEN) {
     int mine = -1;  // lane l: length of sequence l, the key count that ranks sequences
     if (lane < a.B)
       mine = PAGED ? a.kv_lens[lane] : a.cu_k[lane + 1] - a.cu_k[lane];
@@ -210,8 +262,9 @@ void prefill_kernel(PrefillParams a) {
     k_start = min(max(a.cu_k[b], 0), a.total_k);
     nk = min(max(a.cu_k[b + 1], k_start), a.total_k) - k_start;
   }
-  // Varlen query tiles are counted per sequence (the grid covers the longest); the causal
-  // order is reversed per sequence so that each one's heaviest tile goes first.
+  // Varlen query tiles are counted per sequence (beyond 64 sequences the grid covers the
+  // longest for each); the causal order is reversed per sequence so that each one's
+  // heaviest tile goes first.
   const int nqt = VARLEN ? (nq + S::BM - 1) / S::BM : a.num_qtiles;
   if (VARLEN && qrank >= nqt) return;
   const int qtile = CAUSAL ? (nqt - 1 - qrank) : qrank;
@@ -834,6 +887,11 @@ hipError_t launch_prefill(PrefillParams p, int d, int causal, hipStream_t stream
   constexpr int BM = PrefillShape<128>::BM;
   p.num_qtiles = (p.Nq + BM - 1) / BM;
   p.total_wg = p.num_qtiles * p.Hq * p.B;
+  // ragged batch of at most 64 sequences: the tile bound of varlen_work_item per head
+  if (p.cu_q && p.B <= 64) {
+    const long tiles = ((long)p.total_q + (long)p.B * (BM - 1)) / BM;
+    p.total_wg = (int)std::min<long>(tiles * p.Hq, (long)p.total_wg);
+  }
   // A zero scale makes every visible weight 1.  A tiny positive exponent scale gives the
   // same fp32 weights (2^(tiny) rounds to 1) while keeping -inf * c = -inf for masked
   // keys, so the kernel needs no separate zero-weight select.

@@ -758,6 +758,21 @@ def test_prefill_varlen_odd_group_size():
     check("varlen Hq=6 Hkv=2", o, lse, ro, rl)
 
 
+@pytest.mark.parametrize("B", [64, 65])
+def test_prefill_varlen_many_sequences(B):
+    """Up to 64 sequences, each workgroup finds its (sequence, query tile) from the
+    cumulative lengths, over a grid sized from the total; beyond 64 the grid covers the
+    longest sequence for each.  Empty sequences and tile-edge lengths included."""
+    rng = np.random.default_rng(7800 + B)
+    lens = [int(x) for x in rng.integers(0, 600, B)]
+    lens[3], lens[10], lens[11], lens[B - 1] = 0, 256, 257, 512
+    q, k, v, cu_q, cu_k = ai.varlen_inputs(7800 + B, lens, lens, 8, 2, 64)
+    for causal in (True, False):
+        o, lse = run_varlen(q, k, v, cu_q, cu_k, causal, 0.125)
+        ro, rl = attention_prefill_varlen(f64(q), f64(k), f64(v), cu_q, cu_k, 0.125, causal)
+        check(f"varlen B={B} causal={causal}", o, lse, ro, rl)
+
+
 def test_prefill_varlen_sequence_without_keys():
     q, k, v, cu_q, cu_k = ai.varlen_inputs(7600, [10, 20], [30, 0], 2, 2, 64)
     o, lse = run_varlen(q, k, v, cu_q, cu_k, False, 0.125)
