@@ -573,24 +573,18 @@ void prefill_kernel(PrefillParams a) {
       if (grp != 0) return;
       const char* src = stage(j) + S::TILE;
       char* dst = smem + S::RING + (j & 1) * S::VTILE;
+      // unit u: bf16 chunk c of row R (its 8 codes at byte 8c of the code row).  16
+      // consecutive lanes read 128 contiguous bytes of codes, and 8 consecutive lanes write
+      // the chunks c..c+7 of one row, a contiguous 128-byte half after the XOR: neither
+      // access pattern has a bank conflict.
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int t = tid + 256 * hh;
-        const int R = t >> 3, c = t & 7;
-        const int sw = chunk_swizzle<D>(R);
-        if constexpr (D == 128) {
-          const u32x4 w = *(const u32x4*)(src + t * 16);
-          const u32x2 e0 = e4m3x4_to_bf16x4(w[0]), e1 = e4m3x4_to_bf16x4(w[1]);
-          const u32x2 e2 = e4m3x4_to_bf16x4(w[2]), e3 = e4m3x4_to_bf16x4(w[3]);
-          *(u32x4*)(dst + R * S::ROWB + (((2 * c) ^ sw) << 4)) =
-              u32x4{e0[0], e0[1], e1[0], e1[1]};
-          *(u32x4*)(dst + R * S::ROWB + (((2 * c + 1) ^ sw) << 4)) =
-              u32x4{e2[0], e2[1], e3[0], e3[1]};
-        } else {
-          const u32x2 w = *(const u32x2*)(src + t * 8);
-          const u32x2 e0 = e4m3x4_to_bf16x4(w[0]), e1 = e4m3x4_to_bf16x4(w[1]);
-          *(u32x4*)(dst + R * S::ROWB + ((c ^ sw) << 4)) = u32x4{e0[0], e0[1], e1[0], e1[1]};
-        }
+      for (int i = 0; i < D / 32; ++i) {
+        const int u = tid + 256 * i;
+        const int R = u / (D / 8), c = u % (D / 8);
+        const u32x2 w = *(const u32x2*)(src + R * D + 8 * c);
+        const u32x2 e0 = e4m3x4_to_bf16x4(w[0]), e1 = e4m3x4_to_bf16x4(w[1]);
+        *(u32x4*)(dst + R * S::ROWB + ((c ^ chunk_swizzle<D>(R)) << 4)) =
+            u32x4{e0[0], e0[1], e1[0], e1[1]};
       }
     }
   };
