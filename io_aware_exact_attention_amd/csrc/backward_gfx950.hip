@@ -329,67 +329,95 @@ void bwd_dkdv_kernel(BwdParams a) {
     const float* nl_t = (const float*)(st + 2 * S::TILE);
     const float* d_t = (const float*)(st + 2 * S::TILE + 256);
     const int q0 = (qt0 + it % per_head) * S::TROWS;
-#pragma unroll
-    for (int qh = 0; qh < 2; ++qh) {
-      // S and dP for 32 queries; accumulator r is query q0 + 32*qh + 16*(r/8) + 8*g + r%8
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        const bf16x8 qa = lds_read_b128(st + to.row[t] + qh * 32 * S::ROWB);
-        const bf16x8 da = lds_read_b128(st + S::TILE + to.row[t] + qh * 32 * S::ROWB);
-        s = E::mfma32(qa, kop[t], s);
-        dp = E::mfma32(da, vop[t], dp);
-      }
+    // One operand stream per tile.  Per 32-query half: the S and dP products (Q and dO rows
+    // against K^T, V^T in registers), the weights, then the dV and dK products (dO^T and
+    // Q^T by transposing reads).  The LDS reads run kLead MFMAs ahead of their use, across
+    // the weights (the dV and dK operands do not depend on them) and across the halves, so
+    // that the matrix core, fed by one wave per SIMD, does not wait out each read.
+    constexpr int P1 = 2 * (D / 16);  // S and dP MFMAs per half
+    constexpr int P2 = 4 * (D / 32);  // dV and dK MFMAs per half: 2 query steps x D/32 x 2
+    constexpr int HM = P1 + P2;
+    constexpr int NM = 2 * HM;
+    constexpr int kLead = 8;
+    // operand of MFMA m: S (even) and dP (odd) steps first, then (step t, block db) pairs
+    // of dV (even) and dK (odd)
+    auto load = [&](int m) -> bf16x8 {
+      const int qh = m / HM, mm = m % HM;
+      if (mm < P1)
+        return lds_read_b128(st + ((mm & 1) ? S::TILE : 0) + to.row[mm >> 1] +
+                             qh * 32 * S::ROWB);
+      const int x = mm - P1;
+      return to.trans(st + ((x & 1) ? 0 : S::TILE), (x >> 1) % (D / 32),
+                      2 * qh + x / (2 * (D / 32)));
+    };
+    f32x16 s = f32x16{}, dp = f32x16{};
+    uint32_t ppk[8], dpk[8];
+    // P = exp2(S*c - LSE*log2(e)) and dS = P * (dP - D) of half qh; MASK zeroes the pairs
+    // that are outside the causal triangle or past Nq, Nk.  Accumulator r is query
+    // q0 + 32*qh + 16*(r/8) + 8*g + r%8.
+    auto weights = [&](int qh, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
       const int qb = 32 * qh + 8 * g;
       const f32x4 NL[4] = {*(const f32x4*)(nl_t + qb), *(const f32x4*)(nl_t + qb + 4),
                            *(const f32x4*)(nl_t + qb + 16), *(const f32x4*)(nl_t + qb + 20)};
       const f32x4 Dv[4] = {*(const f32x4*)(d_t + qb), *(const f32x4*)(d_t + qb + 4),
                            *(const f32x4*)(d_t + qb + 16), *(const f32x4*)(d_t + qb + 20)};
-      uint32_t ppk[8], dpk[8];
-      // P = exp2(S*c - LSE*log2(e)) and dS = P * (dP - D); MASK zeroes the pairs that are
-      // outside the causal triangle or past Nq, Nk
-      auto weights = [&](auto mask_tag) {
-        constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          float pv[2], dsv[2];
+      for (int jj = 0; jj < 8; ++jj) {
+        float pv[2], dsv[2];
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int r = 2 * jj + e;
-            const float p = fast_exp2(fmaf(s[r], a.c, NL[r >> 2][r & 3]));
-            if (MASK) {
-              const int qi = q0 + qb + 16 * (r >> 3) + (r & 7);
-              const bool vis = kvalid && qi < a.Nq && (!CAUSAL || key <= qi + off);
-              pv[e] = vis ? p : 0.f;
-            } else {
-              pv[e] = p;
-            }
-            dsv[e] = pv[e] * (dp[r] - Dv[r >> 2][r & 3]);
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * jj + e;
+          const float p = fast_exp2(fmaf(s[r], a.c, NL[r >> 2][r & 3]));
+          if (MASK) {
+            const int qi = q0 + qb + 16 * (r >> 3) + (r & 7);
+            const bool vis = kvalid && qi < a.Nq && (!CAUSAL || key <= qi + off);
+            pv[e] = vis ? p : 0.f;
+          } else {
+            pv[e] = p;
           }
-          ppk[jj] = E::pack2(pv[0], pv[1]);
-          dpk[jj] = E::pack2(dsv[0], dsv[1]);
+          dsv[e] = pv[e] * (dp[r] - Dv[r >> 2][r & 3]);
         }
-      };
-      // every pair of this wave's 32 keys and the half's 32 queries is visible when the
-      // half's rows are all below Nq, the wave's keys all below Nk and, under causal
-      // masking, the half's first query sees the wave's last key (wave-uniform)
-      const int kmax = k0 + 32 * wave + 31;
-      const int qfirst = q0 + 32 * qh;
-      const bool all_visible =
-          qfirst + 31 < a.Nq && kmax < a.Nk && (!CAUSAL || kmax <= qfirst + off);
-      if (all_visible) weights(std::integral_constant<bool, false>{});
-      else weights(std::integral_constant<bool, true>{});
-      // dV^T += dO^T P and dK^T += Q^T dS in 16-query steps
+        ppk[jj] = E::pack2(pv[0], pv[1]);
+        dpk[jj] = E::pack2(dsv[0], dsv[1]);
+      }
+    };
+    bf16x8 ops[NM];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u32x4 pw = {ppk[4 * t], ppk[4 * t + 1], ppk[4 * t + 2], ppk[4 * t + 3]};
-        const u32x4 dw = {dpk[4 * t], dpk[4 * t + 1], dpk[4 * t + 2], dpk[4 * t + 3]};
+    for (int m = 0; m < kLead; ++m) ops[m] = load(m);
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          dv[db] = E::mfma32(to.trans(st + S::TILE, db, 2 * qh + t),
-                             __builtin_bit_cast(bf16x8, pw), dv[db]);
-          dk[db] = E::mfma32(to.trans(st, db, 2 * qh + t), __builtin_bit_cast(bf16x8, dw),
-                             dk[db]);
+    for (int qh = 0; qh < 2; ++qh) {
+      s = dp = f32x16{};
+#pragma unroll
+      for (int mm = 0; mm < P1; ++mm) {
+        const int m = qh * HM + mm;
+        if (m + kLead < NM) ops[m + kLead] = load(m + kLead);
+        if (mm & 1) dp = E::mfma32(ops[m], vop[mm >> 1], dp);
+        else s = E::mfma32(ops[m], kop[mm >> 1], s);
+      }
+      {
+        // every pair of this wave's 32 keys and the half's 32 queries is visible when the
+        // half's rows are all below Nq, the wave's keys all below Nk and, under causal
+        // masking, the half's first query sees the wave's last key (wave-uniform)
+        const int kmax = k0 + 32 * wave + 31;
+        const int qfirst = q0 + 32 * qh;
+        const bool all_visible =
+            qfirst + 31 < a.Nq && kmax < a.Nk && (!CAUSAL || kmax <= qfirst + off);
+        if (all_visible) weights(qh, std::integral_constant<bool, false>{});
+        else weights(qh, std::integral_constant<bool, true>{});
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS, 16-query step t
+#pragma unroll
+      for (int x = 0; x < P2; ++x) {
+        const int m = qh * HM + P1 + x;
+        if (m + kLead < NM) ops[m + kLead] = load(m + kLead);
+        const int t = x / (2 * (D / 32)), db = (x >> 1) % (D / 32);
+        if (x & 1) {
+          const u32x4 dw = {dpk[4 * t], dpk[4 * t + 1], dpk[4 * t + 2], dpk[4 * t + 3]};
+          dk[db] = E::mfma32(ops[m], __builtin_bit_cast(bf16x8, dw), dk[db]);
+        } else {
+          const u32x4 pw = {ppk[4 * t], ppk[4 * t + 1], ppk[4 * t + 2], ppk[4 * t + 3]};
+          dv[db] = E::mfma32(ops[m], __builtin_bit_cast(bf16x8, pw), dv[db]);
         }
       }
     }
