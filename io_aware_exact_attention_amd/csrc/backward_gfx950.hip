@@ -203,7 +203,7 @@ void bwd_dq_kernel(BwdParams a) {
     } else {
       wait_vmcnt<0>();
     }
-    __syncthreads();
+    block_barrier();
     const char* st = smem + (j & 1) * STAGE;
     // S^T and dP^T for the tile's two 32-key halves
     f32x16 s[2], dp[2];
@@ -244,7 +244,7 @@ void bwd_dq_kernel(BwdParams a) {
       for (int db = 0; db < D / 32; ++db)
         acc[db] = E::mfma32(to.trans(st, db, t4), __builtin_bit_cast(bf16x8, pw), acc[db]);
     }
-    __syncthreads();  // every wave is done with this stage before it is refilled
+    block_barrier();  // every wave is done with this stage before it is refilled
   }
 
   if (qvalid) store_row<D, E>(a.dq + ((size_t)bh * a.Nq + qrow) * D, acc, a.scale, g);
@@ -324,7 +324,7 @@ void bwd_dkdv_kernel(BwdParams a) {
     } else {
       wait_vmcnt<0>();
     }
-    __syncthreads();
+    block_barrier();
     const char* st = smem + (it & 1) * STAGE;
     const float* nl_t = (const float*)(st + 2 * S::TILE);
     const float* d_t = (const float*)(st + 2 * S::TILE + 256);
@@ -358,10 +358,9 @@ void bwd_dkdv_kernel(BwdParams a) {
     auto weights = [&](int qh, auto mask_tag) {
       constexpr bool MASK = decltype(mask_tag)::value;
       const int qb = 32 * qh + 8 * g;
-      const f32x4 NL[4] = {*(const f32x4*)(nl_t + qb), *(const f32x4*)(nl_t + qb + 4),
-                           *(const f32x4*)(nl_t + qb + 16), *(const f32x4*)(nl_t + qb + 20)};
-      const f32x4 Dv[4] = {*(const f32x4*)(d_t + qb), *(const f32x4*)(d_t + qb + 4),
-                           *(const f32x4*)(d_t + qb + 16), *(const f32x4*)(d_t + qb + 20)};
+      auto rd = [&](const float* t, int o) { return lds_read_f32x4((const char*)(t + qb + o)); };
+      const f32x4 NL[4] = {rd(nl_t, 0), rd(nl_t, 4), rd(nl_t, 16), rd(nl_t, 20)};
+      const f32x4 Dv[4] = {rd(d_t, 0), rd(d_t, 4), rd(d_t, 16), rd(d_t, 20)};
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         float pv[2], dsv[2];
@@ -421,7 +420,7 @@ void bwd_dkdv_kernel(BwdParams a) {
         }
       }
     }
-    __syncthreads();  // every wave is done with this stage before it is refilled
+    block_barrier();  // every wave is done with this stage before it is refilled
   }
 
   if (kvalid) {

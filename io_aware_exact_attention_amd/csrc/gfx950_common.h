@@ -49,6 +49,23 @@ __device__ __forceinline__ bf16x8 lds_read_b128(const char* __restrict__ p) {
   return *(const bf16x8*)p;
 }
 
+// 16-byte LDS read of four floats, with the same alias-scope property as lds_read_tr.
+__device__ __forceinline__ f32x4 lds_read_f32x4(const char* __restrict__ p) {
+  return *(const f32x4*)p;
+}
+
+// Workgroup barrier that is also a hard scheduling boundary: no instruction (memory or
+// ALU) is moved across it.  Unlike __syncthreads() it is no memory fence, so it does not
+// wait for the LDS DMA a wave has in flight for a later tile: kernels order those writes
+// with explicit vmcnt waits before it.
+__device__ __forceinline__ void block_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 // One 16-byte-per-lane LDS DMA (buffer_load_dwordx4 ... lds): lane l reads

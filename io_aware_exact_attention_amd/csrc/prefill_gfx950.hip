@@ -76,18 +76,6 @@ __device__ __forceinline__ int chunk_swizzle_f8(int R) {
   else return b3 | ((b1 ^ b2) << 1);
 }
 
-// Workgroup barrier that is also a hard scheduling boundary: no instruction (memory or
-// ALU) is moved across it, so the MFMA and softmax phases of the two wave groups stay
-// where the schedule puts them.  The LDS DMA writes are ordered by explicit vmcnt waits
-// before it.
-__device__ __forceinline__ void block_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 // Order in which workgroups take (query tile, head) pairs.  Workgroup p runs on XCD
 // p % 8.  When the B*Hq heads split evenly over the 8 XCDs, XCD x owns a contiguous block
 // of them, so a head's K/V (and those of heads sharing a KV head) are read through one L2.
