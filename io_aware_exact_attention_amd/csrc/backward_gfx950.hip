@@ -120,6 +120,20 @@ __device__ __forceinline__ void store_row(uint16_t* out, const f32x16 (&acc)[D /
     }
 }
 
+// Requires the dK and dV accumulators to sit in the accumulation registers (AGPRs) here.
+// The loop of bwd_dkdv_kernel calls it at the top of a tile and after each half's score
+// products; without it the register allocator gives the first half's scores the first
+// dV, dK blocks' registers and moves those blocks to vector registers and back at every
+// tile (64 extra moves), which also leaves fewer vector registers for the read-ahead.
+template <int N>
+__device__ __forceinline__ void pin_acc(f32x16 (&x)[N], f32x16 (&y)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    asm volatile("" : "+a"(x[i]));
+    asm volatile("" : "+a"(y[i]));
+  }
+}
+
 // ------------------------------------------------------------------------------ dQ
 template <int D, bool CAUSAL, typename E>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -325,6 +339,7 @@ void bwd_dkdv_kernel(BwdParams a) {
       wait_vmcnt<0>();
     }
     block_barrier();
+    pin_acc(dk, dv);
     const char* st = smem + (it & 1) * STAGE;
     const float* nl_t = (const float*)(st + 2 * S::TILE);
     const float* d_t = (const float*)(st + 2 * S::TILE + 256);
@@ -355,12 +370,10 @@ void bwd_dkdv_kernel(BwdParams a) {
     // P = exp2(S*c - LSE*log2(e)) and dS = P * (dP - D) of half qh; MASK zeroes the pairs
     // that are outside the causal triangle or past Nq, Nk.  Accumulator r is query
     // q0 + 32*qh + 16*(r/8) + 8*g + r%8.
+    f32x4 NL[4], Dv[4];
     auto weights = [&](int qh, auto mask_tag) {
       constexpr bool MASK = decltype(mask_tag)::value;
       const int qb = 32 * qh + 8 * g;
-      auto rd = [&](const float* t, int o) { return lds_read_f32x4((const char*)(t + qb + o)); };
-      const f32x4 NL[4] = {rd(nl_t, 0), rd(nl_t, 4), rd(nl_t, 16), rd(nl_t, 20)};
-      const f32x4 Dv[4] = {rd(d_t, 0), rd(d_t, 4), rd(d_t, 16), rd(d_t, 20)};
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         float pv[2], dsv[2];
@@ -387,13 +400,25 @@ void bwd_dkdv_kernel(BwdParams a) {
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
       s = dp = f32x16{};
+      {
+        // the half's row statistics: read before its products, used after them
+        const int qb = 32 * qh + 8 * g;
+        auto rd = [&](const float* t, int o) { return lds_read_f32x4((const char*)(t + qb + o)); };
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          NL[i] = rd(nl_t, 4 * (i & 1) + 16 * (i >> 1));
+          Dv[i] = rd(d_t, 4 * (i & 1) + 16 * (i >> 1));
+        }
+      }
 #pragma unroll
       for (int mm = 0; mm < P1; ++mm) {
         const int m = qh * HM + mm;
         if (m + kLead < NM) ops[m + kLead] = load(m + kLead);
         if (mm & 1) dp = E::mfma32(ops[m], vop[mm >> 1], dp);
         else s = E::mfma32(ops[m], kop[mm >> 1], s);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      pin_acc(dk, dv);
       {
         // every pair of this wave's 32 keys and the half's 32 queries is visible when the
         // half's rows are all below Nq, the wave's keys all below Nk and, under causal
@@ -418,6 +443,7 @@ void bwd_dkdv_kernel(BwdParams a) {
           const u32x4 pw = {ppk[4 * t], ppk[4 * t + 1], ppk[4 * t + 2], ppk[4 * t + 3]};
           dv[db] = E::mfma32(ops[m], __builtin_bit_cast(bf16x8, pw), dv[db]);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     block_barrier();  // every wave is done with this stage before it is refilled
