@@ -7,7 +7,8 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D = rowsum(dO * O) = rowsum(P * dP),
 //   dQ = scale * dS K,  dK = scale * dS^T Q,
 // and a KV head's dK, dV sum over the query heads that read it.  Two kernels, each a pass
-// over the score matrix in 64-row tiles staged through LDS by DMA (double-buffered):
+// over the score matrix in 64-row tiles staged through LDS by DMA (a two-stage ring in
+// the dQ pass, three stages in the dK/dV pass):
 //
 //  bwd_dq_kernel    a workgroup of 4 waves owns 128 queries of one head (32 per wave, on
 //                   lanes) and streams the head's K and V tiles:
@@ -270,7 +271,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdParams a) {
   using S = BwdShape<D>;
   constexpr int STAGE = 2 * S::TILE + 512;  // Q tile, dO tile, LSE and D of the tile's rows
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  constexpr int NST = 3;                    // ring stages: two tiles in flight
+  __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -307,11 +309,16 @@ void bwd_dkdv_kernel(BwdParams a) {
   const int iters = G * per_head;
 
   const TileOffsets<D> to(lane, wave);
-  auto issue = [&](int it) {
+  // byte offset of ring stage k (a uniform value whose range the compiler can see, so that
+  // constant offsets fold into the LDS instructions)
+  auto stage_off = [](int k) {
+    return (unsigned)__builtin_amdgcn_readfirstlane(k * STAGE) & 0x1ffffu;
+  };
+  auto issue = [&](int it, int stage) {
     const int h = kvh * G + it / per_head;
     const int q0 = (qt0 + it % per_head) * S::TROWS;
     const size_t r0 = (size_t)(b * a.Hq + h) * a.Nq + q0;
-    char* st = smem + (it & 1) * STAGE;
+    char* st = smem + stage_off(stage);
     const int nbytes = __builtin_amdgcn_readfirstlane((a.Nq - q0) * S::ROWB);
 #pragma unroll
     for (int i = 0; i < S::DMA; ++i) {
@@ -330,17 +337,25 @@ void bwd_dkdv_kernel(BwdParams a) {
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) dk[i] = dv[i] = f32x16{};
 
-  if (iters > 0) issue(0);
+  // Stage (it + 2) % NST, refilled at the top of iteration it, was last read in iteration
+  // it - 1, which ended with a barrier.
+  // Waves 0 and 1 issue one more DMA per tile (the row statistics) than the count the
+  // waits allow for, so their waits cover one more instruction than needed.
+  if (iters > 0) issue(0, 0);
+  if (iters > 1) issue(1, 1);
+  int cur = 0;  // ring stage of tile it
   for (int it = 0; it < iters; ++it) {
-    if (it + 1 < iters) {
-      issue(it + 1);
+    if (it + 2 < iters) {
+      issue(it + 2, cur == 0 ? 2 : cur - 1);
+      wait_vmcnt<4 * S::DMA>();
+    } else if (it + 1 < iters) {
       wait_vmcnt<2 * S::DMA>();
     } else {
       wait_vmcnt<0>();
     }
     block_barrier();
     pin_acc(dk, dv);
-    const char* st = smem + (it & 1) * STAGE;
+    const char* st = smem + stage_off(cur);
     const float* nl_t = (const float*)(st + 2 * S::TILE);
     const float* d_t = (const float*)(st + 2 * S::TILE + 256);
     const int q0 = (qt0 + it % per_head) * S::TROWS;
@@ -447,6 +462,7 @@ void bwd_dkdv_kernel(BwdParams a) {
       }
     }
     block_barrier();  // every wave is done with this stage before it is refilled
+    cur = cur == NST - 1 ? 0 : cur + 1;
   }
 
   if (kvalid) {
