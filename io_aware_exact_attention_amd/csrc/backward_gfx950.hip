@@ -343,6 +343,9 @@ void bwd_dkdv_kernel(BwdParams a) {
   // waits allow for, so their waits cover one more instruction than needed.
   if (iters > 0) issue(0, 0);
   if (iters > 1) issue(1, 1);
+  // the tile loop in the wave's phase order (below); each order has a loop of its own so
+  // that the register allocator treats the two separately
+  auto run = [&](auto order_tag) {
   int cur = 0;  // ring stage of tile it
   for (int it = 0; it < iters; ++it) {
     if (it + 2 < iters) {
@@ -359,111 +362,118 @@ void bwd_dkdv_kernel(BwdParams a) {
     const float* nl_t = (const float*)(st + 2 * S::TILE);
     const float* d_t = (const float*)(st + 2 * S::TILE + 256);
     const int q0 = (qt0 + it % per_head) * S::TROWS;
-    // One operand stream per tile.  Per 32-query half: the S and dP products (Q and dO rows
-    // against K^T, V^T in registers), the weights, then the dV and dK products (dO^T and
-    // Q^T by transposing reads).  The LDS reads run kLead MFMAs ahead of their use, across
-    // the weights (the dV and dK operands do not depend on them) and across the halves, so
-    // that the matrix core, fed by one wave per SIMD, does not wait out each read.
-    constexpr int P1 = 2 * (D / 16);  // S and dP MFMAs per half
-    constexpr int P2 = 4 * (D / 32);  // dV and dK MFMAs per half: 2 query steps x D/32 x 2
-    constexpr int HM = P1 + P2;
-    constexpr int NM = 2 * HM;
+    // One operand stream per tile, in four phases of P MFMAs: a query half's S and dP
+    // products (Q and dO rows against K^T, V^T in registers) or its dV and dK products (dO^T
+    // and Q^T by transposing reads), with the half's weights formed between the two.  Even
+    // waves take the order S0 W0 D0 S1 W1 D1, odd waves S0 S1 W0 D0 W1 D1, so that the
+    // waves of a workgroup, which start each tile together at the barrier, do not all ask
+    // the LDS for operands at once while it sits idle during their weights.  The LDS reads
+    // run kLead MFMAs ahead of their use, across the phases.
+    constexpr int P = D / 8;  // S, dP x D/16 steps, or dV, dK x 2 query steps x D/32 blocks
+    constexpr int NM = 4 * P;
     constexpr int kLead = 8;
-    // operand of MFMA m: S (even) and dP (odd) steps first, then (step t, block db) pairs
-    // of dV (even) and dK (odd)
-    auto load = [&](int m) -> bf16x8 {
-      const int qh = m / HM, mm = m % HM;
-      if (mm < P1)
-        return lds_read_b128(st + ((mm & 1) ? S::TILE : 0) + to.row[mm >> 1] +
-                             qh * 32 * S::ROWB);
-      const int x = mm - P1;
-      return to.trans(st + ((x & 1) ? 0 : S::TILE), (x >> 1) % (D / 32),
-                      2 * qh + x / (2 * (D / 32)));
-    };
-    f32x16 s = f32x16{}, dp = f32x16{};
-    uint32_t ppk[8], dpk[8];
-    // P = exp2(S*c - LSE*log2(e)) and dS = P * (dP - D) of half qh; MASK zeroes the pairs
-    // that are outside the causal triangle or past Nq, Nk.  Accumulator r is query
-    // q0 + 32*qh + 16*(r/8) + 8*g + r%8.
+    f32x16 sc[2], dpc[2];
+    uint32_t ppk[2][8], dpk[2][8];
     f32x4 NL[4], Dv[4];
-    auto weights = [&](int qh, auto mask_tag) {
+    // the row statistics of half h, read at the start of the phase before its weights
+    auto read_stats = [&](int h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int o = 32 * h + 8 * g + 4 * (i & 1) + 16 * (i >> 1);
+        NL[i] = lds_read_f32x4((const char*)(nl_t + o));
+        Dv[i] = lds_read_f32x4((const char*)(d_t + o));
+      }
+    };
+    // P = exp2(S*c - LSE*log2(e)) and dS = P * (dP - D) of half h, packed; accumulator r is
+    // query q0 + 32*h + 16*(r/8) + 8*g + r%8.  Only the causal triangle needs a mask (MASK:
+    // the half has a pair above it), applied by setting the exponent to -inf.  Rows past Nq
+    // need none: their Q, dO, LSE and D rows are staged as zeros, so P = 1 and dS = 0 there
+    // and both meet a zero dO or Q row.  Lanes of keys past Nk hold zero K and V rows;
+    // whatever they compute stays in their own accumulator column, which is not stored.
+    auto weights = [&](int h, auto mask_tag) {
       constexpr bool MASK = decltype(mask_tag)::value;
-      const int qb = 32 * qh + 8 * g;
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         float pv[2], dsv[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int r = 2 * jj + e;
-          const float p = fast_exp2(fmaf(s[r], a.c, NL[r >> 2][r & 3]));
+          float x = fmaf(sc[h][r], a.c, NL[r >> 2][r & 3]);
           if (MASK) {
-            const int qi = q0 + qb + 16 * (r >> 3) + (r & 7);
-            const bool vis = kvalid && qi < a.Nq && (!CAUSAL || key <= qi + off);
-            pv[e] = vis ? p : 0.f;
-          } else {
-            pv[e] = p;
+            const int qi = q0 + 32 * h + 8 * g + 16 * (r >> 3) + (r & 7);
+            x = key <= qi + off ? x : -INFINITY;
           }
-          dsv[e] = pv[e] * (dp[r] - Dv[r >> 2][r & 3]);
+          pv[e] = fast_exp2(x);
+          dsv[e] = pv[e] * (dpc[h][r] - Dv[r >> 2][r & 3]);
         }
-        ppk[jj] = E::pack2(pv[0], pv[1]);
-        dpk[jj] = E::pack2(dsv[0], dsv[1]);
+        ppk[h][jj] = E::pack2(pv[0], pv[1]);
+        dpk[h][jj] = E::pack2(dsv[0], dsv[1]);
       }
     };
-    bf16x8 ops[NM];
+    // half h has a (query, key) pair above the causal diagonal unless its first query sees
+    // the wave's last key (wave-uniform)
+    auto diagonal = [&](int h) { return CAUSAL && k0 + 32 * wave + 31 > q0 + 32 * h + off; };
+    auto tile = [&](auto order_tag) {
+      constexpr bool ALT = decltype(order_tag)::value;
+      // phase ph: S and dP products (else dV and dK) of half half_of(ph); the weights of
+      // half w_after(ph) (if >= 0) follow it
+      auto is_s = [](int ph) { return ALT ? ph < 2 : (ph & 1) == 0; };
+      auto half_of = [](int ph) { return ALT ? ph & 1 : ph >> 1; };
+      auto w_after = [](int ph) { return ph == 2 ? 1 : ph == (ALT ? 1 : 0) ? 0 : -1; };
+      // operand of MFMA m: S (even) and dP (odd) steps, or (query step t, block db) pairs
+      // of dV (even) and dK (odd)
+      auto load = [&](int m) -> bf16x8 {
+        const int ph = m / P, x = m % P, h = half_of(ph);
+        if (is_s(ph))
+          return lds_read_b128(st + ((x & 1) ? S::TILE : 0) + to.row[x >> 1] +
+                               h * 32 * S::ROWB);
+        return to.trans(st + ((x & 1) ? 0 : S::TILE), (x >> 1) % (D / 32),
+                        2 * h + x / (2 * (D / 32)));
+      };
+      bf16x8 ops[NM];
 #pragma unroll
-    for (int m = 0; m < kLead; ++m) ops[m] = load(m);
+      for (int m = 0; m < kLead; ++m) ops[m] = load(m);
+      sc[0] = dpc[0] = sc[1] = dpc[1] = f32x16{};
 #pragma unroll
-    for (int qh = 0; qh < 2; ++qh) {
-      s = dp = f32x16{};
-      {
-        // the half's row statistics: read before its products, used after them
-        const int qb = 32 * qh + 8 * g;
-        auto rd = [&](const float* t, int o) { return lds_read_f32x4((const char*)(t + qb + o)); };
+      for (int ph = 0; ph < 4; ++ph) {
+        const int h = half_of(ph), wh = w_after(ph);
+        if (wh >= 0) read_stats(wh);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          NL[i] = rd(nl_t, 4 * (i & 1) + 16 * (i >> 1));
-          Dv[i] = rd(d_t, 4 * (i & 1) + 16 * (i >> 1));
+        for (int x = 0; x < P; ++x) {
+          const int m = ph * P + x;
+          if (m + kLead < NM) ops[m + kLead] = load(m + kLead);
+          if (is_s(ph)) {
+            if (x & 1) dpc[h] = E::mfma32(ops[m], vop[x >> 1], dpc[h]);
+            else sc[h] = E::mfma32(ops[m], kop[x >> 1], sc[h]);
+          } else {
+            // dV^T += dO^T P and dK^T += Q^T dS, 16-query step t
+            const int t = x / (2 * (D / 32)), db = (x >> 1) % (D / 32);
+            if (x & 1) {
+              const u32x4 w = {dpk[h][4 * t], dpk[h][4 * t + 1], dpk[h][4 * t + 2],
+                               dpk[h][4 * t + 3]};
+              dk[db] = E::mfma32(ops[m], __builtin_bit_cast(bf16x8, w), dk[db]);
+            } else {
+              const u32x4 w = {ppk[h][4 * t], ppk[h][4 * t + 1], ppk[h][4 * t + 2],
+                               ppk[h][4 * t + 3]};
+              dv[db] = E::mfma32(ops[m], __builtin_bit_cast(bf16x8, w), dv[db]);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (wh >= 0) {
+          pin_acc(dk, dv);
+          if (diagonal(wh)) weights(wh, std::integral_constant<bool, true>{});
+          else weights(wh, std::integral_constant<bool, false>{});
         }
       }
-#pragma unroll
-      for (int mm = 0; mm < P1; ++mm) {
-        const int m = qh * HM + mm;
-        if (m + kLead < NM) ops[m + kLead] = load(m + kLead);
-        if (mm & 1) dp = E::mfma32(ops[m], vop[mm >> 1], dp);
-        else s = E::mfma32(ops[m], kop[mm >> 1], s);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      pin_acc(dk, dv);
-      {
-        // every pair of this wave's 32 keys and the half's 32 queries is visible when the
-        // half's rows are all below Nq, the wave's keys all below Nk and, under causal
-        // masking, the half's first query sees the wave's last key (wave-uniform)
-        const int kmax = k0 + 32 * wave + 31;
-        const int qfirst = q0 + 32 * qh;
-        const bool all_visible =
-            qfirst + 31 < a.Nq && kmax < a.Nk && (!CAUSAL || kmax <= qfirst + off);
-        if (all_visible) weights(qh, std::integral_constant<bool, false>{});
-        else weights(qh, std::integral_constant<bool, true>{});
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS, 16-query step t
-#pragma unroll
-      for (int x = 0; x < P2; ++x) {
-        const int m = qh * HM + P1 + x;
-        if (m + kLead < NM) ops[m + kLead] = load(m + kLead);
-        const int t = x / (2 * (D / 32)), db = (x >> 1) % (D / 32);
-        if (x & 1) {
-          const u32x4 dw = {dpk[4 * t], dpk[4 * t + 1], dpk[4 * t + 2], dpk[4 * t + 3]};
-          dk[db] = E::mfma32(ops[m], __builtin_bit_cast(bf16x8, dw), dk[db]);
-        } else {
-          const u32x4 pw = {ppk[4 * t], ppk[4 * t + 1], ppk[4 * t + 2], ppk[4 * t + 3]};
-          dv[db] = E::mfma32(ops[m], __builtin_bit_cast(bf16x8, pw), dv[db]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+    };
+    tile(order_tag);
     block_barrier();  // every wave is done with this stage before it is refilled
     cur = cur == NST - 1 ? 0 : cur + 1;
   }
+  };
+  if (wave & 1) run(std::integral_constant<bool, true>{});
+  else run(std::integral_constant<bool, false>{});
 
   if (kvalid) {
     const size_t out = ((size_t)bh * a.Nk + key) * D;
