@@ -182,7 +182,7 @@ void bwd_dq_kernel(BwdParams a) {
   }
   const float Dq = dpart + wave_xor(dpart, 32);
   if (g == 0 && qvalid) {
-    a.dvec[rowi] = Dq;
+    a.dvec[rowi] = -Dq;                     // the dK/dV pass starts its dP sums from -D
     a.nlse[rowi] = -a.lse[rowi] * kLog2e;  // the exponent offset the dK/dV pass adds
   }
   const float lse2 = qvalid ? a.lse[rowi] * kLog2e : INFINITY;
@@ -374,14 +374,15 @@ void bwd_dkdv_kernel(BwdParams a) {
     constexpr int kLead = 8;
     f32x16 sc[2], dpc[2];
     uint32_t ppk[2][8], dpk[2][8];
-    f32x4 NL[4], Dv[4];
-    // the row statistics of half h, read at the start of the phase before its weights
+    f32x4 NL[2][4], ND[2][4];
+    // the row statistics of half h (-LSE*log2(e) and -D), read a phase before its S and dP
+    // products: the dP sums start from -D, so that they end as dP - D
     auto read_stats = [&](int h) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int o = 32 * h + 8 * g + 4 * (i & 1) + 16 * (i >> 1);
-        NL[i] = lds_read_f32x4((const char*)(nl_t + o));
-        Dv[i] = lds_read_f32x4((const char*)(d_t + o));
+        NL[h][i] = lds_read_f32x4((const char*)(nl_t + o));
+        ND[h][i] = lds_read_f32x4((const char*)(d_t + o));
       }
     };
     // P = exp2(S*c - LSE*log2(e)) and dS = P * (dP - D) of half h, packed; accumulator r is
@@ -398,13 +399,13 @@ void bwd_dkdv_kernel(BwdParams a) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int r = 2 * jj + e;
-          float x = fmaf(sc[h][r], a.c, NL[r >> 2][r & 3]);
+          float x = fmaf(sc[h][r], a.c, NL[h][r >> 2][r & 3]);
           if (MASK) {
             const int qi = q0 + 32 * h + 8 * g + 16 * (r >> 3) + (r & 7);
             x = key <= qi + off ? x : -INFINITY;
           }
           pv[e] = fast_exp2(x);
-          dsv[e] = pv[e] * (dpc[h][r] - Dv[r >> 2][r & 3]);
+          dsv[e] = pv[e] * dpc[h][r];
         }
         ppk[h][jj] = E::pack2(pv[0], pv[1]);
         dpk[h][jj] = E::pack2(dsv[0], dsv[1]);
@@ -420,6 +421,8 @@ void bwd_dkdv_kernel(BwdParams a) {
       auto is_s = [](int ph) { return ALT ? ph < 2 : (ph & 1) == 0; };
       auto half_of = [](int ph) { return ALT ? ph & 1 : ph >> 1; };
       auto w_after = [](int ph) { return ph == 2 ? 1 : ph == (ALT ? 1 : 0) ? 0 : -1; };
+      // the phase at whose start the statistics of half h are read (h = 0: the tile's start)
+      auto stats_at = [](int h) { return h == 0 || ALT ? 0 : 1; };
       // operand of MFMA m: S (even) and dP (odd) steps, or (query step t, block db) pairs
       // of dV (even) and dK (odd)
       auto load = [&](int m) -> bf16x8 {
@@ -433,11 +436,17 @@ void bwd_dkdv_kernel(BwdParams a) {
       bf16x8 ops[NM];
 #pragma unroll
       for (int m = 0; m < kLead; ++m) ops[m] = load(m);
-      sc[0] = dpc[0] = sc[1] = dpc[1] = f32x16{};
 #pragma unroll
       for (int ph = 0; ph < 4; ++ph) {
         const int h = half_of(ph), wh = w_after(ph);
-        if (wh >= 0) read_stats(wh);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          if (stats_at(hh) == ph) read_stats(hh);
+        if (is_s(ph)) {
+          sc[h] = f32x16{};
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dpc[h][r] = ND[h][r >> 2][r & 3];
+        }
 #pragma unroll
         for (int x = 0; x < P; ++x) {
           const int m = ph * P + x;

@@ -74,7 +74,7 @@ constexpr int kDecodeWaves = 4;
 constexpr int kDecodeMaxSplits = 1024;  // chunks per sequence, at most
 
 // Backward (bf16 or fp16): gradients of the prefill attention.  Layouts as for prefill; dvec and
-// nlse are [B, Hq, Nq] fp32 workspace arrays for D = rowsum(dO * O) and -LSE * log2(e),
+// nlse are [B, Hq, Nq] fp32 workspace arrays for -D = -rowsum(dO * O) and -LSE * log2(e),
 // written by the first kernel and read by the second.
 struct BwdParams {
   const uint16_t* q;
