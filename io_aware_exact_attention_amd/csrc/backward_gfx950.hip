@@ -220,19 +220,36 @@ void bwd_dq_kernel(BwdParams a) {
     }
     block_barrier();
     const char* st = smem + (j & 1) * STAGE;
-    // S^T and dP^T for the tile's two 32-key halves
+    // One operand stream per tile: S^T and dP^T for the tile's two 32-key halves (K and V
+    // rows against Q^T, dO^T in registers), the weights, then dQ^T += K^T dS^T (K^T by
+    // transposing reads).  The LDS reads run kLead MFMAs ahead of their use, across the
+    // weights.
+    constexpr int NS = 4 * (D / 16);  // S and dP MFMAs: 2 halves x D/16 steps x 2
+    constexpr int NM = NS + 4 * (D / 32);
+    constexpr int kLead = 4;
+    // operand of MFMA m: (half kb, step t) pairs of S (even) and dP (odd), then (16-key
+    // step t4, block db) of dQ
+    auto load = [&](int m) -> bf16x8 {
+      if (m < NS) {
+        const int kb = m / (2 * (D / 16)), t = (m >> 1) % (D / 16);
+        return lds_read_b128(st + ((m & 1) ? S::TILE : 0) + to.row[t] + kb * 32 * S::ROWB);
+      }
+      const int x = m - NS;
+      return to.trans(st, x % (D / 32), x / (D / 32));
+    };
+    bf16x8 ops[NM];
+#pragma unroll
+    for (int m = 0; m < kLead; ++m) ops[m] = load(m);
     f32x16 s[2], dp[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      dp[kb] = f32x16{};
+    for (int kb = 0; kb < 2; ++kb) s[kb] = dp[kb] = f32x16{};
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        const bf16x8 ka = lds_read_b128(st + to.row[t] + kb * 32 * S::ROWB);
-        const bf16x8 va = lds_read_b128(st + S::TILE + to.row[t] + kb * 32 * S::ROWB);
-        s[kb] = E::mfma32(ka, qop[t], s[kb]);
-        dp[kb] = E::mfma32(va, doop[t], dp[kb]);
-      }
+    for (int m = 0; m < NS; ++m) {
+      if (m + kLead < NM) ops[m + kLead] = load(m + kLead);
+      const int kb = m / (2 * (D / 16)), t = (m >> 1) % (D / 16);
+      if (m & 1) dp[kb] = E::mfma32(ops[m], doop[t], dp[kb]);
+      else s[kb] = E::mfma32(ops[m], qop[t], s[kb]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // dS^T = P^T * (dP^T - D), P^T = exp(S - LSE); accumulator r of half kb is key
     // j*64 + 32*kb + 16*(r/8) + 8*g + r%8
@@ -252,12 +269,14 @@ void bwd_dq_kernel(BwdParams a) {
       }
     // dQ^T += K^T dS^T in 16-key steps
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
+    for (int x = 0; x < NM - NS; ++x) {
+      const int m = NS + x;
+      if (m + kLead < NM) ops[m + kLead] = load(m + kLead);
+      const int t4 = x / (D / 32), db = x % (D / 32);
       const u32x4 pw = {pk[t4 >> 1][4 * (t4 & 1) + 0], pk[t4 >> 1][4 * (t4 & 1) + 1],
                         pk[t4 >> 1][4 * (t4 & 1) + 2], pk[t4 >> 1][4 * (t4 & 1) + 3]};
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-        acc[db] = E::mfma32(to.trans(st, db, t4), __builtin_bit_cast(bf16x8, pw), acc[db]);
+      acc[db] = E::mfma32(ops[m], __builtin_bit_cast(bf16x8, pw), acc[db]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     block_barrier();  // every wave is done with this stage before it is refilled
   }
