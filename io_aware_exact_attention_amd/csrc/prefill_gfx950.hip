@@ -588,6 +588,12 @@ void prefill_kernel(PrefillParams a) {
     constexpr int M = P0 + (DO_QK ? NQK : 0);
     const char* sv = vstage(jpv);
     const char* sk = stage(jqk);
+    // The wave of the other group on this SIMD runs the softmax meanwhile.  The SIMD's
+    // arbiter would favour the older of the two waves whenever both can issue; a raised
+    // priority lets this wave's MFMAs issue as soon as their operands are there, and the
+    // softmax's vector instructions fill the cycles in between.
+    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_sched_barrier(0);
     auto load = [&](int m) -> bf16x8 {
       if (m < P0) return pv_operand(sv, m);
       return qk_operand(sk, m - P0);
@@ -650,6 +656,8 @@ void prefill_kernel(PrefillParams a) {
       sacc[1] = s1;
     }
     if (DO_PV) l_rd += r0 + r1;
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Online softmax of tile j held in sacc; MASK applies the causal diagonal and the ragged
