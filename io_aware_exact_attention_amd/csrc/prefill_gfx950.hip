@@ -555,25 +555,24 @@ void prefill_kernel(PrefillParams a) {
   // F8: widen V tile j (E4M3 in its ring stage, rows in byte order) into its bf16 buffer in
   // the layout the transposing P.V reads expect.  Widening happens in even slots, where
   // group 0 issues MFMAs and group 1 runs the softmax; group 0's 256 threads do it all
-  // (D/4 codes each), which keeps the softmax slot's vector work unchanged.
-  auto widen = [&](int j) {
+  // (D/4 codes each), which keeps the softmax slot's vector work unchanged.  Part i
+  // (i < D/32) widens D/32 codes per thread; the parts run inside group 0's MFMA slot, one
+  // after every few MFMAs, where their few vector and LDS instructions hide in the MFMAs'
+  // shadow.
+  auto widen_part = [&](int j, int i) {
     if constexpr (F8) {
-      if (grp != 0) return;
       const char* src = stage(j) + S::TILE;
       char* dst = smem + S::RING + (j & 1) * S::VTILE;
       // unit u: bf16 chunk c of row R (its 8 codes at byte 8c of the code row).  16
       // consecutive lanes read 128 contiguous bytes of codes, and 8 consecutive lanes write
       // the chunks c..c+7 of one row, a contiguous 128-byte half after the XOR: neither
       // access pattern has a bank conflict.
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i) {
-        const int u = tid + 256 * i;
-        const int R = u / (D / 8), c = u % (D / 8);
-        const u32x2 w = *(const u32x2*)(src + R * D + 8 * c);
-        const u32x2 e0 = e4m3x4_to_bf16x4(w[0]), e1 = e4m3x4_to_bf16x4(w[1]);
-        *(u32x4*)(dst + R * S::ROWB + ((c ^ chunk_swizzle<D>(R)) << 4)) =
-            u32x4{e0[0], e0[1], e1[0], e1[1]};
-      }
+      const int u = tid + 256 * i;
+      const int R = u / (D / 8), c = u % (D / 8);
+      const u32x2 w = *(const u32x2*)(src + R * D + 8 * c);
+      const u32x2 e0 = e4m3x4_to_bf16x4(w[0]), e1 = e4m3x4_to_bf16x4(w[1]);
+      *(u32x4*)(dst + R * S::ROWB + ((c ^ chunk_swizzle<D>(R)) << 4)) =
+          u32x4{e0[0], e0[1], e1[0], e1[1]};
     }
   };
   auto prefetch_pv = [&](int j) {
@@ -581,11 +580,14 @@ void prefill_kernel(PrefillParams a) {
 #pragma unroll
     for (int i = 0; i < kLead; ++i) pre[i] = pv_operand(st, i);
   };
-  auto mfma_slot = [&](int jpv, int jqk, auto pv_tag, auto qk_tag) {
+  // WIDEN (F8, group 0): V tile jqk is widened in parts between the MFMAs
+  auto mfma_slot = [&](int jpv, int jqk, auto pv_tag, auto qk_tag, auto widen_tag) {
     constexpr bool DO_PV = decltype(pv_tag)::value;
     constexpr bool DO_QK = decltype(qk_tag)::value;
+    constexpr bool WIDEN = F8 && decltype(widen_tag)::value;
     constexpr int P0 = DO_PV ? NPV : 0;
     constexpr int M = P0 + (DO_QK ? NQK : 0);
+    constexpr int MPW = M / (D / 32);  // MFMAs per widening part
     const char* sv = vstage(jpv);
     const char* sk = stage(jqk);
     // The wave of the other group on this SIMD runs the softmax meanwhile.  The SIMD's
@@ -638,6 +640,7 @@ void prefill_kernel(PrefillParams a) {
         if (q & 1) s1 = E::mfma32(ops[m], qop[q >> 1], s1);
         else s0 = E::mfma32(ops[m], qop[q >> 1], s0);
       }
+      if (WIDEN && m % MPW == MPW - 1) widen_part(jqk, m / MPW);
     }
     // issue order: [the first kLead Q.K^T reads when nothing was prefetched], then per MFMA
     // m the reads of operand m + kLead (two transposing reads for P.V, one for Q.K^T)
@@ -761,8 +764,7 @@ void prefill_kernel(PrefillParams a) {
   const int j1 = max(1, min(jm, n));  // softmax of tiles [1, j1) needs no mask
   if (grp == 0) {
     slot_begin(0);
-    widen(0);
-    mfma_slot(0, 0, no, yes);
+    mfma_slot(0, 0, no, yes, yes);
     slot_end(0);
     slot_begin(1);
     prefetch_pv(0);
@@ -770,8 +772,7 @@ void prefill_kernel(PrefillParams a) {
     slot_end(1);
     auto iter = [&](int j, auto mask_tag) {
       slot_begin(2 * j);
-      widen(j);
-      mfma_slot(j - 1, j, yes, yes);
+      mfma_slot(j - 1, j, yes, yes, yes);
       slot_end(2 * j);
       slot_begin(2 * j + 1);
       prefetch_pv(j);
@@ -781,26 +782,24 @@ void prefill_kernel(PrefillParams a) {
     for (int j = 1; j < j1; ++j) iter(j, no);
     for (int j = j1; j < n; ++j) iter(j, yes);
     slot_begin(2 * n);
-    mfma_slot(n - 1, 0, yes, no);
+    mfma_slot(n - 1, 0, yes, no, no);
     slot_end(2 * n);
     slot_begin(2 * n + 1);
     slot_end(2 * n + 1);
   } else {
     slot_begin(0);
-    widen(0);
     slot_end(0);
     slot_begin(1);
-    mfma_slot(0, 0, no, yes);
+    mfma_slot(0, 0, no, yes, no);
     slot_end(1);
     // iteration j runs the softmax of tile j-1: masked for tile 0 and tiles >= j1
     auto iter = [&](int j, auto mask_tag) {
       slot_begin(2 * j);
-      widen(j);
       prefetch_pv(j - 1);
       softmax(j - 1, mask_tag);
       slot_end(2 * j);
       slot_begin(2 * j + 1);
-      mfma_slot(j - 1, j, yes, yes);
+      mfma_slot(j - 1, j, yes, yes, no);
       slot_end(2 * j + 1);
     };
     if (n > 1) iter(1, yes);
@@ -811,7 +810,7 @@ void prefill_kernel(PrefillParams a) {
     softmax(n - 1, yes);
     slot_end(2 * n);
     slot_begin(2 * n + 1);
-    mfma_slot(n - 1, 0, yes, no);
+    mfma_slot(n - 1, 0, yes, no, no);
     slot_end(2 * n + 1);
   }
 
