@@ -304,9 +304,12 @@ void prefill_kernel(PrefillParams a) {
     return;
   }
 
-  // This wave's 32 query rows.  The two groups interleave 32-row blocks so that both
-  // reach the causal diagonal at about the same tile.
-  const int wrow0 = m0 + 32 * (2 * (wave & 3) + grp);
+  // This wave's 32 query rows: group 0 holds the first 128 rows of the tile, group 1 the
+  // last 128, one 32-row block per SIMD in each.  Under causal masking group 0's rows then
+  // stop seeing keys two tiles before group 1's, and in those last tiles each slot has
+  // only one role (group 1's MFMAs or group 1's softmax), which runs without the other
+  // contending for the SIMD.
+  const int wrow0 = m0 + 32 * (4 * grp + (wave & 3));
 
   // --- LDS DMA of one K/V tile (buffer_load ... lds): wave-instruction i of this wave
   // fills 1 KB of the stage; lane l fetches the chunk that belongs at LDS position l of
@@ -743,25 +746,42 @@ void prefill_kernel(PrefillParams a) {
     block_barrier();
   };
 
-  // First tile that needs masking for some row of the workgroup: the causal diagonal of
-  // its first query row, or the ragged end of the keys.
-  int jm = nk / S::BN;
-  if (CAUSAL) jm = min(jm, (m0 + off + 1) / S::BN);
-  jm = min(jm, ntiles);
+  // This wave's tiles, from its own rows (the last real one: rows past nq are never
+  // stored):
+  //   [0, jv)  every key visible to every row (tile 0 is masked all the same: peeled);
+  //   [jv, jd) the causal diagonal of some row, or the ragged end of the keys: masked;
+  //   [jd, n)  no key visible to any row: skipped, the wave only issues its share of the
+  //            K/V DMA and passes the barriers.  Skipping is exact: those weights are 0.
+  // FP8 keeps every tile, since group 0 widens each V tile for the whole workgroup.
+  const int n = ntiles;
+  int jd = n;
+  int jv = nk / S::BN;
+  if (CAUSAL) {
+    const int last = min(wrow0 + 31, nq - 1);
+    jv = min(jv, max(wrow0 + off + 1, 0) / S::BN);
+    if (!F8) jd = min(n, wrow0 >= nq ? 1 : max(last + off, 0) / S::BN + 1);
+  } else if (!F8 && wrow0 >= nq) {
+    jd = 1;
+  }
+  jd = max(jd, 1);
+  jv = max(1, min(jv, jd));
 
   // tile 0 resident before slot 0
   if (ntiles > 1) wait_vmcnt<S::LOADS_PER_TILE>(); else wait_vmcnt<0>();
   block_barrier();
 
   // Group 0: slot 2j = MFMA (P.V of j-1, Q.K^T of j); slot 2j+1 = softmax of j and the
-  // first P.V operands of j.  Group 1 runs one slot behind.  The loops carry no per-wave
-  // conditions: a wave whose rows end before the workgroup's last tile computes those
-  // tiles fully masked (P = 0).  The first and last tiles are peeled.  Both groups pass
-  // 2n+2 barriers.
+  // first P.V operands of j.  Group 1 runs one slot behind.  The first tile and the
+  // wave's last live tile (jd - 1) are peeled; slots past it keep only the DMA and the
+  // barriers, so every wave passes 2n+2 barriers.
   std::integral_constant<bool, false> no;
   std::integral_constant<bool, true> yes;
-  const int n = ntiles;
-  const int j1 = max(1, min(jm, n));  // softmax of tiles [1, j1) needs no mask
+  auto idle_slots = [&](int s0) {
+    for (int s = s0; s < 2 * n + 2; ++s) {
+      slot_begin(s);
+      slot_end(s);
+    }
+  };
   if (grp == 0) {
     slot_begin(0);
     mfma_slot(0, 0, no, yes, yes);
@@ -779,20 +799,19 @@ void prefill_kernel(PrefillParams a) {
       softmax(j, mask_tag);
       slot_end(2 * j + 1);
     };
-    for (int j = 1; j < j1; ++j) iter(j, no);
-    for (int j = j1; j < n; ++j) iter(j, yes);
-    slot_begin(2 * n);
-    mfma_slot(n - 1, 0, yes, no, no);
-    slot_end(2 * n);
-    slot_begin(2 * n + 1);
-    slot_end(2 * n + 1);
+    for (int j = 1; j < jv; ++j) iter(j, no);
+    for (int j = jv; j < jd; ++j) iter(j, yes);
+    slot_begin(2 * jd);
+    mfma_slot(jd - 1, 0, yes, no, no);
+    slot_end(2 * jd);
+    idle_slots(2 * jd + 1);
   } else {
     slot_begin(0);
     slot_end(0);
     slot_begin(1);
     mfma_slot(0, 0, no, yes, no);
     slot_end(1);
-    // iteration j runs the softmax of tile j-1: masked for tile 0 and tiles >= j1
+    // iteration j runs the softmax of tile j-1: masked for tile 0 and tiles >= jv
     auto iter = [&](int j, auto mask_tag) {
       slot_begin(2 * j);
       prefetch_pv(j - 1);
@@ -802,16 +821,17 @@ void prefill_kernel(PrefillParams a) {
       mfma_slot(j - 1, j, yes, yes, no);
       slot_end(2 * j + 1);
     };
-    if (n > 1) iter(1, yes);
-    for (int j = 2; j < min(j1 + 1, n); ++j) iter(j, no);
-    for (int j = max(j1 + 1, 2); j < n; ++j) iter(j, yes);
-    slot_begin(2 * n);
-    prefetch_pv(n - 1);
-    softmax(n - 1, yes);
-    slot_end(2 * n);
-    slot_begin(2 * n + 1);
-    mfma_slot(n - 1, 0, yes, no, no);
-    slot_end(2 * n + 1);
+    if (jd > 1) iter(1, yes);
+    for (int j = 2; j < min(jv + 1, jd); ++j) iter(j, no);
+    for (int j = max(jv + 1, 2); j < jd; ++j) iter(j, yes);
+    slot_begin(2 * jd);
+    prefetch_pv(jd - 1);
+    softmax(jd - 1, yes);
+    slot_end(2 * jd);
+    slot_begin(2 * jd + 1);
+    mfma_slot(jd - 1, 0, yes, no, no);
+    slot_end(2 * jd + 1);
+    idle_slots(2 * jd + 2);
   }
 
   // --- epilogue: O = acc / (sum of rounded weights) -> bf16; LSE = m*scale + ln l with l
