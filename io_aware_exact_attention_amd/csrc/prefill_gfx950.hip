@@ -751,16 +751,16 @@ void prefill_kernel(PrefillParams a) {
   //   [0, jv)  every key visible to every row (tile 0 is masked all the same: peeled);
   //   [jv, jd) the causal diagonal of some row, or the ragged end of the keys: masked;
   //   [jd, n)  no key visible to any row: skipped, the wave only issues its share of the
-  //            K/V DMA and passes the barriers.  Skipping is exact: those weights are 0.
-  // FP8 keeps every tile, since group 0 widens each V tile for the whole workgroup.
+  //            K/V DMA (FP8, group 0: and widens the V tiles, which group 1 may still
+  //            read) and passes the barriers.  Skipping is exact: those weights are 0.
   const int n = ntiles;
   int jd = n;
   int jv = nk / S::BN;
   if (CAUSAL) {
     const int last = min(wrow0 + 31, nq - 1);
     jv = min(jv, max(wrow0 + off + 1, 0) / S::BN);
-    if (!F8) jd = min(n, wrow0 >= nq ? 1 : max(last + off, 0) / S::BN + 1);
-  } else if (!F8 && wrow0 >= nq) {
+    jd = min(n, wrow0 >= nq ? 1 : max(last + off, 0) / S::BN + 1);
+  } else if (wrow0 >= nq) {
     jd = 1;
   }
   jd = max(jd, 1);
@@ -779,6 +779,13 @@ void prefill_kernel(PrefillParams a) {
   auto idle_slots = [&](int s0) {
     for (int s = s0; s < 2 * n + 2; ++s) {
       slot_begin(s);
+      if constexpr (F8) {
+        // group 0's even slot 2j: widen V tile j (with no MFMAs to hide behind)
+        if (grp == 0 && (s & 1) == 0 && (s >> 1) < n) {
+#pragma unroll
+          for (int i = 0; i < D / 32; ++i) widen_part(s >> 1, i);
+        }
+      }
       slot_end(s);
     }
   };
@@ -802,7 +809,8 @@ void prefill_kernel(PrefillParams a) {
     for (int j = 1; j < jv; ++j) iter(j, no);
     for (int j = jv; j < jd; ++j) iter(j, yes);
     slot_begin(2 * jd);
-    mfma_slot(jd - 1, 0, yes, no, no);
+    if (F8 && jd < n) mfma_slot(jd - 1, jd, yes, no, yes);  // and widen V tile jd
+    else mfma_slot(jd - 1, 0, yes, no, no);
     slot_end(2 * jd);
     idle_slots(2 * jd + 1);
   } else {
