@@ -440,6 +440,24 @@ def test_prefill_paged_chunks(d, causal, Nq, lens):
 
 
 @pytest.mark.parametrize("causal", [True, False])
+def test_prefill_paged_kv_lens_clamped(causal):
+    # kv_lens live on the device, so the host cannot check them: the kernel clamps each to
+    # [Nq, max_kv_len].  The cache holds (77, 700, 700) tokens; the call passes 10 (below
+    # Nq) and 5000 (above max_kv_len = 700, whose block-table row has 44 entries), and must
+    # equal the call with the clamped lengths.
+    Nq = 77
+    cfg, q, kc, vc, lens, table = make_chunk(3, 4, 2, 128, (77, 700, 700), Nq, seed=2150)
+    assert table.shape[1] == 44
+    bad = np.asarray([10, 5000, 700], np.int32)
+    o, lse = mi.prefill_paged(dev(q).reshape(q.shape), dev(kc).reshape(kc.shape),
+                              dev(vc).reshape(vc.shape), torch.from_numpy(table).cuda(),
+                              torch.from_numpy(bad).cuda(), 700, causal, 0.09)
+    torch.cuda.synchronize()
+    ro, rl = attention_prefill_paged(f64(q), f64(kc), f64(vc), table, lens, 0.09, causal)
+    check(f"prefill_paged clamped kv_lens causal={causal}", o, lse, ro, rl)
+
+
+@pytest.mark.parametrize("causal", [True, False])
 def test_prefill_paged_equals_contiguous_prefill(causal):
     # one sequence: the same key/value rows through the paged and the contiguous kernel
     cfg, q, kc, vc, lens, table = make_chunk(1, 8, 2, 128, (1000,), 333, seed=2100)
