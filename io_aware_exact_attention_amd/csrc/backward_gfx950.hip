@@ -190,6 +190,14 @@ void bwd_dq_kernel(BwdParams a) {
   const int kend = CAUSAL ? min(a.Nk, min(m0 + S::ROWS_WG, a.Nq) + off) : a.Nk;
   const int ntiles = (kend + S::TROWS - 1) / S::TROWS;
   const int lim = CAUSAL ? min(a.Nk - 1, qrow + off) : a.Nk - 1;  // last visible key
+  // the last key every row of this wave sees, and the score that hides a key
+  const int lim_all = CAUSAL ? min(a.Nk - 1, m0 + 32 * wave + off) : a.Nk - 1;
+  const float s_hidden = a.c > 0.f ? -INFINITY : INFINITY;
+  // the last key any real row of this wave sees (-1: the wave holds padding rows only)
+  const int wrow0 = m0 + 32 * wave;
+  const int last_vis = wrow0 >= a.Nq ? -1
+                       : CAUSAL ? min(a.Nk - 1, min(wrow0 + 31, a.Nq - 1) + off)
+                                : a.Nk - 1;
 
   const TileOffsets<D> to(lane, wave);
   const uint16_t* Kh = a.k + (size_t)(b * a.Hkv + kvh) * a.Nk * D;
@@ -219,64 +227,77 @@ void bwd_dq_kernel(BwdParams a) {
       wait_vmcnt<0>();
     }
     block_barrier();
-    const char* st = smem + (j & 1) * STAGE;
-    // One operand stream per tile: S^T and dP^T for the tile's two 32-key halves (K and V
-    // rows against Q^T, dO^T in registers), the weights, then dQ^T += K^T dS^T (K^T by
-    // transposing reads).  The LDS reads run kLead MFMAs ahead of their use, across the
-    // weights.
-    constexpr int NS = 4 * (D / 16);  // S and dP MFMAs: 2 halves x D/16 steps x 2
-    constexpr int NM = NS + 4 * (D / 32);
-    constexpr int kLead = 4;
-    // operand of MFMA m: (half kb, step t) pairs of S (even) and dP (odd), then (16-key
-    // step t4, block db) of dQ
-    auto load = [&](int m) -> bf16x8 {
-      if (m < NS) {
+    // A tile past the last key any row of this wave sees adds nothing to its dQ: the wave
+    // skips it, which frees its SIMD for the other workgroup's wave there.
+    if (j * S::TROWS <= last_vis) {
+      const char* st = smem + (j & 1) * STAGE;
+      // One operand stream per tile: S^T and dP^T for the tile's two 32-key halves (K and V
+      // rows against Q^T, dO^T in registers), the weights, then dQ^T += K^T dS^T (K^T by
+      // transposing reads).  The LDS reads run kLead MFMAs ahead of their use, across the
+      // weights.
+      constexpr int NS = 4 * (D / 16);  // S and dP MFMAs: 2 halves x D/16 steps x 2
+      constexpr int NM = NS + 4 * (D / 32);
+      constexpr int kLead = 4;
+      // operand of MFMA m: (half kb, step t) pairs of S (even) and dP (odd), then (16-key
+      // step t4, block db) of dQ
+      auto load = [&](int m) -> bf16x8 {
+        if (m < NS) {
+          const int kb = m / (2 * (D / 16)), t = (m >> 1) % (D / 16);
+          return lds_read_b128(st + ((m & 1) ? S::TILE : 0) + to.row[t] + kb * 32 * S::ROWB);
+        }
+        const int x = m - NS;
+        return to.trans(st, x % (D / 32), x / (D / 32));
+      };
+      bf16x8 ops[NM];
+  #pragma unroll
+      for (int m = 0; m < kLead; ++m) ops[m] = load(m);
+      f32x16 s[2], dp[2];
+  #pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = dp[kb] = f32x16{};
+  #pragma unroll
+      for (int m = 0; m < NS; ++m) {
+        if (m + kLead < NM) ops[m + kLead] = load(m + kLead);
         const int kb = m / (2 * (D / 16)), t = (m >> 1) % (D / 16);
-        return lds_read_b128(st + ((m & 1) ? S::TILE : 0) + to.row[t] + kb * 32 * S::ROWB);
+        if (m & 1) dp[kb] = E::mfma32(ops[m], doop[t], dp[kb]);
+        else s[kb] = E::mfma32(ops[m], qop[t], s[kb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      const int x = m - NS;
-      return to.trans(st, x % (D / 32), x / (D / 32));
-    };
-    bf16x8 ops[NM];
-#pragma unroll
-    for (int m = 0; m < kLead; ++m) ops[m] = load(m);
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) s[kb] = dp[kb] = f32x16{};
-#pragma unroll
-    for (int m = 0; m < NS; ++m) {
-      if (m + kLead < NM) ops[m + kLead] = load(m + kLead);
-      const int kb = m / (2 * (D / 16)), t = (m >> 1) % (D / 16);
-      if (m & 1) dp[kb] = E::mfma32(ops[m], doop[t], dp[kb]);
-      else s[kb] = E::mfma32(ops[m], qop[t], s[kb]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // dS^T = P^T * (dP^T - D), P^T = exp(S - LSE); accumulator r of half kb is key
-    // j*64 + 32*kb + 16*(r/8) + 8*g + r%8
-    uint32_t pk[2][8];
-    const int kbase = j * S::TROWS + 8 * g;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int r = 2 * jj;
-        const int key = kbase + 32 * kb + 16 * (r >> 3) + (r & 7);
-        float p0 = fast_exp2(fmaf(s[kb][r], a.c, -lse2));
-        float p1 = fast_exp2(fmaf(s[kb][r + 1], a.c, -lse2));
-        p0 = key <= lim ? p0 : 0.f;
-        p1 = key + 1 <= lim ? p1 : 0.f;
-        pk[kb][jj] = E::pack2(p0 * (dp[kb][r] - Dq), p1 * (dp[kb][r + 1] - Dq));
+      // dS^T = P^T * (dP^T - D), P^T = exp(S - LSE); accumulator r of half kb is key
+      // j*64 + 32*kb + 16*(r/8) + 8*g + r%8
+      uint32_t pk[2][8];
+      const int kbase = j * S::TROWS + 8 * g;
+      // Only a tile past some row's last visible key needs the mask: there the hidden scores
+      // are replaced by an infinity of the sign that sends S*c to -inf (c is never 0), so
+      // their weights come out 0.
+      if (j * S::TROWS + S::TROWS - 1 > lim_all) {
+  #pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kbase + 32 * kb + 16 * (r >> 3) + (r & 7);
+            s[kb][r] = key <= lim ? s[kb][r] : s_hidden;
+          }
       }
-    // dQ^T += K^T dS^T in 16-key steps
-#pragma unroll
-    for (int x = 0; x < NM - NS; ++x) {
-      const int m = NS + x;
-      if (m + kLead < NM) ops[m + kLead] = load(m + kLead);
-      const int t4 = x / (D / 32), db = x % (D / 32);
-      const u32x4 pw = {pk[t4 >> 1][4 * (t4 & 1) + 0], pk[t4 >> 1][4 * (t4 & 1) + 1],
-                        pk[t4 >> 1][4 * (t4 & 1) + 2], pk[t4 >> 1][4 * (t4 & 1) + 3]};
-      acc[db] = E::mfma32(ops[m], __builtin_bit_cast(bf16x8, pw), acc[db]);
-      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+  #pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int r = 2 * jj;
+          const float p0 = fast_exp2(fmaf(s[kb][r], a.c, -lse2));
+          const float p1 = fast_exp2(fmaf(s[kb][r + 1], a.c, -lse2));
+          pk[kb][jj] = E::pack2(p0 * (dp[kb][r] - Dq), p1 * (dp[kb][r + 1] - Dq));
+        }
+      // dQ^T += K^T dS^T in 16-key steps
+  #pragma unroll
+      for (int x = 0; x < NM - NS; ++x) {
+        const int m = NS + x;
+        if (m + kLead < NM) ops[m + kLead] = load(m + kLead);
+        const int t4 = x / (D / 32), db = x % (D / 32);
+        const u32x4 pw = {pk[t4 >> 1][4 * (t4 & 1) + 0], pk[t4 >> 1][4 * (t4 & 1) + 1],
+                          pk[t4 >> 1][4 * (t4 & 1) + 2], pk[t4 >> 1][4 * (t4 & 1) + 3]};
+        acc[db] = E::mfma32(ops[m], __builtin_bit_cast(bf16x8, pw), acc[db]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     block_barrier();  // every wave is done with this stage before it is refilled
   }

@@ -310,6 +310,9 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk;
   p.scale = scale;
   p.c = scale * 1.4426950408889634f;
+  // A zero scale makes every weight exp2(-LSE log2 e).  A tiny exponent scale gives the same
+  // fp32 weights and keeps (+-inf) * c infinite, which the masking relies on.
+  if (p.c == 0.f) p.c = 1e-30f;
   p.f16 = f16;
   (void)hipGetLastError();
   return miattn::launch_backward(p, d, causal ? 1 : 0, stream) == hipSuccess ? ATTN_OK
