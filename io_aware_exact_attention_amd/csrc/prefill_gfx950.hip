@@ -846,10 +846,17 @@ void prefill_kernel(PrefillParams a) {
   // the sum of the unrounded weights
   const float l_tot = l_ex + wave_xor(l_ex, 32);
   const float l_rtot = l_rd + wave_xor(l_rd, 32);
-  if (qrow < nq) {
+  // O leaves through LDS: stored straight from the MFMA layout, every store instruction
+  // would scatter 16-byte pieces over 32 rows.  After the last barrier no wave reads the
+  // ring any more, so each wave stages its 32 x D block there (rows padded by 16 bytes)
+  // and writes whole rows, 16 bytes per lane.  One wave's LDS writes and reads execute in
+  // order, so the wave needs no barrier of its own.
+  constexpr int OROWB = 2 * D + 16;
+  static_assert(S::kWaves * 32 * OROWB <= S::LDS, "O staging must fit the LDS");
+  char* ostage = smem + wave * 32 * OROWB;
+  {
     const float inv = (F8 ? a.v_scale : 1.f) / l_rtot;
-    uint16_t* orow = VARLEN ? a.o + ((size_t)(q_start + qrow) * a.Hq + hq) * D
-                            : a.o + ((size_t)(b * a.Hq + hq) * a.Nq + qrow) * D;
+    char* srow = ostage + (lane & 31) * OROWB;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -857,12 +864,24 @@ void prefill_kernel(PrefillParams a) {
         const int dv = 32 * db + 8 * a4 + 4 * g;
         const u32x2 w = {E::pack2(oacc[db][4 * a4 + 0] * inv, oacc[db][4 * a4 + 1] * inv),
                          E::pack2(oacc[db][4 * a4 + 2] * inv, oacc[db][4 * a4 + 3] * inv)};
-        *(u32x2*)(orow + dv) = w;
+        *(u32x2*)(srow + 2 * dv) = w;
       }
-    if (g == 0 && a.lse)
-      a.lse[VARLEN ? (size_t)hq * a.total_q + q_start + qrow
-                   : (size_t)(b * a.Hq + hq) * a.Nq + qrow] = (m_run * c + log2f(l_tot)) * kLn2;
   }
+#pragma unroll
+  for (int i = 0; i < 32 * (D / 8) / 64; ++i) {
+    const int idx = 64 * i + lane;  // 16-byte chunk of the wave's block
+    const int r = idx / (D / 8), ch = idx % (D / 8);
+    const int row = wrow0 + r;
+    const u32x4 w = *(const u32x4*)(ostage + r * OROWB + 16 * ch);
+    if (row < nq) {
+      uint16_t* orow = VARLEN ? a.o + ((size_t)(q_start + row) * a.Hq + hq) * D
+                              : a.o + ((size_t)(b * a.Hq + hq) * a.Nq + row) * D;
+      *(u32x4*)(orow + 8 * ch) = w;
+    }
+  }
+  if (qrow < nq && g == 0 && a.lse)
+    a.lse[VARLEN ? (size_t)hq * a.total_q + q_start + qrow
+                 : (size_t)(b * a.Hq + hq) * a.Nq + qrow] = (m_run * c + log2f(l_tot)) * kLn2;
 }
 
 template <int D, bool CAUSAL, typename E>
