@@ -106,19 +106,39 @@ __device__ __forceinline__ float dot8(u32x4 x, u32x4 y, float acc) {
   return acc;
 }
 
-// Stores a lane's 32 x D accumulator block (rows on lanes, columns 32*db + 8*(r/4) +
-// 4*g + r%4 in accumulator r of block db), times mul, in the element type into row `out`.
+// A wave's 32 rows of output written through LDS as whole rows, 16 bytes per lane.  Row r
+// lives in lanes r (columns 32*db + 8*a4 + 0..3) and r + 32 (+4..7) of the accumulators
+// acc[db][4*a4 .. 4*a4+3], the MFMA layout; written times mul in the element type.  Stored
+// straight from that layout, every store instruction would scatter 16-byte pieces over 32
+// rows.
+// stage: this wave's kStagedBytes of LDS, no longer read by any wave; out0: the wave's first
+// row; rows: how many of the 32 rows exist.  One wave's LDS writes and reads execute in
+// order, so the wave needs no barrier of its own.
+template <int D>
+constexpr int kStagedRowBytes = 2 * D + 16;  // rows padded by 16 bytes
+template <int D>
+constexpr int kStagedBytes = 32 * kStagedRowBytes<D>;
 template <int D, typename E>
-__device__ __forceinline__ void store_row(uint16_t* out, const f32x16 (&acc)[D / 32], float mul,
-                                          int g) {
+__device__ __forceinline__ void store_rows_staged(char* stage, uint16_t* out0,
+                                                  const f32x16 (&acc)[D / 32], float mul,
+                                                  int g, int lane, int rows) {
+  constexpr int RB = kStagedRowBytes<D>;
+  char* srow = stage + (lane & 31) * RB;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
       const u32x2 w = {E::pack2(acc[db][4 * a4 + 0] * mul, acc[db][4 * a4 + 1] * mul),
                        E::pack2(acc[db][4 * a4 + 2] * mul, acc[db][4 * a4 + 3] * mul)};
-      *(u32x2*)(out + 32 * db + 8 * a4 + 4 * g) = w;
+      *(u32x2*)(srow + 2 * (32 * db + 8 * a4 + 4 * g)) = w;
     }
+#pragma unroll
+  for (int i = 0; i < 32 * (D / 8) / 64; ++i) {
+    const int idx = 64 * i + lane;  // 16-byte chunk of the wave's block
+    const int r = idx / (D / 8), ch = idx % (D / 8);
+    const u32x4 w = *(const u32x4*)(stage + r * RB + 16 * ch);
+    if (r < rows) *(u32x4*)(out0 + (size_t)r * D + 8 * ch) = w;
+  }
 }
 
 // Requires the dK and dV accumulators to sit in the accumulation registers (AGPRs) here.
@@ -302,7 +322,11 @@ void bwd_dq_kernel(BwdParams a) {
     block_barrier();  // every wave is done with this stage before it is refilled
   }
 
-  if (qvalid) store_row<D, E>(a.dq + ((size_t)bh * a.Nq + qrow) * D, acc, a.scale, g);
+  // every wave passed the loop's last barrier, and no DMA is in flight: the buffers are free
+  static_assert(S::kWaves * kStagedBytes<D> <= 2 * STAGE, "dQ staging must fit the LDS");
+  store_rows_staged<D, E>(smem + wave * kStagedBytes<D>,
+                          a.dq + ((size_t)bh * a.Nq + m0 + 32 * wave) * D, acc, a.scale, g,
+                          lane, min(32, a.Nq - (m0 + 32 * wave)));
 }
 
 // ------------------------------------------------------------------------------ dK, dV
@@ -524,10 +548,14 @@ void bwd_dkdv_kernel(BwdParams a) {
   if (wave & 1) run(std::integral_constant<bool, true>{});
   else run(std::integral_constant<bool, false>{});
 
-  if (kvalid) {
-    const size_t out = ((size_t)bh * a.Nk + key) * D;
-    store_row<D, E>(a.dk + out, dk, a.scale, g);
-    store_row<D, E>(a.dv + out, dv, 1.f, g);
+  // every wave passed the loop's last barrier, and no DMA is in flight: the ring is free
+  static_assert(2 * S::kWaves * kStagedBytes<D> <= NST * STAGE, "dK/dV staging must fit the LDS");
+  {
+    const size_t out = ((size_t)bh * a.Nk + k0 + 32 * wave) * D;
+    const int rows = min(32, a.Nk - (k0 + 32 * wave));
+    char* st = smem + 2 * wave * kStagedBytes<D>;
+    store_rows_staged<D, E>(st, a.dk + out, dk, a.scale, g, lane, rows);
+    store_rows_staged<D, E>(st + kStagedBytes<D>, a.dv + out, dv, 1.f, g, lane, rows);
   }
 }
 
